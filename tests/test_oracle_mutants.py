@@ -1,0 +1,138 @@
+"""Plant a mistake in a copy of the oracle; some pin must catch it.
+
+This shows the pins are sharp enough: a dropped term, a wrong index, a
+reversed tie rule or a lost token would not slip through.
+"""
+
+import importlib.util
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins as P
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "nsa_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("nsa_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = mod          # dataclasses look the module up by name
+    try:
+        spec.loader.exec_module(mod)
+    finally:
+        del sys.modules[spec.name]
+    return mod
+
+
+def mut_no_softmax(O):
+    def f(q, reps, scale):
+        nb, nsub, d = reps.shape
+        lg = (np.asarray(q) @ reps.reshape(nb * nsub, d).T) * scale
+        return lg.sum(axis=0).reshape(nb, nsub).max(axis=1)
+    O.block_scores_group_softmax = f
+
+
+def mut_max_before_head_sum(O):
+    def f(q, reps, scale):
+        nb, nsub, d = reps.shape
+        lg = (np.asarray(q) @ reps.reshape(nb * nsub, d).T) * scale
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        return p.reshape(len(q), nb, nsub).max(axis=2).sum(axis=0)
+    O.block_scores_group_softmax = f
+
+
+def mut_ties_to_higher_id(O):
+    def f(ids, scores, k):
+        ids = np.asarray(ids, dtype=np.int64)
+        order = np.lexsort((-ids, -np.asarray(scores, dtype=np.float64)))
+        return ids[order[:k]]
+    O.top_k = f
+
+
+def mut_tail_dropped(O):
+    def f(blocks, L):
+        parts = [np.arange(b * 64, (b + 1) * 64) for b in blocks] + [np.zeros(0, dtype=np.int64)]
+        return np.concatenate(parts).astype(np.int64)
+    O.token_set = f
+
+
+def mut_stop_block_excluded(O):
+    orig = O.early_stop_attention
+
+    def f(q, keys, values, order, L, tau, scale):
+        n, _ = orig(q, keys, values, order, L, tau, scale)
+        n2 = n - 1 if n < len(order) else n
+        return n2, O.sparse_attention(q, keys, values, list(order[:n2]), L, scale)
+    O.early_stop_attention = f
+
+
+def mut_sub_block_shift(O):
+    def f(keys, nb, storage):
+        d = keys.shape[1]
+        x = np.asarray(keys[1: nb * 64 + 1], dtype=np.float64).reshape(nb, 4, 16, d)
+        return O.rounded_means(np.moveaxis(x, 2, 3), storage)
+    O.block_reps = f
+
+
+def mut_eviction_forgets_old(O):
+    def f(prev_set, n_seen, nb, E, k_e):
+        cand = np.arange(n_seen, nb, dtype=np.int64)
+        if k_e == 0 or cand.size == 0:
+            return np.asarray(prev_set, dtype=np.int64)
+        return np.sort(O.top_k(cand, E[cand], min(k_e, cand.size)))
+    O.eviction_update = f
+
+
+def mut_attention_unscaled(O):
+    orig = O.attend
+    O.attend = lambda q, K, V, scale: orig(q, K, V, 1.0)
+
+
+def mut_round_truncates(O):
+    def f(x):
+        x = np.asarray(x, dtype=np.float64)
+        m, e = np.frexp(x)
+        return np.ldexp(np.trunc(m * 256.0) / 256.0, e)
+    O.round_bf16 = f
+
+
+def mut_parts_overlap(O):
+    def f(S, evict_set, nb, k):
+        return O.top_k(np.arange(nb), S, min(k - len(evict_set), nb))
+    O.query_aware_set = f
+
+
+def mut_mean_by_15(O):
+    orig = O.rounded_means
+    O.rounded_means = lambda x, storage: orig(np.asarray(x) * (16.0 / 15.0), storage)
+
+
+def mut_gamma_ignores_tail(O):
+    def f(selected, prev_selected, prev_tail_block):
+        sel = set(int(b) for b in selected)
+        return len(sel & set(int(b) for b in prev_selected)) / max(len(sel), 1)
+    O.locality = f
+
+
+MUTANTS = [mut_no_softmax, mut_max_before_head_sum, mut_ties_to_higher_id, mut_tail_dropped,
+           mut_stop_block_excluded, mut_sub_block_shift, mut_eviction_forgets_old,
+           mut_attention_unscaled, mut_round_truncates, mut_parts_overlap, mut_mean_by_15,
+           mut_gamma_ignores_tail]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
+def test_mutant_is_caught(mutant):
+    O = fresh_oracle()
+    mutant(O)
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check(O)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no pin catches {mutant.__name__}"
