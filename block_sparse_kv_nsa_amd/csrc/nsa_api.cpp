@@ -1,0 +1,323 @@
+// C ABI of libnsa: argument validation (before any HIP call), workspace
+// layout queries and kernel dispatch.  See include/nsa.h for the contract.
+#include "nsa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "nsa_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nsa_status fail(nsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+nsa_status ok() {
+  g_last_error[0] = '\0';
+  return NSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define NSA_REQUIRE_PTR(p, align)                                                         \
+  do {                                                                                    \
+    if ((p) == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: `%s` is NULL", fn, #p); \
+    if (!aligned((p), (align)))                                                           \
+      return fail(NSA_ERR_INVALID_ARGUMENT, "%s: `%s` is not %d-byte aligned", fn, #p,    \
+                  (int)(align));                                                          \
+  } while (0)
+
+constexpr int kMaxBlocksPerSeq = 16384;
+constexpr int kMaxK = 4096;
+
+nsa_status check_shape(const char* fn, const nsa_shape* s) {
+  if (s == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: shape is NULL", fn);
+  if (s->batch < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: batch must be >= 1", fn);
+  if (s->num_kv_heads < 1 || s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT,
+                "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                s->num_q_heads, s->num_kv_heads);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: group size %d not built (1, 2, 4, 8)", fn, G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: head_dim %d not built (64, 128)", fn, s->head_dim);
+  if (s->block_size != 64)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: block_size must be 64 (got %d)", fn, s->block_size);
+  if (s->sub_block != 16)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: sub_block must be 16 (got %d)", fn, s->sub_block);
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > kMaxBlocksPerSeq)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_blocks_per_seq %d outside [1, %d]", fn,
+                s->max_blocks_per_seq, kMaxBlocksPerSeq);
+  if (s->num_phys_blocks < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: num_phys_blocks must be >= 1", fn);
+  if (s->dtype != NSA_F32 && s->dtype != NSA_BF16)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, s->dtype);
+  if (!(s->softmax_scale >= 0.f) || std::isinf(s->softmax_scale))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite and >= 0", fn);
+  return NSA_OK;
+}
+
+float scale_of(const nsa_shape* s) {
+  return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
+}
+
+nsa_status check_select_params(const char* fn, const nsa_select_params* p) {
+  if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: params is NULL", fn);
+  if (p->mode != NSA_SCORE_GROUP_SOFTMAX && p->mode != NSA_SCORE_FORECAST_RAW)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: unknown score mode %d", fn, p->mode);
+  if (p->k < 1 || p->k > kMaxK)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: k %d outside [1, %d]", fn, p->k, kMaxK);
+  if (p->k_e < 0 || p->k_e > p->k)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: k_e %d outside [0, k=%d]", fn, p->k_e, p->k);
+  if (p->ordered != 0 && p->ordered != 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: ordered must be 0 or 1", fn);
+  if (p->ordered && p->k_e != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: ordered mode takes no eviction set (k_e=0)", fn);
+  return NSA_OK;
+}
+
+nsa_status check_decode_params(const char* fn, const nsa_decode_params* p) {
+  if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: params is NULL", fn);
+  if (p->max_selected < 1 || p->max_selected > kMaxK)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_selected %d outside [1, %d]", fn,
+                p->max_selected, kMaxK);
+  if (p->early_stop != 0 && p->early_stop != 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: early_stop must be 0 or 1", fn);
+  if (!(p->tau >= 0.f) || std::isinf(p->tau))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: tau must be finite and >= 0", fn);
+  return NSA_OK;
+}
+
+bool env_trace() {
+  static const bool on = std::getenv("NSA_TRACE") != nullptr;
+  return on;
+}
+
+int env_int(const char* name) {
+  const char* v = std::getenv(name);
+  return v ? std::atoi(v) : 0;
+}
+
+nsa_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_status_string(nsa_status st) {
+  switch (st) {
+    case NSA_OK: return "NSA_OK";
+    case NSA_ERR_INVALID_ARGUMENT: return "NSA_ERR_INVALID_ARGUMENT";
+    case NSA_ERR_UNSUPPORTED: return "NSA_ERR_UNSUPPORTED";
+    case NSA_ERR_WORKSPACE_TOO_SMALL: return "NSA_ERR_WORKSPACE_TOO_SMALL";
+    case NSA_ERR_HIP: return "NSA_ERR_HIP";
+  }
+  return "NSA_ERR_UNKNOWN";
+}
+
+const char* nsa_last_error(void) { return g_last_error; }
+
+int32_t nsa_abi_version(void) { return NSA_ABI_VERSION; }
+
+nsa_status nsa_update_block_reps(const nsa_shape* shape, const void* k_pool,
+                                 const int32_t* block_table, const float* evict_logits,
+                                 const int32_t* first_block, const int32_t* num_blocks,
+                                 int32_t max_num_blocks, void* reps, float* evict_block_score,
+                                 hipStream_t stream) {
+  const char* fn = "nsa_update_block_reps";
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  NSA_REQUIRE_PTR(k_pool, 16);
+  NSA_REQUIRE_PTR(block_table, 4);
+  NSA_REQUIRE_PTR(first_block, 4);
+  NSA_REQUIRE_PTR(num_blocks, 4);
+  NSA_REQUIRE_PTR(reps, 16);
+  if ((evict_logits == nullptr) != (evict_block_score == nullptr))
+    return fail(NSA_ERR_INVALID_ARGUMENT,
+                "%s: evict_logits and evict_block_score must both be set or both NULL", fn);
+  if (evict_logits) {
+    NSA_REQUIRE_PTR(evict_logits, 4);
+    NSA_REQUIRE_PTR(evict_block_score, 4);
+  }
+  if (max_num_blocks < 0 || max_num_blocks > shape->max_blocks_per_seq)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_num_blocks %d outside [0, %d]", fn,
+                max_num_blocks, shape->max_blocks_per_seq);
+  if (max_num_blocks == 0) return ok();
+  nsa::RepsLaunch L{};
+  L.dtype = shape->dtype;
+  L.D = shape->head_dim;
+  L.k_pool = k_pool;
+  L.table = block_table;
+  L.logits = evict_logits;
+  L.first_block = first_block;
+  L.num_blocks = num_blocks;
+  L.reps = reps;
+  L.E = evict_block_score;
+  L.B = shape->batch;
+  L.Hkv = shape->num_kv_heads;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.max_num_blocks = max_num_blocks;
+  if (env_trace())
+    std::fprintf(stderr, "[nsa] reps grid=(%d,%d) D=%d dtype=%d\n", max_num_blocks,
+                 L.B * L.Hkv, L.D, L.dtype);
+  return launched(fn, nsa::launch_reps(L, stream));
+}
+
+static nsa_status select_layout_checked(const char* fn, const nsa_shape* shape,
+                                        const nsa_select_params* params, int32_t max_seq_len,
+                                        nsa::SelectLayout* lay) {
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  if (nsa_status st = check_select_params(fn, params)) return st;
+  if (max_seq_len < 1 || max_seq_len > shape->max_blocks_per_seq * 64)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_seq_len %d outside [1, %d]", fn, max_seq_len,
+                shape->max_blocks_per_seq * 64);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  *lay = nsa::select_layout(shape->batch, shape->num_kv_heads, G,
+                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len);
+  return NSA_OK;
+}
+
+nsa_status nsa_select_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
+                                      int32_t max_seq_len, size_t* bytes) {
+  const char* fn = "nsa_select_workspace_bytes";
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  nsa::SelectLayout lay;
+  if (nsa_status st = select_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
+  *bytes = lay.bytes;
+  return ok();
+}
+
+nsa_status nsa_select_blocks(const nsa_shape* shape, const nsa_select_params* params,
+                             const void* query, const void* reps, const float* evict_block_score,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t* evict_set,
+                             int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_select_blocks";
+  nsa::SelectLayout lay;
+  if (nsa_status st = select_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
+  NSA_REQUIRE_PTR(query, 16);
+  NSA_REQUIRE_PTR(reps, 16);
+  NSA_REQUIRE_PTR(seq_lens, 4);
+  NSA_REQUIRE_PTR(selected, 4);
+  NSA_REQUIRE_PTR(num_selected, 4);
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (params->k_e > 0) {
+    NSA_REQUIRE_PTR(evict_block_score, 4);
+    NSA_REQUIRE_PTR(evict_set, 4);
+    NSA_REQUIRE_PTR(evict_seen, 4);
+  }
+  if (workspace_bytes < lay.bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, lay.bytes);
+  nsa::SelectLaunch L{};
+  L.dtype = shape->dtype;
+  L.D = shape->head_dim;
+  L.G = shape->num_q_heads / shape->num_kv_heads;
+  L.mode = params->mode;
+  L.query = query;
+  L.reps = reps;
+  L.E = evict_block_score;
+  L.seq_lens = seq_lens;
+  L.evict_set = evict_set;
+  L.evict_seen = evict_seen;
+  L.selected = selected;
+  L.num_selected = num_selected;
+  L.workspace = workspace;
+  L.B = shape->batch;
+  L.Hkv = shape->num_kv_heads;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.k = params->k;
+  L.k_e = params->k_e;
+  L.ordered = params->ordered;
+  L.scale = scale_of(shape);
+  L.lay = lay;
+  if (env_trace())
+    std::fprintf(stderr, "[nsa] select grid=(%d,%d) chunk_reps=%d G=%d mode=%d k=%d k_e=%d ord=%d\n",
+                 lay.chunks, lay.rows, lay.chunk_reps, L.G, L.mode, L.k, L.k_e, L.ordered);
+  return launched(fn, nsa::launch_select(L, stream));
+}
+
+static nsa_status decode_layout_checked(const char* fn, const nsa_shape* shape,
+                                        const nsa_decode_params* params, nsa::DecodeLayout* lay) {
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  if (nsa_status st = check_decode_params(fn, params)) return st;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  *lay = nsa::decode_layout(shape->batch, shape->num_kv_heads, G, shape->head_dim,
+                            params->max_selected, params->early_stop != 0,
+                            env_int("NSA_DECODE_BPW"));
+  return NSA_OK;
+}
+
+nsa_status nsa_decode_workspace_bytes(const nsa_shape* shape, const nsa_decode_params* params,
+                                      size_t* bytes) {
+  const char* fn = "nsa_decode_workspace_bytes";
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  nsa::DecodeLayout lay;
+  if (nsa_status st = decode_layout_checked(fn, shape, params, &lay)) return st;
+  *bytes = lay.bytes;
+  return ok();
+}
+
+nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* params,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* selected, const int32_t* num_selected,
+                             int32_t* num_processed, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_sparse_decode";
+  nsa::DecodeLayout lay;
+  if (nsa_status st = decode_layout_checked(fn, shape, params, &lay)) return st;
+  NSA_REQUIRE_PTR(q, 16);
+  NSA_REQUIRE_PTR(k_pool, 16);
+  NSA_REQUIRE_PTR(v_pool, 16);
+  NSA_REQUIRE_PTR(block_table, 4);
+  NSA_REQUIRE_PTR(seq_lens, 4);
+  NSA_REQUIRE_PTR(selected, 4);
+  NSA_REQUIRE_PTR(num_selected, 4);
+  NSA_REQUIRE_PTR(out, 16);
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (params->early_stop) NSA_REQUIRE_PTR(num_processed, 4);
+  if (workspace_bytes < lay.bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, lay.bytes);
+  nsa::DecodeLaunch L{};
+  L.dtype = shape->dtype;
+  L.D = shape->head_dim;
+  L.G = shape->num_q_heads / shape->num_kv_heads;
+  L.q = q;
+  L.k_pool = k_pool;
+  L.v_pool = v_pool;
+  L.table = block_table;
+  L.seq_lens = seq_lens;
+  L.selected = selected;
+  L.num_selected = num_selected;
+  L.num_processed = num_processed;
+  L.out = out;
+  L.workspace = workspace;
+  L.B = shape->batch;
+  L.Hkv = shape->num_kv_heads;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.max_selected = params->max_selected;
+  L.early_stop = params->early_stop;
+  L.scale = scale_of(shape);
+  L.tau = params->tau;
+  L.lay = lay;
+  if (env_trace())
+    std::fprintf(stderr, "[nsa] decode grid=(%d,%d) bpw=%d G=%d D=%d early_stop=%d\n", lay.splits,
+                 lay.rows, lay.bpw, L.G, L.D, L.early_stop);
+  return launched(fn, nsa::launch_decode(L, stream));
+}
+
+}  // extern "C"

@@ -172,6 +172,8 @@ def block_scores_group_softmax(q: np.ndarray, reps: np.ndarray, scale: float) ->
     block maximum.
     """
     nb, nsub, d = reps.shape
+    if nb == 0:                       # no full block yet: nothing to score
+        return np.zeros(0)
     r = reps.reshape(nb * nsub, d)
     logits = (np.asarray(q, dtype=np.float64) @ r.T) * scale            # [G][4nb]
     logits = logits - logits.max(axis=1, keepdims=True)
