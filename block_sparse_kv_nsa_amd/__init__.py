@@ -23,6 +23,8 @@ from ._abi import (  # noqa: F401
     Shape,
     load,
     nsa_abi_version,
+    nsa_decode_step,
+    nsa_decode_step_workspace_bytes,
     nsa_decode_workspace_bytes,
     nsa_last_error,
     nsa_select_blocks,

@@ -14,7 +14,9 @@ import os
 
 import torch  # noqa: F401  (must precede loading libnsa; see module docstring)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
+# NSA_LIB_PATH selects another build of the library (e.g. a debug build)
+LIB_PATH = os.environ.get("NSA_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
 
 NSA_OK = 0
 NSA_ERR_INVALID_ARGUMENT = 1
@@ -34,6 +36,8 @@ EXPORTS = (
     "nsa_select_blocks",
     "nsa_decode_workspace_bytes",
     "nsa_sparse_decode",
+    "nsa_decode_step_workspace_bytes",
+    "nsa_decode_step",
     "nsa_status_string",
     "nsa_last_error",
     "nsa_abi_version",
@@ -94,7 +98,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m block_sparse_kv_nsa_amd.build`")
+                          "`python block_sparse_kv_nsa_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     P = ctypes.POINTER
@@ -110,6 +114,11 @@ def load() -> ctypes.CDLL:
     lib.nsa_sparse_decode.argtypes = [P(Shape), P(DecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
     lib.nsa_sparse_decode.restype = i32
+    lib.nsa_decode_step_workspace_bytes.argtypes = [P(Shape), P(SelectParams), i32, P(sz)]
+    lib.nsa_decode_step_workspace_bytes.restype = i32
+    lib.nsa_decode_step.argtypes = [P(Shape), P(SelectParams), vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                    vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nsa_decode_step.restype = i32
     lib.nsa_status_string.argtypes = [i32]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []
@@ -202,3 +211,24 @@ def nsa_sparse_decode(shape: Shape, params: DecodeParams, q, k_pool, v_pool, blo
                                   _ptr(out), _ptr(workspace), int(workspace_bytes),
                                   _stream(stream))
     _check(st, "nsa_sparse_decode")
+
+
+def nsa_decode_step_workspace_bytes(shape: Shape, params: SelectParams, max_seq_len: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().nsa_decode_step_workspace_bytes(ctypes.byref(shape), ctypes.byref(params),
+                                                int(max_seq_len), ctypes.byref(out))
+    _check(st, "nsa_decode_step_workspace_bytes")
+    return out.value
+
+
+def nsa_decode_step(shape: Shape, params: SelectParams, query, q, reps, evict_block_score,
+                    k_pool, v_pool, block_table, seq_lens, max_seq_len: int, evict_set,
+                    evict_seen, selected, num_selected, out, workspace, workspace_bytes: int,
+                    stream=None) -> None:
+    st = load().nsa_decode_step(ctypes.byref(shape), ctypes.byref(params), _ptr(query), _ptr(q),
+                                _ptr(reps), _ptr(evict_block_score), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_table), _ptr(seq_lens), int(max_seq_len),
+                                _ptr(evict_set), _ptr(evict_seen), _ptr(selected),
+                                _ptr(num_selected), _ptr(out), _ptr(workspace),
+                                int(workspace_bytes), _stream(stream))
+    _check(st, "nsa_decode_step")

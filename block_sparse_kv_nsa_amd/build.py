@@ -1,6 +1,8 @@
 """Build libnsa.so for gfx950 with hipcc (in-tree, next to this file).
 
-    python -m block_sparse_kv_nsa_amd.build [--debug]
+    python block_sparse_kv_nsa_amd/build.py [--debug]
+
+(run by path: importing the package itself loads the library being built)
 
 Every HIP source is compiled for gfx950 only; packed-fp32 instructions are
 turned off (-packed-fp32-ops).  Objects go to _build/ at the repository
@@ -23,7 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
 
-SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip"]
+SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip", "nsa_step.hip"]
 ARCH = "gfx950"
 
 

@@ -185,7 +185,8 @@ static nsa_status select_layout_checked(const char* fn, const nsa_shape* shape,
                 shape->max_blocks_per_seq * 64);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   *lay = nsa::select_layout(shape->batch, shape->num_kv_heads, G,
-                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len);
+                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len,
+                            env_int("NSA_SELECT_CHUNK"));
   return NSA_OK;
 }
 
@@ -318,6 +319,99 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
     std::fprintf(stderr, "[nsa] decode grid=(%d,%d) bpw=%d G=%d D=%d early_stop=%d\n", lay.splits,
                  lay.rows, lay.bpw, L.G, L.D, L.early_stop);
   return launched(fn, nsa::launch_decode(L, stream));
+}
+
+static nsa_status step_layout_checked(const char* fn, const nsa_shape* shape,
+                                      const nsa_select_params* params, int32_t max_seq_len,
+                                      nsa::StepLayout* lay) {
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  if (nsa_status st = check_select_params(fn, params)) return st;
+  if (params->ordered)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: the fused step takes the ascending mode only", fn);
+  if (max_seq_len < 1 || max_seq_len > shape->max_blocks_per_seq * 64)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_seq_len %d outside [1, %d]", fn, max_seq_len,
+                shape->max_blocks_per_seq * 64);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  *lay = nsa::step_layout(shape->batch, shape->num_kv_heads, G, shape->head_dim, params->k,
+                          params->k_e, max_seq_len, env_int("NSA_DECODE_BPW"));
+  if (lay->dyn_lds > 64 * 1024)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 65536)", fn,
+                lay->dyn_lds);
+  if (lay->bytes >= (size_t)1 << 32)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: workspace above 4 GiB", fn);
+  return NSA_OK;
+}
+
+nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
+                                           int32_t max_seq_len, size_t* bytes) {
+  const char* fn = "nsa_decode_step_workspace_bytes";
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  nsa::StepLayout lay;
+  if (nsa_status st = step_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
+  *bytes = lay.bytes;
+  return ok();
+}
+
+nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* params,
+                           const void* query, const void* q, const void* reps,
+                           const float* evict_block_score, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t* evict_set,
+                           int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "nsa_decode_step";
+  nsa::StepLayout lay;
+  if (nsa_status st = step_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
+  NSA_REQUIRE_PTR(query, 16);
+  NSA_REQUIRE_PTR(q, 16);
+  NSA_REQUIRE_PTR(reps, 16);
+  NSA_REQUIRE_PTR(k_pool, 16);
+  NSA_REQUIRE_PTR(v_pool, 16);
+  NSA_REQUIRE_PTR(block_table, 4);
+  NSA_REQUIRE_PTR(seq_lens, 4);
+  NSA_REQUIRE_PTR(selected, 4);
+  NSA_REQUIRE_PTR(num_selected, 4);
+  NSA_REQUIRE_PTR(out, 16);
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (params->k_e > 0) {
+    NSA_REQUIRE_PTR(evict_block_score, 4);
+    NSA_REQUIRE_PTR(evict_set, 4);
+    NSA_REQUIRE_PTR(evict_seen, 4);
+  }
+  if (workspace_bytes < lay.bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, lay.bytes);
+  nsa::StepLaunch L{};
+  L.dtype = shape->dtype;
+  L.D = shape->head_dim;
+  L.G = shape->num_q_heads / shape->num_kv_heads;
+  L.mode = params->mode;
+  L.query = query;
+  L.q = q;
+  L.reps = reps;
+  L.E = evict_block_score;
+  L.k_pool = k_pool;
+  L.v_pool = v_pool;
+  L.table = block_table;
+  L.seq_lens = seq_lens;
+  L.evict_set = evict_set;
+  L.evict_seen = evict_seen;
+  L.selected = selected;
+  L.num_selected = num_selected;
+  L.out = out;
+  L.workspace = workspace;
+  L.B = shape->batch;
+  L.Hkv = shape->num_kv_heads;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.k = params->k;
+  L.k_e = params->k_e;
+  L.scale = scale_of(shape);
+  L.lay = lay;
+  if (env_trace())
+    std::fprintf(stderr, "[nsa] step rows=%d chunks=%d mloc=%d bpw=%d splits=%d+%d lds=%zu\n",
+                 lay.rows, lay.chunks, lay.mloc, lay.bpw, lay.splitsE, lay.splitsQ, lay.dyn_lds);
+  return launched(fn, nsa::launch_step(L, stream));
 }
 
 }  // extern "C"

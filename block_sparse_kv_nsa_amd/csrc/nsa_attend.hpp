@@ -1,0 +1,281 @@
+// Attention over a list of 64-token key/value slabs for the G query heads of
+// one row, accumulated by one workgroup into an online-softmax partial, and
+// the merge of such partials.  Shared by the split-K decode kernel and the
+// fused decode-step kernel.
+//
+// Layout inside the workgroup: each wave owns 16 of a slab's 64 token rows.
+//   * keys: 4 lanes per token (64 contiguous bytes per token and load); each
+//     lane forms partial q.k for every head and a quad transpose-reduction
+//     leaves one (token, head) logit per lane;
+//   * values: a full row per LPR lanes (coalesced 16-byte loads); weights move
+//     from the key layout to the value layout through 16 x G floats of LDS
+//     per wave.
+// Logits are in base-2 units (scale*log2(e) folded in).  The reference
+// maximum is lazy: weights are taken against a wave-uniform reference per
+// head that is raised (and the accumulators rescaled) only when a logit
+// exceeds it by more than 8, so weights stay <= 2^8 and the common slab needs
+// no cross-lane maximum.
+#pragma once
+
+#include "nsa_device.hpp"
+
+namespace nsa {
+
+constexpr float kLazyMax = 8.f;  // log2 headroom before the reference moves
+
+template <typename T, int D>
+struct VGeo {
+  static constexpr int EPL = Fmt<T>::kPer16B;  // elements per lane per load
+  static constexpr int LPR = D / EPL;          // lanes per value row
+  static constexpr int TPL = kWave / LPR;      // value rows per wave load
+  static constexpr int NLV = kSub / TPL;       // value loads per lane per slab
+};
+
+struct Item {
+  int64_t base;          // element offset of the (block, KV head) slab
+  int valid;             // token rows in use (64, or the tail length)
+  const float* logits;   // precomputed logits [G][64] (early-stop pass 2), else null
+};
+
+template <typename T, int D, int G>
+struct AttendSmem {
+  float p_lds[kWaves][kSub][G];
+  float wm[kWaves][G], wl[kWaves][G];
+  float wacc[kWaves][G][D];
+};
+
+// Accumulate items [i0, i1) (item(it) -> Item) and store the workgroup's
+// (m, l) and acc[D] per head at partial index pidx with agent-scope stores.
+// With PRE the logits come from Item::logits instead of q . k.
+template <typename T, int D, int G, bool PRE, typename ItemFn>
+__device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
+                             ItemFn item, AttendSmem<T, D, G>& sm, __amdgpu_buffer_rsrc_t mlr,
+                             __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
+  using Q = Quad<T, D>;
+  using V = VGeo<T, D>;
+  constexpr int NLD = Q::NLD, EPL = V::EPL, LPR = V::LPR, TPL = V::TPL, NLV = V::NLV;
+  constexpr int KEEP = G >= 4 ? G / 4 : 1;
+  constexpr int DUP = G >= 4 ? 1 : 4 / G;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int q = lane & 3, r = lane >> 2;        // key layout: token wave*16 + r
+  const int sl = lane % LPR, grp = lane / LPR;  // value layout
+  const int h0 = G >= 4 ? q * KEEP : q / DUP;
+  const bool canon = (q % DUP) == 0;
+  const int tk = wave * kSub + r;
+
+  QSlice<T, D> qs[G];
+  if constexpr (!PRE) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) qs[h].load(qrow + h * D, q);
+  }
+
+  float m[G], l[G], acc[G][EPL], mref[KEEP];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KEEP; ++kk) mref[kk] = -INFINITY;
+
+  auto issue = [&](int it, uint4 (&kx)[NLD], uint4 (&vx)[NLV], Item& itm) {
+    itm = item(it);
+    if constexpr (!PRE) {
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld)
+        kx[ld] = load16_stream(kp + itm.base + (int64_t)tk * D + Q::elem(ld, q));
+    }
+#pragma unroll
+    for (int u = 0; u < NLV; ++u)
+      vx[u] = load16_stream(vp + itm.base + (int64_t)(wave * kSub + u * TPL + grp) * D + sl * EPL);
+  };
+
+  auto consume = [&](const Item& itm, const uint4 (&kx)[NLD], const uint4 (&vx)[NLV]) {
+    float lg[KEEP];
+    if constexpr (!PRE) {
+      float v[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
+      quad_reduce<2, G>(v, q);
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) lg[kk] = v[kk] * qscale;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) lg[kk] = itm.logits[(h0 + kk) * kBlock + tk];
+    }
+    bool over = false;
+#pragma unroll
+    for (int kk = 0; kk < KEEP; ++kk) {
+      if (tk >= itm.valid) lg[kk] = -INFINITY;
+      over |= lg[kk] > mref[kk] + kLazyMax;
+    }
+    if (__any(over)) {  // wave-uniform: raise the reference, rescale
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < KEEP; ++kk)
+          if (h0 + kk == h) bm = fmaxf(bm, lg[kk]);
+        bm = wave_max(bm);
+        const float mn = fmaxf(m[h], bm);
+        if (mn > m[h]) {
+          const float alpha = m[h] == -INFINITY ? 0.f : exp2f(m[h] - mn);
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          m[h] = mn;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KEEP; ++kk)
+          if (h0 + kk == h) mref[kk] = m[h];
+      }
+    }
+    if (canon) {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk)
+        sm.p_lds[wave][r][h0 + kk] = lg[kk] == -INFINITY ? 0.f : fast_exp2(lg[kk] - mref[kk]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float pv[NLV][G];
+#pragma unroll
+    for (int u = 0; u < NLV; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[u][h] = sm.p_lds[wave][u * TPL + grp][h];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < NLV; ++u) {
+      float vf[EPL];
+      unpack<T>(vx[u], vf);
+      // rows past the tail may hold anything (even NaN): keep them out of acc
+      if (wave * kSub + u * TPL + grp >= itm.valid) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] += pv[u][h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[u][h], vf[e], acc[h][e]);
+      }
+    }
+  };
+
+  if constexpr (G < 8) {
+    // next slab's loads in flight while the current one is consumed
+    uint4 ka[NLD], va[NLV], kb[NLD], vb[NLV];
+    Item ia, ib;
+    if (i0 < i1) issue(i0, ka, va, ia);
+    for (int it = i0; it < i1; it += 2) {
+      if (it + 1 < i1) issue(it + 1, kb, vb, ib);
+      consume(ia, ka, va);
+      if (it + 1 < i1) {
+        if (it + 2 < i1) issue(it + 2, ka, va, ia);
+        consume(ib, kb, vb);
+      }
+    }
+  } else {
+    // 8 heads: the query slices and accumulators leave no room for a second slab
+    for (int it = i0; it < i1; ++it) {
+      uint4 ka[NLD], va[NLV];
+      Item ia;
+      issue(it, ka, va, ia);
+      consume(ia, ka, va);
+    }
+  }
+
+  // wave partial: l and acc summed over the value-layout token groups
+  // (each group counted its own rows; m is wave-uniform)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) {
+      l[h] += __shfl_xor(l[h], off, kWave);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, kWave);
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm.wacc[wave][h][sl * EPL + e] = acc[h][e];
+      if (sl == 0) {
+        sm.wm[wave][h] = m[h];
+        sm.wl[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
+    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
+    float M = sm.wm[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][h]);
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (sm.wm[w][h] == -INFINITY) continue;
+        const float f = exp2f(sm.wm[w][h] - M);
+        A.x = fmaf(sm.wacc[w][h][c], f, A.x);
+        A.y = fmaf(sm.wacc[w][h][c + 1], f, A.y);
+        A.z = fmaf(sm.wacc[w][h][c + 2], f, A.z);
+        A.w = fmaf(sm.wacc[w][h][c + 3], f, A.w);
+        Ls = fmaf(sm.wl[w][h], f, Ls);
+      }
+    }
+    store_agent_f32x4(acr, (uint32_t)(((pidx * G + h) * D + c) * 4), A);
+    if (c == 0) store_agent_f32x2(mlr, (uint32_t)((pidx * G + h) * 8), f32x2{M, Ls});
+  }
+}
+
+// Merge partials [p0, p0 + nparts) (agent-scope loads) into out[G][D]:
+// 4 channels per thread, partials 4 at a time with their loads in flight
+// together, merged with a running maximum.
+template <typename T, int D, int G>
+__device__ void combine_partials(int64_t p0, int nparts, __amdgpu_buffer_rsrc_t mlr,
+                                 __amdgpu_buffer_rsrc_t acr, T* out) {
+  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
+    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
+    float M = -INFINITY, den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kB = 4;
+    for (int s0 = 0; s0 < nparts; s0 += kB) {
+      f32x2 ml[kB];
+      f32x4 ac[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int64_t pb = p0 + min(s0 + k, nparts - 1);
+        ml[k] = load_agent_f32x2(mlr, (uint32_t)((pb * G + h) * 8));
+        ac[k] = load_agent_f32x4(acr, (uint32_t)(((pb * G + h) * D + c) * 4));
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        if (s0 + k >= nparts || ml[k].x == -INFINITY) continue;
+        if (ml[k].x > M) {
+          const float sc = M == -INFINITY ? 0.f : exp2f(M - ml[k].x);
+          num *= sc;
+          den *= sc;
+          M = ml[k].x;
+        }
+        const float f = exp2f(ml[k].x - M);
+        num += ac[k] * f;
+        den = fmaf(ml[k].y, f, den);
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    out[h * D + c] = from_f32<T>(num.x * inv);
+    out[h * D + c + 1] = from_f32<T>(num.y * inv);
+    out[h * D + c + 2] = from_f32<T>(num.z * inv);
+    out[h * D + c + 3] = from_f32<T>(num.w * inv);
+  }
+}
+
+}  // namespace nsa

@@ -2,27 +2,24 @@
 //
 // Decode reads each selected 64 x D key/value slab once and does 2*G flops
 // per element read (G <= 8 query heads share the slab), far below the fp32
-// vector ridge, so this is a bandwidth-bound GEMV: plain FMA, no MFMA.
-// Slabs are gathered through the block table (S2O technical summary,
+// vector ridge, so this is a bandwidth-bound GEMV: plain FMA / bf16 dot2, no
+// MFMA.  Slabs are gathered through the block table (S2O technical summary,
 // "Permutazione Online": keep the physical layout, load through index
 // arrays), and the online-softmax state (m, l, acc) is the one S2O's kernel
 // carries between its passes ("Implementazione del Kernel").
 //
 // Work split (split-K flash decoding): a grid of (split, row) workgroups;
 // split s takes `bpw` consecutive items of the row's list (the selected
-// blocks in list order, then the tail block).  Inside a workgroup each wave
-// owns 16 of the 64 token rows of every slab; LPR lanes cover one token row
-// with 16-byte loads, so a wave load instruction reads TPL whole contiguous
-// token rows.  Logits are kept in base-2 units (q pre-scaled by
-// scale*log2(e)) so every exponential is a native exp2.  Each workgroup writes
-// one (m, l, acc[D]) partial per head; the last workgroup of the row (atomic
-// ticket) merges them and writes the output.
+// blocks in list order, then the tail block), prefetching the next item's
+// slabs while it computes the current one (attend_items); the last workgroup
+// of each row (atomic ticket) merges the partials and writes the output.
 //
 // Early stop (S2O summary, "Regola di Arresto Anticipato"): pass 1
 // (es_mass_kernel) computes every listed block's logits and per-head
 // (max, sum) and the row's last workgroup finds the stop position n*;
 // pass 2 is the decode kernel reading those logits instead of keys and
 // attending only the first n* listed blocks and the tail.
+#include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
 
@@ -40,33 +37,26 @@ struct DecodeArgs {
   int32_t* num_processed;
   void* out;
   uint32_t* counters;
-  float2* part_ml;       // [rows][splits][G]
+  float* part_ml;        // [rows][splits][G][2]
   float* part_acc;       // [rows][splits][G][D]
   float* es_logits;      // [rows][items_max][G][64]
-  float2* es_ml;         // [rows][items_max][G]
+  float* es_ml;          // [rows][items_max][G][2]
   int Hkv, max_blocks, max_selected, items_max, bpw;
   float qscale, tau;
 };
 
-template <typename T, int D>
-struct Geo {
-  static constexpr int EPL = Fmt<T>::kPer16B;  // elements per lane per load
-  static constexpr int LPR = D / EPL;          // lanes per token row
-  static constexpr int TPL = kWave / LPR;      // token rows per wave load
-  static constexpr int NL = kSub / TPL;        // loads per wave per slab (16 rows)
-};
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, int sl,
-                                           float (&qv)[G][Geo<T, D>::EPL]) {
-  constexpr int EPL = Geo<T, D>::EPL;
-  const T* qb = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    unpack<T>(load16(qb + h * D + sl * EPL), qv[h]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
-  }
+// item `it` of a row's list: listed blocks first, then the tail block
+__device__ __forceinline__ Item item_at(const DecodeArgs& a, int row, int b, int g, int it,
+                                        int nsel, int nb, int tail, int D, int64_t* idx_out) {
+  const bool is_tail = it >= nsel;
+  const int blk = is_tail ? nb : a.selected[(int64_t)row * a.max_selected + it];
+  const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
+  Item x;
+  x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
+  x.valid = is_tail ? tail : kBlock;
+  x.logits = nullptr;
+  *idx_out = it;
+  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -74,12 +64,6 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, in
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G, bool ES>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  using Gm = Geo<T, D>;
-  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, TPL = Gm::TPL, NL = Gm::NL;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int sl = lane % LPR, grp = lane / LPR;
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
   const int L = a.seq_lens[b];
@@ -91,173 +75,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int i0 = split * a.bpw;
   const int i1 = min(i0 + a.bpw, n_items);
 
-  __shared__ float wm[kWaves][G], wl[kWaves][G];
-  __shared__ float wacc[kWaves][G][D];
+  __shared__ AttendSmem<T, D, G> sm;
   __shared__ int s_flag;
 
-  float qv[G][EPL];
-  if constexpr (!ES) load_query<T, D, G>(a, b, g, sl, qv);
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-
-  const int32_t* sel = a.selected + (int64_t)row * a.max_selected;
-  for (int it = i0; it < i1; ++it) {
-    const bool is_tail = it >= nsel;
-    const int blk = is_tail ? nb : sel[it];
-    const int valid = is_tail ? tail : kBlock;
-    const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
-    const int64_t base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
-
-    uint4 kr[NL], vr[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = wave * kSub + i * TPL + grp;
-      const int64_t off = base + (int64_t)t * D + sl * EPL;
-      if constexpr (!ES) kr[i] = load16_stream(static_cast<const T*>(a.k_pool) + off);
-      vr[i] = load16_stream(static_cast<const T*>(a.v_pool) + off);
-    }
-
-    float s[NL][G];
-    if constexpr (!ES) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float x[EPL];
-        unpack<T>(kr[i], x);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], x[e], d);
-          s[i][h] = group_sum<LPR>(d);
-        }
-      }
-    } else {
-      const int item = is_tail ? nlisted : it;  // pass 1 stored the tail after the list
-      const float* lp = a.es_logits + ((int64_t)row * a.items_max + item) * G * kBlock;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int t = wave * kSub + i * TPL + grp;
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = lp[h * kBlock + t];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = wave * kSub + i * TPL + grp;
-      if (t >= valid) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
-      }
-    }
-
-    float vf[NL][EPL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      unpack<T>(vr[i], vf[i]);
-      // rows past the tail may hold anything (even NaN): keep them out of acc
-      if (wave * kSub + i * TPL + grp >= valid) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = s[0][h];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
-      mx = across_groups_max<LPR>(mx);
-      const float mn = fmaxf(m[h], mx);
-      if (mn == -INFINITY) continue;  // wave-uniform: nothing valid yet
-      const float alpha = exp2f(m[h] - mn);
-      float lsum = l[h] * alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float p = exp2f(s[i][h] - mn);
-        lsum += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
-      }
-      l[h] = lsum;
-      m[h] = mn;
-    }
-  }
-
-  // wave partial: sum the token groups (m is already wave-uniform)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = across_groups_sum<LPR>(l[h]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = across_groups_sum<LPR>(acc[h][e]);
-  }
-  if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) wacc[wave][h][sl * EPL + e] = acc[h][e];
-      if (sl == 0) {
-        wm[wave][h] = m[h];
-        wl[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-
-  // workgroup partial
   const int splits = gridDim.x;
-  float2* pml = a.part_ml + ((int64_t)row * splits + split) * G;
-  float* pacc = a.part_acc + ((int64_t)row * splits + split) * G * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, c = idx % D;
-    float M = wm[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][h]);
-    float A = 0.f, Ls = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (wm[w][h] == -INFINITY) continue;
-        const float f = exp2f(wm[w][h] - M);
-        A = fmaf(wacc[w][h][c], f, A);
-        Ls = fmaf(wl[w][h], f, Ls);
-      }
+  const __amdgpu_buffer_rsrc_t mlr =
+      make_rsrc(a.part_ml, (uint32_t)((int64_t)gridDim.y * splits * G * 8));
+  const __amdgpu_buffer_rsrc_t acr =
+      make_rsrc(a.part_acc, (uint32_t)((int64_t)gridDim.y * splits * G * D * 4));
+  const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
+  auto item = [&](int it) {
+    int64_t idx;
+    Item x = item_at(a, row, b, g, it, nsel, nb, tail, D, &idx);
+    if constexpr (ES) {
+      // pass 1 stored the tail after the whole list
+      const int pos = it >= nsel ? nlisted : it;
+      x.logits = a.es_logits + ((int64_t)row * a.items_max + pos) * G * kBlock;
     }
-    pacc[idx] = A;
-    if (c == 0) pml[h] = make_float2(M, Ls);
-  }
+    return x;
+  };
+  attend_items<T, D, G, ES>(qrow, static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
+                            a.qscale, i0, i1, item, sm, mlr, acr, (int64_t)row * splits + split);
 
-  if (!last_of_row(a.counters + row, splits, &s_flag)) return;
-
-  // combine the row's partials
-  const int Hq = a.Hkv * G;
-  T* out = static_cast<T*>(a.out) + ((int64_t)b * Hq + g * G) * D;
-  const float2* rml = a.part_ml + (int64_t)row * splits * G;
-  const float* racc = a.part_acc + (int64_t)row * splits * G * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D;
-    float M = -INFINITY;
-    for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, rml[sp * G + h].x);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int sp = 0; sp < splits; ++sp) {
-        const float2 ml = rml[sp * G + h];
-        if (ml.x == -INFINITY) continue;
-        const float f = exp2f(ml.x - M);
-        num = fmaf(racc[(int64_t)sp * G * D + idx], f, num);
-        den = fmaf(ml.y, f, den);
-      }
-    }
-    out[idx] = from_f32<T>(den > 0.f ? num / den : 0.f);
-  }
+  if (!last_arrival(a.counters + row, splits, &s_flag)) return;
+  T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
+  combine_partials<T, D, G>((int64_t)row * splits, splits, mlr, acr, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -288,12 +130,14 @@ __device__ __forceinline__ float block_inclusive_scan_f(float v, float* sm /*kWa
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
-  using Gm = Geo<T, D>;
-  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, TPL = Gm::TPL, NL = Gm::NL;
+  using Q = Quad<T, D>;
+  constexpr int NLD = Q::NLD;
+  constexpr int KEEP = G >= 4 ? G / 4 : 1;
+  constexpr int DUP = G >= 4 ? 1 : 4 / G;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int sl = lane % LPR, grp = lane / LPR;
+  const int q = lane & 3, r = lane >> 2;
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
   const int L = a.seq_lens[b];
@@ -303,53 +147,52 @@ __global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
   const int n_items = nsel + (tail > 0);
   const int i0 = split * a.bpw;
   const int i1 = min(i0 + a.bpw, n_items);
+  const int h0 = G >= 4 ? q * KEEP : q / DUP;
+  const bool canon = (q % DUP) == 0;
+  const int tk = wave * kSub + r;
 
   __shared__ float red[kWaves][G];
   __shared__ float scan_sm[kWaves];
   __shared__ float sc[G], sT[G], carry[G];
   __shared__ int s_flag, s_stop;
 
-  float qv[G][EPL];
-  load_query<T, D, G>(a, b, g, sl, qv);
+  QSlice<T, D> qs[G];
+  {
+    const T* qb = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qs[h].load(qb + h * D, q);
+  }
+  const T* kp = static_cast<const T*>(a.k_pool);
+  const uint32_t ml_bytes = (uint32_t)((int64_t)gridDim.y * a.items_max * G * 8);
+  const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.es_ml, ml_bytes);
 
-  const int32_t* sel = a.selected + (int64_t)row * a.max_selected;
   for (int it = i0; it < i1; ++it) {
-    const bool is_tail = it >= nsel;
-    const int blk = is_tail ? nb : sel[it];
-    const int valid = is_tail ? tail : kBlock;
-    const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
-    const int64_t base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
-    uint4 kr[NL];
+    int64_t pos;
+    const Item itm = item_at(a, row, b, g, it, nsel, nb, tail, D, &pos);
+    uint4 kx[NLD];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = wave * kSub + i * TPL + grp;
-      kr[i] = load16_stream(static_cast<const T*>(a.k_pool) + base + (int64_t)t * D + sl * EPL);
-    }
-    float s[NL][G];
-    float* lp = a.es_logits + ((int64_t)row * a.items_max + it) * G * kBlock;
+    for (int ld = 0; ld < NLD; ++ld)
+      kx[ld] = load16_stream(kp + itm.base + (int64_t)tk * D + Q::elem(ld, q));
+    float v[G];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = wave * kSub + i * TPL + grp;
-      float x[EPL];
-      unpack<T>(kr[i], x);
+    for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
+    quad_reduce<2, G>(v, q);
+    float lg[KEEP];
+    float* lp = a.es_logits + ((int64_t)row * a.items_max + pos) * G * kBlock;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], x[e], d);
-        d = group_sum<LPR>(d);
-        s[i][h] = t < valid ? d : -INFINITY;
-        if (sl == 0) lp[h * kBlock + t] = s[i][h];
-      }
+    for (int kk = 0; kk < KEEP; ++kk) {
+      lg[kk] = tk < itm.valid ? v[kk] * a.qscale : -INFINITY;
+      if (canon) lp[(h0 + kk) * kBlock + tk] = lg[kk];
     }
     // per-head block max, then sum of 2^(s - max)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = s[0][h];
+      float x = -INFINITY;
 #pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
-      mx = across_groups_max<LPR>(mx);
-      if (lane == 0) red[wave][h] = mx;
+      for (int kk = 0; kk < KEEP; ++kk)
+        if (h0 + kk == h && canon) x = fmaxf(x, lg[kk]);
+      x = wave_max(x);
+      if (lane == 0) red[wave][h] = x;
     }
     __syncthreads();
     float bm[G];
@@ -363,12 +206,11 @@ __global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float ps = 0.f;
-      if (bm[h] != -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) ps += exp2f(s[i][h] - bm[h]);
-      }
-      // every lane of a group holds the same values: count each token once
-      ps = across_groups_sum<LPR>(ps);
+      for (int kk = 0; kk < KEEP; ++kk)
+        if (h0 + kk == h && canon && bm[h] != -INFINITY) ps += exp2f(lg[kk] - bm[h]);
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) ps += __shfl_xor(ps, off, kWave);
       if (lane == 0) red[wave][h] = ps;
     }
     __syncthreads();
@@ -377,25 +219,28 @@ __global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
       float tot = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) tot += red[w][h];
-      a.es_ml[((int64_t)row * a.items_max + it) * G + h] = make_float2(bm[h], tot);
+      store_agent_f32x2(mlr, (uint32_t)((((int64_t)row * a.items_max + pos) * G + h) * 8),
+                        f32x2{bm[h], tot});
     }
     __syncthreads();
   }
 
-  if (!last_of_row(a.counters + row, gridDim.x, &s_flag)) return;
+  if (!last_arrival(a.counters + row, gridDim.x, &s_flag)) return;
 
   // stop position: c_h = row max logit; T_h = tail mass; A_h(n) = T_h + sum
   // of the first n block masses; n* = first n with M_h(n) < tau*A_h(n) for
   // every head, else nsel
-  const float2* ml = a.es_ml + (int64_t)row * a.items_max * G;
+  auto ml_at = [&](int item, int h) {
+    return load_agent_f32x2(mlr, (uint32_t)((((int64_t)row * a.items_max + item) * G + h) * 8));
+  };
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float c = -INFINITY;
-    for (int i = 0; i < n_items; ++i) c = fmaxf(c, ml[i * G + h].x);
+    for (int i = 0; i < n_items; ++i) c = fmaxf(c, ml_at(i, h).x);
     sc[h] = c;
     float tmass = 0.f;
     if (tail > 0) {
-      const float2 v = ml[nsel * G + h];
+      const f32x2 v = ml_at(nsel, h);
       tmass = v.x == -INFINITY ? 0.f : v.y * exp2f(v.x - c);
     }
     sT[h] = tmass;
@@ -410,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h) {
       float mass = 0.f;
       if (n <= nsel) {
-        const float2 v = ml[(n - 1) * G + h];
+        const f32x2 v = ml_at(n - 1, h);
         mass = v.x == -INFINITY ? 0.f : v.y * exp2f(v.x - sc[h]);
       }
       float tot;
@@ -442,10 +287,10 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   a.out = L.out;
   char* ws = static_cast<char*>(L.workspace);
   a.counters = reinterpret_cast<uint32_t*>(ws);
-  a.part_ml = reinterpret_cast<float2*>(ws + lay.off_ml);
+  a.part_ml = reinterpret_cast<float*>(ws + lay.off_ml);
   a.part_acc = reinterpret_cast<float*>(ws + lay.off_acc);
   a.es_logits = reinterpret_cast<float*>(ws + lay.off_es_logits);
-  a.es_ml = reinterpret_cast<float2*>(ws + lay.off_es_ml);
+  a.es_ml = reinterpret_cast<float*>(ws + lay.off_es_ml);
   a.Hkv = L.Hkv;
   a.max_blocks = L.max_blocks;
   a.max_selected = L.max_selected;

@@ -113,29 +113,6 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 // ---------------------------------------------------------------------------
 // wavefront helpers
 // ---------------------------------------------------------------------------
-template <int kWidth>
-__device__ __forceinline__ float group_sum(float v) {
-  // sum over aligned groups of kWidth lanes (kWidth a power of two <= 64)
-#pragma unroll
-  for (int off = 1; off < kWidth; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-template <int kFrom>
-__device__ __forceinline__ float across_groups_max(float v) {
-  // max over lanes that share (lane % kFrom)
-#pragma unroll
-  for (int off = kFrom; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
-template <int kFrom>
-__device__ __forceinline__ float across_groups_sum(float v) {
-#pragma unroll
-  for (int off = kFrom; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // Merge two (max, sum of 2^(x - max)) pairs.
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
@@ -147,34 +124,6 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
 // ---------------------------------------------------------------------------
 // workgroup helpers (kThreads threads)
 // ---------------------------------------------------------------------------
-struct ScanSmem {
-  int wave_tot[kWaves];
-};
-
-// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, ScanSmem& sm, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(x, off, kWave);
-    if (lane >= off) x += t;
-  }
-  if (lane == kWave - 1) sm.wave_tot[wave] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = sm.wave_tot[w];
-    before += (w < wave) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x - v;
-}
-
 // Order-preserving map float -> uint32 (larger float, larger key; -0 == +0).
 // Real keys are >= 0x007FFFFF, so 0 marks an excluded entry.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -182,126 +131,318 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-struct SelectSmem {
-  uint32_t hist[256];
-  int digit;
-  int above;
-  ScanSmem scan;
-};
+// ---------------------------------------------------------------------------
+// single-wave top-m selection over keys in LDS (no workgroup barriers)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v &= (uint32_t)__shfl_xor((int)v, off, kWave);
+  return v;
+}
 
-// Find the m-th largest key among keys[0..n) (1 <= m <= n): 4 passes of an
-// 8-bit most-significant-digit radix select with LDS histograms.  Returns the
-// threshold key T; *take_eq = how many entries equal to T belong to the top m
-// (the lowest-index ones, which gives ties to the lower index).
-__device__ uint32_t radix_select(const uint32_t* keys, int n, int m, SelectSmem& sm,
-                                 int* take_eq) {
-  uint32_t prefix = 0, mask = 0;
-  int remaining = m;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+// Called by all 64 lanes of one wave.  Finds the m-th largest of keys[0..n)
+// (1 <= m <= number of nonzero keys; a zero key marks an excluded entry and
+// is never chosen) with an MSD radix select whose first digit starts at the
+// highest bit where the keys differ (scores of one row share their top bits,
+// so a fixed first digit would send every key to one histogram bin), then
+// visits the chosen entries in index order -- all keys above the threshold
+// and the lowest-index entries equal to it -- calling emit(i, rank).
+// Keys are taken kTile per lane at a time into registers (index
+// tile*64*kTile + j*64 + lane), so LDS latency is paid once per tile and the
+// histogram atomics issue back to back.  hist: 256 words of LDS for this wave.
+template <typename Emit>
+__device__ void wave_top_m(const uint32_t* keys, int n, int m, uint32_t* hist, Emit emit) {
+  constexpr int kTile = 32;
+  constexpr int kSpan = kTile * kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  auto load_tile = [&](int t0, uint32_t (&kr)[kTile]) {
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      const int i = t0 + j * kWave + lane;
+      kr[j] = i < n ? keys[i] : 0u;
     }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      // lane l owns digits 4l..4l+3; count entries with a larger digit
-      const int l = threadIdx.x;
-      const int c0 = sm.hist[4 * l], c1 = sm.hist[4 * l + 1], c2 = sm.hist[4 * l + 2],
-                c3 = sm.hist[4 * l + 3];
-      const int mine = c0 + c1 + c2 + c3;
-      // suffix sum over lanes l+1..63
+  };
+  uint32_t kor = 0u, kand = ~0u;
+  for (int t0 = 0; t0 < n; t0 += kSpan) {
+    uint32_t kr[kTile];
+    load_tile(t0, kr);
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      if (kr[j] != 0u) {  // 0 marks an excluded entry
+        kor |= kr[j];
+        kand &= kr[j];
+      }
+    }
+  }
+  kor = wave_or(kor);
+  kand = wave_and(kand);
+  uint32_t T, prefix = 0u, mask = 0u;
+  int take_eq = m;
+  const uint32_t diff = kor ^ kand;
+  if (diff == 0u) {
+    T = kor;  // all candidate keys equal: the lowest m indices
+  } else {
+    int hi = 31 - __builtin_clz(diff);
+    mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    prefix = kand & mask;
+    int remaining = m;
+    while (true) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+#pragma unroll
+      for (int i = 0; i < 256 / kWave; ++i) hist[i * kWave + lane] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int t0 = 0; t0 < n; t0 += kSpan) {
+        uint32_t kr[kTile];
+        load_tile(t0, kr);
+#pragma unroll
+        for (int j = 0; j < kTile; ++j)
+          if (kr[j] != 0u && (kr[j] & mask) == prefix) atomicAdd(&hist[(kr[j] >> lo) & dmask], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+      // lane l owns digits 4l..4l+3: entries with a larger digit, then pick
+      const uint4 c = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+      const int mine = (int)(c.x + c.y + c.z + c.w);
       int x = mine;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int t = __shfl_down(x, off, kWave);
-        if (l + off < kWave) x += t;
+        if (lane + off < kWave) x += t;
       }
-      int above = x - mine;  // entries with digit >= 4(l+1)
-      // digits 4l+3 .. 4l, high to low
-      const int cs[4] = {c0, c1, c2, c3};
+      int above = x - mine;
+      int found_digit = -1, found_above = 0;
+      const int cs[4] = {(int)c.x, (int)c.y, (int)c.z, (int)c.w};
 #pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (above < remaining && remaining <= above + cs[q]) {
-          sm.digit = 4 * l + q;
-          sm.above = above;
+      for (int qd = 3; qd >= 0; --qd) {
+        if (above < remaining && remaining <= above + cs[qd]) {
+          found_digit = 4 * lane + qd;
+          found_above = above;
         }
-        above += cs[q];
+        above += cs[qd];
       }
+      const uint64_t who = __ballot(found_digit >= 0);
+      const int src = __builtin_ctzll(who);
+      const int digit = __shfl(found_digit, src, kWave);
+      const int abv = __shfl(found_above, src, kWave);
+      prefix |= (uint32_t)digit << lo;
+      mask |= dmask << lo;
+      remaining -= abv;
+      if (lo == 0) break;
+      hi = lo - 1;
     }
-    __syncthreads();
-    prefix |= (uint32_t)sm.digit << shift;
-    mask |= 255u << shift;
-    remaining -= sm.above;
-    __syncthreads();
+    T = prefix;
+    take_eq = remaining;
   }
-  *take_eq = remaining;
-  return prefix;
-}
-
-// Visit the top-m entries chosen by radix_select in index order; emit(i, pos)
-// receives the entry index and its rank in index order.  Returns m.
-template <typename Emit>
-__device__ int compact_selected(const uint32_t* keys, int n, uint32_t T, int take_eq,
-                                ScanSmem& sm, Emit emit) {
-  const int per = (n + kThreads - 1) / kThreads;
-  const int s0 = min(n, (int)threadIdx.x * per), s1 = min(n, s0 + per);
-  int eq = 0;
-  for (int i = s0; i < s1; ++i) eq += keys[i] == T;
-  int tot;
-  int eq_before = block_exclusive_scan(eq, sm, &tot);
-  int cnt = 0;
-  {
-    int e = eq_before;
-    for (int i = s0; i < s1; ++i) {
-      const uint32_t key = keys[i];
-      if (key > T) {
-        ++cnt;
-      } else if (key == T) {
-        cnt += (e < take_eq);
-        ++e;
-      }
+  // emit in index order
+  int eq_seen = 0, taken = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int t0 = 0; t0 < n; t0 += kSpan) {
+    uint32_t kr[kTile];
+    load_tile(t0, kr);
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      const bool gt = kr[j] > T;
+      const bool eq = kr[j] == T && kr[j] != 0u;
+      const uint64_t eqm = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(eqm & below);
+      const bool take = gt || (eq && eq_rank < take_eq);
+      const uint64_t tk = __ballot(take);
+      if (take) emit(t0 + j * kWave + lane, taken + __popcll(tk & below));
+      eq_seen += __popcll(eqm);
+      taken += __popcll(tk);
     }
   }
-  int total;
-  int pos = block_exclusive_scan(cnt, sm, &total);
-  {
-    int e = eq_before;
-    for (int i = s0; i < s1; ++i) {
-      const uint32_t key = keys[i];
-      bool take = false;
-      if (key > T) {
-        take = true;
-      } else if (key == T) {
-        take = e < take_eq;
-        ++e;
-      }
-      if (take) emit(i, pos++);
-    }
-  }
-  return total;
 }
 
 // ---------------------------------------------------------------------------
-// cross-workgroup "last one finishes the row" ticket
+// cross-workgroup hand-off without cache-wide fences
 // ---------------------------------------------------------------------------
-// Every thread publishes its global writes, one thread takes a ticket; the
-// workgroup that draws the last ticket of its row returns true (after an
-// acquire fence) and resets the counter to zero for the next launch.
-__device__ __forceinline__ bool last_of_row(uint32_t* counter, uint32_t expected, int* flag) {
-  __threadfence();
+// A workgroup that hands data to the last workgroup of its row writes that
+// data with agent-scope stores (sc1: written through to the agent's coherence
+// point rather than left dirty in this XCD's L2), waits until every one of its
+// own memory operations has completed, and only then takes a ticket with an
+// agent-scope atomic.  The workgroup that draws the last ticket reads the data
+// with agent-scope loads (sc1: not served from a possibly stale L2 line of its
+// own XCD).  This replaces release/acquire fences, which on a multi-XCD part
+// write back / invalidate the whole L2 per workgroup.
+__device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t expected, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev + 1 == expected;
-    if (last) atomicExch(counter, 0u);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
   __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag != 0;
 }
+
+// Buffer resource over [base, base+bytes): out-of-range loads return zero and
+// out-of-range stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+constexpr int kSC1 = 16;  // cache-policy bits: agent scope
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_agent_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, kSC1);
+}
+__device__ __forceinline__ void store_agent_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, kSC1);
+}
+__device__ __forceinline__ void store_agent_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kSC1);
+}
+__device__ __forceinline__ float load_agent_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSC1));
+}
+__device__ __forceinline__ f32x2 load_agent_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kSC1));
+}
+__device__ __forceinline__ f32x4 load_agent_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSC1));
+}
+
+// ---------------------------------------------------------------------------
+// lane exchange (DPP within 16-lane rows, swizzle across rows)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+
+// value of the lane whose index differs in bit 1 (D = 2) or bit 0 (D = 1)
+template <int D>
+__device__ __forceinline__ float quad_partner(float v) {
+  if constexpr (D == 2) return dpp_mov<kDppQuadXor2>(v);
+  else return dpp_mov<kDppQuadXor1>(v);
+}
+
+// Butterfly reduction of N per-lane partial sums across the 4 lanes of a quad,
+// transposing as it goes: while more than one value is left, each lane keeps
+// half of its values and receives its partner's partial sums of that half, so
+// 4 lanes x N values reduce in (N/2 + N/4 ...) exchanges instead of 2N.
+// Afterwards lane q (= lane & 3) holds the full sums of value indices
+// [q*N/4, (q+1)*N/4) when N >= 4, or of index q / (4/N) when N < 4.
+template <int D, int N>
+__device__ __forceinline__ void quad_reduce(float* v, int q) {
+  if constexpr (D >= 1) {
+    if constexpr (N >= 2) {
+      const bool hi = (q & D) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float lo_v = v[i], hi_v = v[i + N / 2];
+        const float keep = hi ? hi_v : lo_v;
+        const float send = hi ? lo_v : hi_v;
+        v[i] = keep + quad_partner<D>(send);
+      }
+      quad_reduce<D / 2, N / 2>(v, q);
+    } else {
+      v[0] += quad_partner<D>(v[0]);
+      quad_reduce<D / 2, 1>(v, q);
+    }
+  }
+}
+
+// max over all 64 lanes, result in every lane
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// row-vector access with 4 lanes per vector (keys, representatives)
+// ---------------------------------------------------------------------------
+// A D-element vector is read by the 4 lanes of a quad: load ld (of NLD) of
+// lane q reads bytes [64*ld + 16*q, +16), so one load instruction of a wave
+// covers 64 contiguous bytes of each of its 16 vectors.
+template <typename T, int D>
+struct Quad {
+  static constexpr int EPL = Fmt<T>::kPer16B;
+  static constexpr int NLD = D / (4 * EPL);  // 16-byte loads per lane per vector
+  static_assert(NLD >= 1, "head_dim too small");
+  __device__ static __forceinline__ int elem(int ld, int q) { return ld * 4 * EPL + q * EPL; }
+};
+
+// The lane's slice of a query vector, kept in the form its dot product uses:
+// bf16 pairs for v_dot2 on bf16 data, floats otherwise.
+template <typename T, int D>
+struct QSlice;
+
+template <int D>
+struct QSlice<bf16, D> {
+  using Q = Quad<bf16, D>;
+  uint32_t p[Q::NLD][4];
+  __device__ __forceinline__ void load(const bf16* qv, int q) {
+#pragma unroll
+    for (int ld = 0; ld < Q::NLD; ++ld) {
+      const uint4 w = load16(qv + Q::elem(ld, q));
+      p[ld][0] = w.x;
+      p[ld][1] = w.y;
+      p[ld][2] = w.z;
+      p[ld][3] = w.w;
+    }
+  }
+  // partial dot product with the lane's 16-byte pieces of a vector
+  __device__ __forceinline__ float dot(const uint4 (&x)[Q::NLD]) const {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float acc = 0.f;
+#pragma unroll
+    for (int ld = 0; ld < Q::NLD; ++ld) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[ld][0]),
+                                            __builtin_bit_cast(bf16x2, x[ld].x), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[ld][1]),
+                                            __builtin_bit_cast(bf16x2, x[ld].y), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[ld][2]),
+                                            __builtin_bit_cast(bf16x2, x[ld].z), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[ld][3]),
+                                            __builtin_bit_cast(bf16x2, x[ld].w), acc, false);
+    }
+    return acc;
+  }
+};
+
+template <int D>
+struct QSlice<float, D> {
+  using Q = Quad<float, D>;
+  float f[Q::NLD][4];
+  __device__ __forceinline__ void load(const float* qv, int q) {
+#pragma unroll
+    for (int ld = 0; ld < Q::NLD; ++ld) unpack<float>(load16(qv + Q::elem(ld, q)), f[ld]);
+  }
+  __device__ __forceinline__ float dot(const uint4 (&x)[Q::NLD]) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int ld = 0; ld < Q::NLD; ++ld) {
+      acc = fmaf(f[ld][0], __uint_as_float(x[ld].x), acc);
+      acc = fmaf(f[ld][1], __uint_as_float(x[ld].y), acc);
+      acc = fmaf(f[ld][2], __uint_as_float(x[ld].z), acc);
+      acc = fmaf(f[ld][3], __uint_as_float(x[ld].w), acc);
+    }
+    return acc;
+  }
+};
+
+// native 2^x (v_exp_f32): for softmax weights, where results below 2^-126
+// are negligible next to the running maximum's weight of >= 1
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace nsa

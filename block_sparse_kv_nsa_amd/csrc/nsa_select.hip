@@ -48,16 +48,17 @@ struct SelectArgs {
 
 template <typename T, int D, int G, bool FORECAST>
 __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
-  constexpr int EPL = Fmt<T>::kPer16B;   // elements per lane per 16-byte load
-  constexpr int LPR = D / EPL;           // lanes per representative
-  constexpr int RPW = kWave / LPR;       // representatives per wave per load
-  constexpr int RPB = kWaves * RPW;      // ... per workgroup per load
-  constexpr int GS = FORECAST ? 1 : G;   // logits per sub-block
-  constexpr int U = 4;                   // loads in flight per thread
+  using Q = Quad<T, D>;
+  constexpr int NLD = Q::NLD;             // 16-byte loads per lane per representative
+  constexpr int GS = FORECAST ? 1 : G;    // logits per sub-block
+  constexpr int KEEP = GS >= 4 ? GS / 4 : 1;  // logits a lane ends up holding per rep
+  constexpr int DUP = GS >= 4 ? 1 : 4 / GS;   // lanes of a quad holding the same logit
+  constexpr int U = 8;                    // representatives per lane in flight
+  constexpr int RPI = kThreads / 4;       // representatives per workgroup and load slot
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int sl = lane % LPR, grp = lane / LPR;
+  const int q = lane & 3, r = lane >> 2;  // quad lane, representative within the wave
   const int row = blockIdx.y, chunk = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
   // blocks past the host bound max_seq_len/64 are ignored (no out-of-range
@@ -66,70 +67,65 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   const int nsub = nb * kSubs;
   const int j0 = chunk * a.chunk_reps;
   const int j1 = min(j0 + a.chunk_reps, nsub);
+  const int h0 = GS >= 4 ? q * KEEP : q / DUP;  // first head of the lane's logits
+  const bool canon = (q % DUP) == 0;
 
-  __shared__ float red_m[kWaves][G], red_s[kWaves][G];
+  __shared__ float red_m[kWaves][4][KEEP], red_s[kWaves][4][KEEP];
   __shared__ int s_flag;
 
-  float qv[GS][EPL];
+  QSlice<T, D> qs[GS];
   {
     const T* qb = static_cast<const T*>(a.query) +
                   (FORECAST ? (int64_t)row * D : ((int64_t)b * a.Hkv + g) * G * D);
 #pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      unpack<T>(load16(qb + h * D + sl * EPL), qv[h]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
-    }
+    for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
   }
 
   const T* rb = static_cast<const T*>(a.reps) + (int64_t)row * a.max_blocks * kSubs * D;
-  float* lb = a.logits + (int64_t)row * a.logits_row;
-  float m[GS], s[GS];
+  const __amdgpu_buffer_rsrc_t lrs =
+      make_rsrc(a.logits + (int64_t)row * a.logits_row, (uint32_t)(a.logits_row * 4));
+  float m[KEEP], s[KEEP];
 #pragma unroll
-  for (int h = 0; h < GS; ++h) {
-    m[h] = -INFINITY;
-    s[h] = 0.f;
+  for (int kk = 0; kk < KEEP; ++kk) {
+    m[kk] = -INFINITY;
+    s[kk] = 0.f;
   }
 
-  // the trip count is uniform per wave; lanes past j1 compute on zeros
-  for (int jw = j0 + wave * RPW; jw < j1; jw += RPB * U) {
-    uint4 v[U];
+  for (int jb = j0 + wave * 16 + r; jb - r - wave * 16 < j1; jb += RPI * U) {
+    uint4 x[U][NLD];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jw + u * RPB + grp;
-      v[u] = j < j1 ? load16_stream(rb + (int64_t)j * D + sl * EPL) : make_uint4(0, 0, 0, 0);
+      const int j = jb + u * RPI;
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld)
+        x[u][ld] = j < j1 ? load16_stream(rb + (int64_t)j * D + Q::elem(ld, q))
+                          : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jw + u * RPB + grp;
-      float x[EPL];
-      unpack<T>(v[u], x);
-      float lg[GS];
+      const int j = jb + u * RPI;
+      float v[GS];
 #pragma unroll
-      for (int h = 0; h < GS; ++h) {
-        float acc = 0.f;
+      for (int h = 0; h < GS; ++h) v[h] = qs[h].dot(x[u]);
+      quad_reduce<2, GS>(v, q);
+      if (j < j1 && canon) {
+        float lg[KEEP];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qv[h][e], x[e], acc);
-        lg[h] = group_sum<LPR>(acc);
-      }
-      if (j < j1) {
-        if (sl == 0) {
-          float* dst = lb + (int64_t)j * GS;
-          if constexpr (GS % 4 == 0) {
+        for (int kk = 0; kk < KEEP; ++kk) lg[kk] = v[kk] * a.qscale;
+        const uint32_t off = (uint32_t)(j * GS + h0) * 4u;
+        if constexpr (KEEP == 1) store_agent_f32(lrs, off, lg[0]);
+        else if constexpr (KEEP == 2) store_agent_f32x2(lrs, off, f32x2{lg[0], lg[1]});
+        else {
 #pragma unroll
-            for (int h = 0; h < GS; h += 4)
-              *reinterpret_cast<float4*>(dst + h) = make_float4(lg[h], lg[h + 1], lg[h + 2], lg[h + 3]);
-          } else {
-#pragma unroll
-            for (int h = 0; h < GS; ++h) dst[h] = lg[h];
-          }
+          for (int kk = 0; kk < KEEP; kk += 4)
+            store_agent_f32x4(lrs, off + kk * 4, f32x4{lg[kk], lg[kk + 1], lg[kk + 2], lg[kk + 3]});
         }
         if constexpr (!FORECAST) {
 #pragma unroll
-          for (int h = 0; h < GS; ++h) {
-            const float M = fmaxf(m[h], lg[h]);
-            s[h] = s[h] * exp2f(m[h] - M) + exp2f(lg[h] - M);
-            m[h] = M;
+          for (int kk = 0; kk < KEEP; ++kk) {
+            const float M = fmaxf(m[kk], lg[kk]);
+            s[kk] = s[kk] * exp2f(m[kk] - M) + exp2f(lg[kk] - M);
+            m[kk] = M;
           }
         }
       }
@@ -137,107 +133,160 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   }
 
   if constexpr (!FORECAST) {
-    // chunk statistics per head: merge lanes of other groups, then waves
+    // chunk statistics per head: merge the 16 lanes holding the same heads
+    // (same quad lane q), then the 4 waves
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int kk = 0; kk < KEEP; ++kk) {
 #pragma unroll
-      for (int off = LPR; off < kWave; off <<= 1) {
-        const float m2 = __shfl_xor(m[h], off, kWave);
-        const float s2 = __shfl_xor(s[h], off, kWave);
-        merge_ms(m[h], s[h], m2, s2);
+      for (int off = 4; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m[kk], off, kWave);
+        const float s2 = __shfl_xor(s[kk], off, kWave);
+        merge_ms(m[kk], s[kk], m2, s2);
       }
-      if (lane == 0) {
-        red_m[wave][h] = m[h];
-        red_s[wave][h] = s[h];
+      if (r == 0) {
+        red_m[wave][q][kk] = m[kk];
+        red_s[wave][q][kk] = s[kk];
       }
     }
     __syncthreads();
     if (threadIdx.x < G) {
       const int h = threadIdx.x;
-      float M = red_m[0][h], S = red_s[0][h];
-      for (int w = 1; w < kWaves; ++w) merge_ms(M, S, red_m[w][h], red_s[w][h]);
-      a.stats[((int64_t)row * gridDim.x + chunk) * G + h] = make_float2(M, S);
+      const int qq = G >= 4 ? h / KEEP : h * DUP, kk = G >= 4 ? h % KEEP : 0;
+      float M = red_m[0][qq][kk], S = red_s[0][qq][kk];
+      for (int w = 1; w < kWaves; ++w) merge_ms(M, S, red_m[w][qq][kk], red_s[w][qq][kk]);
+      const __amdgpu_buffer_rsrc_t srs =
+          make_rsrc(a.stats, (uint32_t)((int64_t)gridDim.y * gridDim.x * G * 8));
+      store_agent_f32x2(srs, (uint32_t)((((int64_t)row * gridDim.x + chunk) * G + h) * 8),
+                        f32x2{M, S});
     }
   }
 
-  if (!last_of_row(a.counters + row, gridDim.x, &s_flag)) return;
+  if (!last_arrival(a.counters + row, gridDim.x, &s_flag)) return;
 
   // ---------------------------------------------------------------------
   // the row's last workgroup: normalise, score blocks, select
   // ---------------------------------------------------------------------
   extern __shared__ uint32_t dyn[];
-  uint32_t* keys = dyn;                                     // nb_max + k_e
+  uint32_t* keys = dyn;                                            // nb_max + k_e
   int* ev_old = reinterpret_cast<int*>(keys + a.nb_max + a.k_e);   // k_e
-  int* ev_new = ev_old + a.k_e;                             // k_e
-  int* ord = ev_new + a.k_e;                                // k (ordered mode)
+  int* ev_new = ev_old + a.k_e;                                    // k_e
+  int* ord = ev_new + a.k_e;                                       // k (ordered mode)
   uint8_t* flags = reinterpret_cast<uint8_t*>(ord + (a.ordered ? a.k : 0));  // nb_max
-  __shared__ SelectSmem ssm;
   __shared__ float sM[G], sInvZ[G];
 
   if constexpr (!FORECAST) {
+    // per-head softmax normaliser: every thread merges the chunk statistics
+    // of head tid % G it is given (all loads in flight at once), then lanes of
+    // the same head merge across the wave and the waves through LDS
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(a.stats, (uint32_t)((int64_t)gridDim.y * gridDim.x * G * 8));
+    const int nstat = (int)gridDim.x * G;
+    float M = -INFINITY, S = 0.f;
+    for (int i = threadIdx.x; i < nstat; i += kThreads) {
+      const f32x2 st = load_agent_f32x2(srs, (uint32_t)(((int64_t)row * nstat + i) * 8));
+      merge_ms(M, S, st.x, st.y);
+    }
+#pragma unroll
+    for (int off = G; off < kWave; off <<= 1) {
+      const float m2 = __shfl_xor(M, off, kWave);
+      const float s2 = __shfl_xor(S, off, kWave);
+      merge_ms(M, S, m2, s2);
+    }
+    __shared__ float fin_m[kWaves][G], fin_s[kWaves][G];
+    if (lane < G) {
+      fin_m[wave][lane] = M;
+      fin_s[wave][lane] = S;
+    }
+    __syncthreads();
     if (threadIdx.x < G) {
       const int h = threadIdx.x;
-      float M = -INFINITY, S = 0.f;
-      for (int c = 0; c < (int)gridDim.x; ++c) {
-        const float2 st = a.stats[((int64_t)row * gridDim.x + c) * G + h];
-        merge_ms(M, S, st.x, st.y);
-      }
-      sM[h] = M;
-      sInvZ[h] = S > 0.f ? 1.f / S : 0.f;
+      float Mh = fin_m[0][h], Sh = fin_s[0][h];
+      for (int w = 1; w < kWaves; ++w) merge_ms(Mh, Sh, fin_m[w][h], fin_s[w][h]);
+      sM[h] = Mh;
+      sInvZ[h] = Sh > 0.f ? 1.f / Sh : 0.f;
     }
   }
   __syncthreads();
 
-  // eviction set: the k_e best of (old set U newly full blocks) by E
-  int n_e = 0;
+  // eviction set: the k_e best of (old set U newly full blocks) by E.  With
+  // no newly full block the candidates are the old set itself: unchanged.
+  __shared__ int s_ne;
+  __shared__ __align__(16) uint32_t hist[256];
+  if (threadIdx.x == 0) s_ne = 0;
   if (a.k_e > 0 && !a.ordered) {
     int seen = a.evict_seen[row];
     if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
     const int nprev = min(a.k_e, seen);
-    for (int i = threadIdx.x; i < nprev; i += kThreads) ev_old[i] = a.evict_set[(int64_t)row * a.k_e + i];
+    for (int i = threadIdx.x; i < nprev; i += kThreads)
+      ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
     __syncthreads();
     const int ncand = nprev + nb - seen;
-    const float* Er = a.E + (int64_t)row * a.max_blocks;
-    for (int i = threadIdx.x; i < nprev; i += kThreads)
-      ev_old[i] = min(max(ev_old[i], 0), nb - 1);  // corrupted state cannot index out of range
-    __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += kThreads) {
-      const int id = i < nprev ? ev_old[i] : seen + i - nprev;
-      keys[i] = order_key(Er[id]);
+    const int n_e = min(a.k_e, ncand);
+    if (seen == nb) {
+      for (int i = threadIdx.x; i < n_e; i += kThreads) ev_new[i] = ev_old[i];
+    } else {
+      const float* Er = a.E + (int64_t)row * a.max_blocks;
+      for (int i = threadIdx.x; i < ncand; i += kThreads) {
+        const int id = i < nprev ? ev_old[i] : seen + i - nprev;
+        keys[i] = order_key(Er[id]);
+      }
+      __syncthreads();
+      if (wave == 0 && n_e > 0) {
+        wave_top_m(keys, ncand, n_e, hist, [&](int i, int pos) {
+          ev_new[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
+        });
+      }
     }
-    __syncthreads();
-    n_e = min(a.k_e, ncand);
-    if (n_e > 0) {
-      int take;
-      const uint32_t thr = radix_select(keys, ncand, n_e, ssm, &take);
-      compact_selected(keys, ncand, thr, take, ssm.scan, [&](int i, int pos) {
-        ev_new[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
-      });
-    }
+    if (threadIdx.x == 0) s_ne = n_e;
     __syncthreads();
     for (int i = threadIdx.x; i < a.k_e; i += kThreads)
       a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? ev_new[i] : -1;
     if (threadIdx.x == 0) a.evict_seen[row] = nb;
   }
+  __syncthreads();
+  const int n_e = s_ne;
 
-  // block scores -> order keys in LDS
-  for (int blk = threadIdx.x; blk < nb; blk += kThreads) {
-    const float* lp = lb + (int64_t)blk * kSubs * GS;
-    float best = -INFINITY;
-    if constexpr (FORECAST) {
+  // block scores -> order keys in LDS; each thread takes kBatch blocks at a
+  // time with all their logit loads in flight before any arithmetic
+  constexpr int kBatch = GS >= 8 ? 4 : 8;
+  for (int b0 = threadIdx.x; b0 < nb; b0 += kThreads * kBatch) {
+    f32x4 lgv[kBatch][GS];
 #pragma unroll
-      for (int j = 0; j < kSubs; ++j) best = fmaxf(best, lp[j]);
-    } else {
+    for (int bb = 0; bb < kBatch; ++bb) {
+      const int blk = b0 + bb * kThreads;
 #pragma unroll
-      for (int j = 0; j < kSubs; ++j) {
-        float gsum = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) gsum += exp2f(lp[j * G + h] - sM[h]) * sInvZ[h];
-        best = fmaxf(best, gsum);
-      }
+      for (int i = 0; i < GS; ++i)
+        lgv[bb][i] = blk < nb ? load_agent_f32x4(lrs, (uint32_t)((blk * kSubs * GS + 4 * i) * 4))
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    keys[blk] = order_key(best);
-    flags[blk] = 0;
+#pragma unroll
+    for (int bb = 0; bb < kBatch; ++bb) {
+      const int blk = b0 + bb * kThreads;
+      if (blk >= nb) break;
+      float lg[kSubs * GS];
+#pragma unroll
+      for (int i = 0; i < GS; ++i) {
+        lg[4 * i] = lgv[bb][i].x;
+        lg[4 * i + 1] = lgv[bb][i].y;
+        lg[4 * i + 2] = lgv[bb][i].z;
+        lg[4 * i + 3] = lgv[bb][i].w;
+      }
+      float best = -INFINITY;
+      if constexpr (FORECAST) {
+#pragma unroll
+        for (int j = 0; j < kSubs; ++j) best = fmaxf(best, lg[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSubs; ++j) {
+          float gsum = 0.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) gsum += exp2f(lg[j * G + h] - sM[h]) * sInvZ[h];
+          best = fmaxf(best, gsum);
+        }
+      }
+      keys[blk] = order_key(best);
+      flags[blk] = 0;
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < n_e; i += kThreads) {
@@ -246,23 +295,47 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   }
   __syncthreads();
 
+  // query-aware part (or the ordered list) on wave 0, no workgroup barriers
   const int mq = a.ordered ? min(a.k, nb) : min(a.k - n_e, nb - n_e);
-  if (mq > 0) {
-    int take;
-    const uint32_t thr = radix_select(keys, nb, mq, ssm, &take);
-    const bool ordered = a.ordered != 0;
-    compact_selected(keys, nb, thr, take, ssm.scan, [&](int i, int pos) {
-      if (ordered) ord[pos] = i;
-      else flags[i] = 1;
-    });
+  int32_t* out = a.selected + (int64_t)row * a.k;
+  __shared__ int s_count;
+  if (wave == 0) {
+    if (mq > 0) {
+      const bool ordered = a.ordered != 0;
+      wave_top_m(keys, nb, mq, hist, [&](int i, int pos) {
+        if (ordered) ord[pos] = i;
+        else flags[i] = 1;
+      });
+    }
+    if (!a.ordered) {
+      // selected = flagged blocks, ascending
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+      int taken = 0;
+      const uint64_t below = (1ull << lane) - 1ull;
+      for (int base = 0; base < nb; base += 8 * kWave) {
+        bool f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = base + j * kWave + lane;
+          f[j] = i < nb && flags[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint64_t bm = __ballot(f[j]);
+          if (f[j]) out[taken + __popcll(bm & below)] = base + j * kWave + lane;
+          taken += __popcll(bm);
+        }
+      }
+      if (lane == 0) s_count = taken;
+    } else if (lane == 0) {
+      s_count = mq;
+    }
   }
   __syncthreads();
-
-  int32_t* out = a.selected + (int64_t)row * a.k;
-  int count;
+  const int count = s_count;
   if (a.ordered) {
     // rank = entries with a larger key, or an equal key and a lower id
-    count = mq;
     for (int i = threadIdx.x; i < mq; i += kThreads) {
       const int id = ord[i];
       const uint32_t key = keys[id];
@@ -274,14 +347,6 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
       }
       out[rank] = id;
     }
-  } else {
-    const int per = (nb + kThreads - 1) / kThreads;
-    const int s0 = min(nb, (int)threadIdx.x * per), s1 = min(nb, s0 + per);
-    int cnt = 0;
-    for (int i = s0; i < s1; ++i) cnt += flags[i];
-    int pos = block_exclusive_scan(cnt, ssm.scan, &count);
-    for (int i = s0; i < s1; ++i)
-      if (flags[i]) out[pos++] = i;
   }
   for (int i = count + threadIdx.x; i < a.k; i += kThreads) out[i] = -1;
   if (threadIdx.x == 0) a.num_selected[row] = count;

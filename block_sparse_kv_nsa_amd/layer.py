@@ -59,6 +59,7 @@ class SparseDecodeLayer:
         self.sel_ws_bytes = A.nsa_select_workspace_bytes(self.shape, self.sel_params, cap)
         self.dec_ws_bytes = A.nsa_decode_workspace_bytes(self.shape, self.dec_params)
         self.sel_ws = torch.zeros(self.sel_ws_bytes, dtype=torch.uint8, device=dev)
+        self.step_ws, self.step_ws_bytes = None, 0
         self.dec_ws = torch.zeros(self.dec_ws_bytes, dtype=torch.uint8, device=dev)
 
     # -- the three calls ---------------------------------------------------
@@ -91,6 +92,20 @@ class SparseDecodeLayer:
                             self.seq_lens, self.selected if selected is None else selected,
                             self.num_selected if num_selected is None else num_selected,
                             self.num_processed, self.out, self.dec_ws, self.dec_ws_bytes, stream)
+
+    def step(self, query: torch.Tensor, q: torch.Tensor, max_seq_len: int, stream=None) -> None:
+        """Selection and decode in one launch (ascending mode)."""
+        if self.step_ws is None:
+            self.step_ws_bytes = A.nsa_decode_step_workspace_bytes(self.shape, self.sel_params,
+                                                                   64 * self.max_blocks)
+            self.step_ws = torch.zeros(self.step_ws_bytes, dtype=torch.uint8, device=self.device)
+        ke = self.k_e > 0
+        A.nsa_decode_step(self.shape, self.sel_params, query, q, self.reps,
+                          self.evict_scores if ke else None, self.k_pool, self.v_pool,
+                          self.block_table, self.seq_lens, max_seq_len,
+                          self.evict_set if ke else None, self.evict_seen if ke else None,
+                          self.selected, self.num_selected, self.out, self.step_ws,
+                          self.step_ws_bytes, stream)
 
     def reset_state(self) -> None:
         self.evict_set.fill_(-1)

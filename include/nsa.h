@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 1
+#define NSA_ABI_VERSION 2
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -218,6 +218,35 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
                              const int32_t* selected, const int32_t* num_selected,
                              int32_t* num_processed, void* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Fused step -- nsa_select_blocks followed by nsa_sparse_decode in one launch
+ * (ascending mode: params->ordered must be 0).  Same inputs, state and
+ * outputs as the two calls (selected / num_selected as nsa_select_blocks
+ * writes them; out as nsa_sparse_decode writes it).  The computation is
+ * identical; the schedule differs: the eviction set depends on the eviction
+ * scores only (NOSA summary, "Mecanismo de Doble Seleccion"), so attention
+ * over it proceeds while the query-aware part is still being scored and
+ * selected, and one persistent grid runs every stage.
+ *
+ *   query  selector input: [B][Hq][D] (group softmax) or [B][Hkv][D]
+ *          (forecast); q: attention queries [B][Hq][D] (may equal query)
+ * The workspace follows the select workspace's counter rule (zero before
+ * its first use; left zero by every completed call); its first 16 bytes
+ * hold queue counters and an error word that is nonzero if a wait between
+ * stages ever expired (results of that call are then undefined).
+ * ------------------------------------------------------------------------ */
+nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
+                                           int32_t max_seq_len, size_t* bytes);
+
+nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* params,
+                           const void* query, const void* q, const void* reps,
+                           const float* evict_block_score, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t* evict_set,
+                           int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* nsa_status_string(nsa_status status);

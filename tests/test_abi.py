@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
