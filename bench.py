@@ -4,8 +4,9 @@
 
 One step = one pass of the decode hot path for one attention layer over one
 batch: block representatives of blocks that filled (none at the measured
-workload's steps), scoring + selection (nsa_select_blocks) and the sparse
-decode (nsa_sparse_decode).  Inputs are seeded synthetic tensors already
+workload's steps), then scoring, selection and the sparse decode, either as
+nsa_select_blocks + nsa_sparse_decode (default, --path split) or as the one
+fused launch nsa_decode_step (--path fused).  Inputs are seeded synthetic tensors already
 resident in HBM when timing starts.  Steps rotate over R independent layer
 instances (own pools, representatives, state and workspaces; R x working set
 >= 1 GiB) so that the ~256 MB Infinity Cache cannot hold the step's bytes and
@@ -40,6 +41,7 @@ WORKLOADS = {"tiny-fp32": 0, "nosa-1b": 1, "sparda-8b": 2, "long-128k": 3, "earl
 KERNEL_SOURCES = {
     "select": "block_sparse_kv_nsa_amd/csrc/nsa_select.hip",
     "decode": "block_sparse_kv_nsa_amd/csrc/nsa_decode.hip",
+    "step": "block_sparse_kv_nsa_amd/csrc/nsa_step.hip",
 }
 
 
@@ -53,13 +55,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle leg")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows sampled by the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="split", choices=("fused", "split"),
+                    help="fused: one nsa_decode_step launch; split: nsa_select_blocks + "
+                         "nsa_sparse_decode")
     return ap.parse_args()
 
 
 def source_hash(rel: str) -> str:
     h = hashlib.sha256()
     for part in (rel, "block_sparse_kv_nsa_amd/csrc/nsa_device.hpp",
-                 "block_sparse_kv_nsa_amd/csrc/nsa_internal.hpp"):
+                 "block_sparse_kv_nsa_amd/csrc/nsa_internal.hpp",
+                 "block_sparse_kv_nsa_amd/csrc/nsa_attend.hpp"):
         with open(os.path.join(ROOT, part), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -161,6 +167,7 @@ def gpu_leg(args, cfg):
                   for t in range(steps)]
     ones = torch.ones(cfg.batch, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    fused = args.path == "fused" and not cfg.ordered
 
     def step(i, ev=None):
         lay = layers[i % R]
@@ -170,6 +177,12 @@ def gpu_leg(args, cfg):
             lay.update_reps(fill_first[t], ones, 1, stream)
         if ev is not None:
             ev[0].record(stream)
+        if fused:
+            lay.step(sel_q[t], qs[t], cfg.seq_len(t), stream)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].record(stream)
+            return
         lay.select(sel_q[t], cfg.seq_len(t), stream)
         if ev is not None:
             ev[1].record(stream)
@@ -199,7 +212,7 @@ def gpu_leg(args, cfg):
     sb = select_bytes(cfg, L_mid)
     db = decode_bytes(cfg, L_mid, int(round(n_sel)))
     return dict(R=R, total_ms=total_ms, wall_s=wall, sel_ms=sel_ms, dec_ms=dec_ms,
-                sel_bytes=sb, dec_bytes=db, n_sel=n_sel)
+                sel_bytes=sb, dec_bytes=db, n_sel=n_sel, fused=fused)
 
 
 # ----------------------------------------------------------------------------
@@ -259,10 +272,13 @@ def main():
     g = gpu_leg(args, cfg)
     ms_per_step = g["total_ms"] / args.steps
     value = cfg.batch / (ms_per_step / 1e3)
-    kernels = {
-        "select": {"ms": g["sel_ms"], "bytes": g["sel_bytes"]},
-        "decode": {"ms": g["dec_ms"], "bytes": g["dec_bytes"]},
-    }
+    if g["fused"]:
+        kernels = {"step": {"ms": g["sel_ms"], "bytes": g["sel_bytes"] + g["dec_bytes"]}}
+    else:
+        kernels = {
+            "select": {"ms": g["sel_ms"], "bytes": g["sel_bytes"]},
+            "decode": {"ms": g["dec_ms"], "bytes": g["dec_bytes"]},
+        }
     for k in kernels.values():
         k["GB/s"] = k["bytes"] / (k["ms"] / 1e3) / 1e9
         k["frac"] = k["GB/s"] / HBM_PEAK_GBS

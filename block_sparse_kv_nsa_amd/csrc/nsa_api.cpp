@@ -316,8 +316,8 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
   L.tau = params->tau;
   L.lay = lay;
   if (env_trace())
-    std::fprintf(stderr, "[nsa] decode grid=(%d,%d) bpw=%d G=%d D=%d early_stop=%d\n", lay.splits,
-                 lay.rows, lay.bpw, L.G, L.D, L.early_stop);
+    std::fprintf(stderr, "[nsa] decode rows=%d items=%d bpw=%d (0: by occupancy) G=%d D=%d "
+                 "early_stop=%d\n", lay.rows, lay.items_max, lay.bpw, L.G, L.D, L.early_stop);
   return launched(fn, nsa::launch_decode(L, stream));
 }
 

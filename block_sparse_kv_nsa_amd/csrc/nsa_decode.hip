@@ -295,10 +295,21 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   a.max_blocks = L.max_blocks;
   a.max_selected = L.max_selected;
   a.items_max = lay.items_max;
-  a.bpw = lay.bpw;
   a.qscale = L.scale * 1.4426950408889634f;  // natural -> base-2 logits
   a.tau = L.tau;
-  dim3 grid(lay.splits, lay.rows);
+  int bpw = lay.bpw;
+  if (bpw <= 0) {
+    const void* fn = L.early_stop ? reinterpret_cast<const void*>(decode_kernel<T, D, G, true>)
+                                  : reinterpret_cast<const void*>(decode_kernel<T, D, G, false>);
+    int per_cu = 0, dev = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    bpw = balanced_blocks_per_split(lay.rows, lay.items_max, max(1, per_cu) * max(1, cus));
+  }
+  a.bpw = bpw;
+  dim3 grid((lay.items_max + bpw - 1) / bpw, lay.rows);
   if (L.early_stop) {
     es_mass_kernel<T, D, G><<<grid, kThreads, 0, stream>>>(a);
     hipError_t e = hipGetLastError();

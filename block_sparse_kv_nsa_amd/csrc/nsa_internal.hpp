@@ -88,6 +88,29 @@ inline int decode_blocks_per_split(int rows, int items_max) {
   return bpw;
 }
 
+// Items per decode workgroup when `slots` workgroups fit on the device at
+// once: the fewest rounds of resident workgroups times the per-workgroup work
+// (bpw items plus about one item's worth of set-up and merge), so that a
+// launch does not end with a nearly empty second round.  Ties go to the
+// smaller bpw (more parallelism per row).
+inline int balanced_blocks_per_split(int rows, int items, int slots) {
+  int best = 1;
+  long best_cost = -1;
+  for (int bpw = 1; bpw <= 16; ++bpw) {
+    const long wgs = (long)rows * ((items + bpw - 1) / bpw);
+    const long rounds = (wgs + slots - 1) / (slots > 0 ? slots : 1);
+    const long cost = rounds * (bpw + 1);
+    if (best_cost < 0 || cost < best_cost) {
+      best = bpw;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+// bpw_override > 0 fixes the items per workgroup; 0 leaves the choice to the
+// launch (balanced_blocks_per_split with the kernel's occupancy).  Partial
+// buffers are sized for one item per split, so any choice fits.
 inline DecodeLayout decode_layout(int B, int Hkv, int G, int D, int max_selected, bool early_stop,
                                   int bpw_override) {
   DecodeLayout s{};
@@ -95,9 +118,8 @@ inline DecodeLayout decode_layout(int B, int Hkv, int G, int D, int max_selected
   s.G = G;
   s.D = D;
   s.items_max = max_selected + 1;  // listed blocks + the partial tail block
-  s.bpw = bpw_override > 0 ? bpw_override : decode_blocks_per_split(s.rows, s.items_max);
-  s.splits = (s.items_max + s.bpw - 1) / s.bpw;
-  // partial buffers are sized for one item per split so any bpw fits
+  s.bpw = bpw_override > 0 ? bpw_override : 0;
+  s.splits = s.bpw > 0 ? (s.items_max + s.bpw - 1) / s.bpw : 0;
   const size_t max_splits = (size_t)s.items_max;
   s.off_ml = round_up((size_t)4 * s.rows, 256);
   s.off_acc = round_up(s.off_ml + (size_t)s.rows * max_splits * G * 8, 256);

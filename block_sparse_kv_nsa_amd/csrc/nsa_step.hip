@@ -36,7 +36,10 @@
 namespace nsa {
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 22;  // sleep-polls before a wait gives up
+// A wait gives up after 0.2 s of the constant-rate wall clock; once any wait
+// has given up, later waits of the launch return at once, so a broken
+// hand-off ends the launch quickly with the error word set.
+constexpr int kWaitMs = 200;
 
 struct StepArgs {
   const void* query;  // group-softmax: [B][Hq][D]; forecast: [B][Hkv][D]
@@ -64,6 +67,7 @@ struct StepArgs {
   int Hkv, max_blocks, nb_max, k, k_e, chunks, mloc, bpw, splitsE, splitsQ;
   int nE, nA, nDE, nDQ;
   float qscale_sel, qscale_att;
+  uint64_t wait_ticks;  // wall-clock ticks before a wait gives up
   uint32_t stats_bytes, lse_bytes, cand_bytes, elist_bytes, qlist_bytes, ml_bytes, acc_bytes;
 };
 
@@ -74,16 +78,17 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Whole workgroup: wait until *p >= target (bounded).
-__device__ void wait_word(uint32_t* p, uint32_t target, uint32_t* err) {
-  if (threadIdx.x == 0) {
-    uint32_t n = 0;
+// Whole workgroup: wait until *p >= target (bounded in time).
+__device__ void wait_word(uint32_t* p, uint32_t target, uint32_t* err, uint64_t wait_ticks) {
+  if (threadIdx.x == 0 && ld_agent(p) < target) {
+    const uint64_t t0 = (uint64_t)wall_clock64();
     while (ld_agent(p) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++n == kSpinLimit) {
+      if (ld_agent(err) != 0u) break;
+      if ((uint64_t)wall_clock64() - t0 > wait_ticks) {
         st_agent(err, 1u);
         break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
   }
   __syncthreads();
@@ -282,7 +287,7 @@ struct Step {
         }
         publish(rc + kFlagLse);
       }
-      wait_word(rc + kFlagLse, 1u, err);
+      wait_word(rc + kFlagLse, 1u, err, a.wait_ticks);
       if (threadIdx.x < G) {
         const f32x2 v = load_agent_f32x2(lr, (uint32_t)(((int64_t)row * G + threadIdx.x) * 8));
         sm.sM[threadIdx.x] = v.x;
@@ -291,7 +296,7 @@ struct Step {
     }
 
     // ---- eviction set of the row (excluded from the query-aware part)
-    wait_word(rc + kFlagE, 1u, err);
+    wait_word(rc + kFlagE, 1u, err, a.wait_ticks);
     const int n_e = (int)ld_agent(rc + kNE);
     const int blk0 = j0 / kSubs;
     for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
@@ -417,7 +422,7 @@ struct Step {
     const int tail = L - nb * kBlock;
     uint32_t* rc = a.rowctl + (int64_t)row * kRowWords;
     uint32_t* err = a.ctrl + kErr;
-    wait_word(rc + (EVICT ? kFlagE : kFlagQ), 1u, err);
+    wait_word(rc + (EVICT ? kFlagE : kFlagQ), 1u, err, a.wait_ticks);
     const int nlist = (int)ld_agent(rc + (EVICT ? kNE : kNQ));
     const int n_items = nlist + (EVICT && tail > 0);
     const int i0 = split * a.bpw;
@@ -562,8 +567,14 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
     return e;
-  int nwg = max(1, per_cu) * max(1, cus);
-  nwg = max(nwg, lay.chunks);  // a row's chunks must fit in the grid at once
+  int wall_khz = 0;
+  if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+    return e;
+  a.wait_ticks = (uint64_t)max(wall_khz, 1) * kWaitMs;
+  const int nwg = max(1, per_cu) * max(1, cus);
+  // every scoring task of a row waits for the row's other scoring tasks, so a
+  // row's chunks must all be resident at once
+  if (lay.chunks > nwg) return hipErrorLaunchOutOfResources;
   step_kernel<T, D, G, FORECAST><<<nwg, kThreads, dyn, stream>>>(a);
   return hipGetLastError();
 }

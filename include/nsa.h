@@ -232,9 +232,12 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  *   query  selector input: [B][Hq][D] (group softmax) or [B][Hkv][D]
  *          (forecast); q: attention queries [B][Hq][D] (may equal query)
  * The workspace follows the select workspace's counter rule (zero before
- * its first use; left zero by every completed call); its first 16 bytes
- * hold queue counters and an error word that is nonzero if a wait between
- * stages ever expired (results of that call are then undefined).
+ * its first use; left zero by every completed call), except for 32-bit word
+ * 2 (bytes 8-11): an error word, sticky, set nonzero when a wait between
+ * stages expired (results of such a call are undefined).  The sequences'
+ * scoring work must fit the grid at once: a call whose longest sequence
+ * needs more 8192-token chunks than the device holds workgroups of this
+ * kernel fails with NSA_ERR_HIP.
  * ------------------------------------------------------------------------ */
 nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
                                            int32_t max_seq_len, size_t* bytes);

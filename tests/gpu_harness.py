@@ -93,9 +93,9 @@ def prefill(layer, cfg: W.Config) -> None:
     layer.update_reps(first, num, nb0)
 
 
-def run_step(layer, cfg: W.Config, step: int, seq_lens=None) -> None:
+def run_step(layer, cfg: W.Config, step: int, seq_lens=None, fused: bool = False) -> None:
     """One decode step: (the token is already in the pool) reps of a block
-    that just filled, then select, then decode."""
+    that just filled, then select and decode (two calls, or the fused one)."""
     dev = layer.device
     L = cfg.seq_len(step)
     lens = np.full(cfg.batch, L, dtype=np.int32) if seq_lens is None else seq_lens
@@ -105,8 +105,17 @@ def run_step(layer, cfg: W.Config, step: int, seq_lens=None) -> None:
         first = torch.from_numpy((lens // 64 - 1).astype(np.int32)).to(dev)
         num = torch.from_numpy(filled.astype(np.int32)).to(dev)
         layer.update_reps(first, num, 1)
+    if fused:
+        layer.step(device_query(cfg, step), device_q(cfg, step), int(lens.max()))
+        return
     layer.select(device_query(cfg, step), int(lens.max()))
     layer.decode(device_q(cfg, step))
+
+
+def step_error_word(layer) -> int:
+    """The fused step's sticky error word (workspace word 2)."""
+    torch.cuda.synchronize()
+    return int(layer.step_ws[8:12].view(torch.int32).item())
 
 
 @dataclass
@@ -239,11 +248,12 @@ def stop_ratio_near_tau(q, orow, order, L, tau, n) -> bool:
     return bool(np.any(np.abs(ratio - tau) <= NEAR_TIE * tau))
 
 
-def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, row_inputs=None):
+def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, row_inputs=None,
+                  fused: bool = False):
     """Prefill + every decode step of cfg; compare sampled rows each step."""
     log(f"[case] {cfg.name}: B={cfg.batch} ctx={cfg.context} Hq={cfg.num_q_heads} "
           f"Hkv={cfg.num_kv_heads} D={cfg.head_dim} {cfg.dtype} {cfg.mode} k={cfg.k} "
-          f"k_e={cfg.k_e} ordered={cfg.ordered} steps={cfg.steps}")
+          f"k_e={cfg.k_e} ordered={cfg.ordered} steps={cfg.steps} fused={fused}")
     batch = batch if batch is not None else W.build_batch(cfg)
     layer = make_layer(cfg, batch)
     prefill(layer, cfg)
@@ -255,7 +265,9 @@ def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, ro
     prev = {r: None for r in rows}
     stats = {"gamma_min": 1.0, "n_star": []}
     for t in range(cfg.steps):
-        run_step(layer, cfg, t)
+        run_step(layer, cfg, t, fused=fused)
+        if fused:
+            assert step_error_word(layer) == 0, f"a stage wait expired at step {t}"
         if t % check_every and t != cfg.steps - 1:
             # still advance the oracle's eviction state from the GPU's
             res = fetch(layer)

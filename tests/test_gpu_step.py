@@ -1,0 +1,142 @@
+"""GPU parity of the fused decode step (nsa_decode_step) against the CPU oracle,
+and against the two-call path (nsa_select_blocks + nsa_sparse_decode).
+
+Every case prints what it runs before touching the GPU.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def test_step_config0_tiny_fp32():
+    H.run_and_check(W.config(0), fused=True)
+
+
+def test_step_config1_all_rows():
+    _, st = H.run_and_check(W.config(1), fused=True)
+    assert st["gamma_min"] >= 0.75
+
+
+def test_step_config1_fill_steps():
+    cfg = W.config(1, steps=160, batch=4)
+    _, st = H.run_and_check(cfg, check_every=3, fused=True)
+    assert st["gamma_min"] >= 0.75
+
+
+def test_step_config2_forecast_sampled_rows():
+    cfg = W.config(2)
+    H.run_and_check(cfg, rows=H.sample_rows(cfg, 12), fused=True)
+
+
+def test_step_config3_long_context_sampled_rows():
+    cfg = W.config(3)
+    _, st = H.run_and_check(cfg, rows=H.sample_rows(cfg, 6), check_every=3, fused=True)
+    assert st["gamma_min"] >= 0.75
+
+
+SMALL = [
+    ("f32", 64, 1, "group_softmax"),
+    ("f32", 128, 2, "group_softmax"),
+    ("bf16", 64, 8, "group_softmax"),
+    ("bf16", 128, 4, "group_softmax"),
+    ("bf16", 128, 8, "group_softmax"),
+    ("bf16", 128, 4, "forecast"),
+    ("f32", 64, 4, "forecast"),
+    ("bf16", 64, 1, "forecast"),
+]
+
+
+@pytest.mark.parametrize("dtype,D,G,mode", SMALL)
+def test_step_small_shapes(dtype, D, G, mode):
+    cfg = W.Config(f"step-small-{dtype}-{D}-{G}-{mode}", 60 + SMALL.index((dtype, D, G, mode)),
+                   batch=3, context=64 * 41 + 37, num_q_heads=2 * G, num_kv_heads=2,
+                   head_dim=D, dtype=dtype, mode=mode, k=12, k_e=0 if mode == "forecast" else 8,
+                   steps=30)
+    H.run_and_check(cfg, fused=True)
+
+
+def test_step_multi_chunk_rows():
+    """Rows of 3 scoring chunks (384 blocks) with a ragged last chunk."""
+    cfg = W.Config("step-chunks", 70, batch=2, context=64 * 300 + 5, num_q_heads=8,
+                   num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=40,
+                   k_e=24, steps=3)
+    H.run_and_check(cfg, fused=True)
+
+
+@pytest.mark.parametrize("k,k_e", [(8, 4), (8, 8), (8, 0)])
+def test_step_ragged_batch_edges(k, k_e):
+    cfg = W.Config("ragged", 50, batch=5, context=64 * 24, num_q_heads=8, num_kv_heads=2,
+                   head_dim=128, dtype="bf16", mode="group_softmax", k=k, k_e=k_e, steps=1)
+    lens = np.array([37, 64, 64 * 5 + 1, 64 * 20, 64 * 3], dtype=np.int32)
+    H.log(f"[case] fused, ragged seq_lens {lens.tolist()} k={k} k_e={k_e}")
+    batch = W.build_batch(cfg)
+    layer = H.make_layer(cfg, batch)
+    first = torch.zeros(cfg.batch, dtype=torch.int32, device="cuda")
+    num = torch.from_numpy(lens // 64).to("cuda")
+    layer.update_reps(first, num, int((lens // 64).max()))
+    layer.seq_lens.copy_(torch.from_numpy(lens))
+    layer.step(H.device_query(cfg, 0), H.device_q(cfg, 0), int(lens.max()))
+    assert H.step_error_word(layer) == 0
+    res = H.fetch(layer)
+    for b in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            orow = H.oracle_row(cfg, b, g)
+            assert res.num_selected[b, g] == min(k, int(lens[b]) // 64)
+            H.check_step(cfg, res, orow, b, g, 0, seq_len=int(lens[b]))
+
+
+def _two_layers(cfg):
+    batch = W.build_batch(cfg)
+    a, b = H.make_layer(cfg, batch), H.make_layer(cfg, batch)
+    H.prefill(a, cfg)
+    H.prefill(b, cfg)
+    return a, b
+
+
+def test_step_agrees_with_two_calls_and_resets_counters():
+    """Same selection and eviction state as select + decode; outputs within
+    one bf16 rounding where the sets agree; queue and row counters back at
+    zero after every call (so the next call needs no clearing)."""
+    cfg = W.Config("step-vs-split", 71, batch=3, context=64 * 200 + 9, num_q_heads=8,
+                   num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=24,
+                   k_e=16, steps=70)
+    H.log("[case] fused step vs two calls, 70 steps")
+    split, fused = _two_layers(cfg)
+    same_rows = 0
+    for t in range(cfg.steps):
+        H.run_step(split, cfg, t)
+        H.run_step(fused, cfg, t, fused=True)
+        assert H.step_error_word(fused) == 0
+        words = fused.step_ws[:fused.step_ws_bytes].view(torch.int32)
+        assert int(words[0]) == 0 and int(words[1]) == 0, "queue counters not reset"
+        rowctl = words[64:64 + 8 * cfg.rows]
+        assert int(rowctl.abs().sum()) == 0, "row counters/flags not reset"
+        rs, rf = H.fetch(split), H.fetch(fused)
+        assert np.array_equal(rs.evict_set, rf.evict_set)
+        for b in range(cfg.batch):
+            for g in range(cfg.num_kv_heads):
+                if np.array_equal(rs.selected[b, g], rf.selected[b, g]):
+                    same_rows += 1
+                    G = cfg.group
+                    d = np.abs(rs.out[b, g * G:(g + 1) * G] - rf.out[b, g * G:(g + 1) * G]).max()
+                    assert d <= 1e-2, (t, b, g, d)
+    assert same_rows >= 0.9 * cfg.steps * cfg.rows
+
+
+def test_step_rejects_ordered_mode():
+    cfg = W.Config("step-ordered", 72, batch=1, context=64 * 10, num_q_heads=4, num_kv_heads=1,
+                   head_dim=128, dtype="bf16", mode="group_softmax", k=8, k_e=0, steps=1,
+                   ordered=True, tau=1e-3)
+    H.log("[case] fused step in ordered mode must be refused")
+    layer = H.make_layer(cfg, W.build_batch(cfg))
+    with pytest.raises(Exception):
+        layer.step(H.device_query(cfg, 0), H.device_q(cfg, 0), cfg.seq_len(0))
