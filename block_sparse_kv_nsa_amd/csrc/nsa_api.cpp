@@ -9,6 +9,8 @@
 
 #include "nsa_internal.hpp"
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -333,10 +335,13 @@ static nsa_status step_layout_checked(const char* fn, const nsa_shape* shape,
                 shape->max_blocks_per_seq * 64);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   *lay = nsa::step_layout(shape->batch, shape->num_kv_heads, G, shape->head_dim, params->k,
-                          params->k_e, max_seq_len, env_int("NSA_DECODE_BPW"));
-  if (lay->dyn_lds > 64 * 1024)
-    return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 65536)", fn,
-                lay->dyn_lds);
+                          params->k_e, max_seq_len);
+  const size_t lds = nsa::gang_dyn_lds(*lay, params->k, params->k_e, nsa::kMaxGang);
+  if (lds > 64 * 1024)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 65536)", fn, lds);
+  if (4 * lay->nb_max > nsa::kMaxGang * nsa::kGangReps)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: max_seq_len %d above the fused step's %d tokens", fn,
+                max_seq_len, nsa::kMaxGang * nsa::kGangReps * 16);
   if (lay->bytes >= (size_t)1 << 32)
     return fail(NSA_ERR_UNSUPPORTED, "%s: workspace above 4 GiB", fn);
   return NSA_OK;
@@ -407,11 +412,57 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
   L.k = params->k;
   L.k_e = params->k_e;
   L.scale = scale_of(shape);
+  L.gang_override = env_int("NSA_STEP_GANG");
+  const int pct = env_int("NSA_STEP_EFIRST");
+  L.e_first_pct = pct > 0 ? (pct > 100 ? 100 : pct) : 50;
   L.lay = lay;
   if (env_trace())
-    std::fprintf(stderr, "[nsa] step rows=%d chunks=%d mloc=%d bpw=%d splits=%d+%d lds=%zu\n",
-                 lay.rows, lay.chunks, lay.mloc, lay.bpw, lay.splitsE, lay.splitsQ, lay.dyn_lds);
+    std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d mloc_max=%d gang=%d efirst=%d%%\n", lay.rows,
+                 lay.nb_max, lay.mloc_max, L.gang_override, L.e_first_pct);
   return launched(fn, nsa::launch_step(L, stream));
 }
 
 }  // extern "C"
+
+namespace nsa {
+
+hipError_t grid_info(const void* kernel, int threads, size_t dyn_lds, GridInfo* out) {
+  struct Entry {
+    const void* kernel;
+    int dev;
+    size_t lds;
+    GridInfo info;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].kernel == kernel && cache[i].dev == dev && cache[i].lds == dyn_lds) {
+        *out = cache[i].info;
+        return hipSuccess;
+      }
+  }
+  GridInfo gi{};
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&gi.per_cu, kernel, threads, dyn_lds)) !=
+      hipSuccess)
+    return e;
+  if ((e = hipDeviceGetAttribute(&gi.cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+      hipSuccess)
+    return e;
+  if ((e = hipDeviceGetAttribute(&gi.wall_khz, hipDeviceAttributeWallClockRate, dev)) !=
+      hipSuccess)
+    return e;
+  gi.per_cu = gi.per_cu > 0 ? gi.per_cu : 1;
+  gi.cus = gi.cus > 0 ? gi.cus : 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 64) cache[used++] = Entry{kernel, dev, dyn_lds, gi};
+  *out = gi;
+  return hipSuccess;
+}
+
+}  // namespace nsa

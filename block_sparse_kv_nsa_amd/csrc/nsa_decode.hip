@@ -301,12 +301,10 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   if (bpw <= 0) {
     const void* fn = L.early_stop ? reinterpret_cast<const void*>(decode_kernel<T, D, G, true>)
                                   : reinterpret_cast<const void*>(decode_kernel<T, D, G, false>);
-    int per_cu = 0, dev = 0, cus = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
-    if (e == hipSuccess) e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    GridInfo gi;
+    const hipError_t e = grid_info(fn, kThreads, 0, &gi);
     if (e != hipSuccess) return e;
-    bpw = balanced_blocks_per_split(lay.rows, lay.items_max, max(1, per_cu) * max(1, cus));
+    bpw = balanced_blocks_per_split(lay.rows, lay.items_max, gi.per_cu * gi.cus);
   }
   a.bpw = bpw;
   dim3 grid((lay.items_max + bpw - 1) / bpw, lay.rows);

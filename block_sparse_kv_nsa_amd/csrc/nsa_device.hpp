@@ -261,6 +261,119 @@ __device__ void wave_top_m(const uint32_t* keys, int n, int m, uint32_t* hist, E
 }
 
 // ---------------------------------------------------------------------------
+// workgroup top-m
+// ---------------------------------------------------------------------------
+// The same selection as wave_top_m (the m largest keys, ties to the lower
+// index, emitted in index order with emit(i, rank)), computed by all kThreads
+// threads, without atomics on shared histogram bins.  Each entry is packed as
+// (key << 32) | ~index, so packed values are distinct and order by key, then
+// by lower index; the m-th largest packed value Tm is the exact threshold.
+//  1. Every thread takes the maximum of its entries i = t, t+256, ...; the
+//     m-th largest of these 256 maxima, T0, is <= Tm (m distinct entries are
+//     >= T0), and only the threads whose maximum is >= T0 -- at most m of
+//     them -- hold entries >= T0, so there are at most m * ceil(n/256)
+//     candidates.
+//  2. Candidates (packed >= T0) are gathered and Tm is found by counting,
+//     for each candidate, the candidates above it.
+//  3. One wave visits the entries in index order and emits packed >= Tm.
+// More than kTopCap candidates (large m, or many entries per thread) falls
+// back to wave_top_m.  Called by all threads; ends with a barrier.
+constexpr int kTopCap = 1024;
+
+struct TopSmem {
+  uint64_t tmax[kThreads];
+  uint64_t cand[kTopCap];
+  uint64_t t0, tm;
+  int count;
+  uint32_t hist[256];  // for the fallback
+};
+
+__device__ __forceinline__ uint64_t top_pack(uint32_t key, int i) {
+  return key != 0u ? ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)i) : 0ull;
+}
+
+template <typename Emit>
+__device__ void wg_top_m(const uint32_t* keys, int n, int m, TopSmem& ts, Emit emit) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  uint64_t mx = 0ull;
+  for (int i = t; i < n; i += kThreads) {
+    const uint64_t p = top_pack(keys[i], i);
+    mx = p > mx ? p : mx;
+  }
+  ts.tmax[t] = mx;
+  if (t == 0) {
+    ts.t0 = 1ull;  // fewer than m nonzero maxima: every entry is a candidate
+    ts.tm = ~0ull;
+    ts.count = 0;
+  }
+  __syncthreads();
+  if (mx != 0ull) {
+    // 16 maxima per batch, all loads issued before the compares
+    int above = 0;
+    for (int j0 = 0; j0 < kThreads; j0 += 16) {
+      uint64_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = ts.tmax[j0 + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) above += v[j] > mx;
+    }
+    if (above == m - 1) ts.t0 = mx;
+  }
+  __syncthreads();
+  const uint64_t t0 = ts.t0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = 0; base < n; base += kThreads) {
+    const int i = base + t;
+    const uint64_t p = i < n ? top_pack(keys[i], i) : 0ull;
+    const bool c = p >= t0;
+    const uint64_t bm = __ballot(c);
+    int pos0 = 0;
+    if (lane == 0 && bm != 0ull) pos0 = atomicAdd(&ts.count, __popcll(bm));
+    pos0 = __shfl(pos0, 0, kWave);
+    const int pos = pos0 + __popcll(bm & below);
+    if (c && pos < kTopCap) ts.cand[pos] = p;
+  }
+  __syncthreads();
+  const int nc = ts.count;
+  if (nc > kTopCap) {
+    if (wave == 0) wave_top_m(keys, n, m, ts.hist, emit);
+    __syncthreads();
+    return;
+  }
+  // candidates past nc read as 0 (below every candidate)
+  const int nc16 = (nc + 15) & ~15;
+  for (int i = nc + t; i < nc16; i += kThreads) ts.cand[i] = 0ull;
+  __syncthreads();
+  for (int ci = t; ci < nc; ci += kThreads) {
+    const uint64_t mine = ts.cand[ci];
+    int above = 0;
+    for (int j0 = 0; j0 < nc16; j0 += 16) {
+      uint64_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = ts.cand[j0 + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) above += v[j] > mine;
+    }
+    if (above == m - 1) ts.tm = mine;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t tm = ts.tm;
+    int taken = 0;
+    for (int base = 0; base < n; base += kWave) {
+      const int i = base + lane;
+      const bool take = i < n && top_pack(keys[i], i) >= tm;
+      const uint64_t bm = __ballot(take);
+      if (take) emit(i, taken + __popcll(bm & below));
+      taken += __popcll(bm);
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // cross-workgroup hand-off without cache-wide fences
 // ---------------------------------------------------------------------------
 // A workgroup that hands data to the last workgroup of its row writes that

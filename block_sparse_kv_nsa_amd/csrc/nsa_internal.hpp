@@ -10,6 +10,14 @@ namespace nsa {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Resident workgroups per compute unit of a kernel (at a dynamic shared
+// memory size), compute units and wall-clock rate of the current device,
+// cached per (kernel, device, shared memory) after the first query.
+struct GridInfo {
+  int per_cu, cus, wall_khz;
+};
+hipError_t grid_info(const void* kernel, int threads, size_t dyn_lds, GridInfo* out);
+
 struct RepsLaunch {
   int dtype, D;
   const void* k_pool;
@@ -150,50 +158,75 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// fused step: [queue ctrl | row ctrl | chunk stats | row normaliser | chunk
-//              candidates | eviction lists | query-aware lists | partials]
+// fused step (one gang of workgroups per row):
+//   [control words | arrival words | member statistics | member candidates |
+//    member partial (m, l) | member partial acc]
+// Member buffers are sized for kMaxGang members so that the gang size can be
+// chosen at launch from the device's capacity.
 // ---------------------------------------------------------------------------
-enum : int { kHead = 0, kExit = 1, kErr = 2, kCtrlWords = 4 };
-enum : int {
-  kCntA = 0, kFlagLse = 1, kCntS = 2, kFlagQ = 3, kFlagE = 4, kCntD = 5, kNE = 6, kNQ = 7,
-  kRowWords = 8
-};
+enum : int { kErr = 2, kCtrlWords = 4 };
+constexpr int kGangWords = 3;    // per row: statistics, candidates, partials
+constexpr int kMaxGang = 64;     // most workgroups per row
+constexpr int kGangReps = 512;   // most representatives a member scores (in registers)
 
 struct StepLayout {
-  int rows, G, D, nb_max, chunks, mloc, bpw, splitsE, splitsQ;
-  size_t off_rowctl, off_stats, off_lse, off_cand, off_elist, off_qlist, off_ml, off_acc, bytes;
-  size_t dyn_lds;
+  int rows, G, D, nb_max, mloc_max;
+  size_t off_words, off_stats, off_cand, off_ml, off_acc, bytes;
 };
 
-constexpr int kStepChunk = 512;  // representatives per scoring task
-
-inline StepLayout step_layout(int B, int Hkv, int G, int D, int k, int k_e, int max_seq_len,
-                              int bpw_override) {
+inline StepLayout step_layout(int B, int Hkv, int G, int D, int k, int k_e, int max_seq_len) {
   StepLayout s{};
   s.rows = B * Hkv;
   s.G = G;
   s.D = D;
   s.nb_max = max_seq_len / 64;
-  const int nsub = 4 * s.nb_max;
-  s.chunks = nsub > 0 ? (nsub + kStepChunk - 1) / kStepChunk : 1;
-  s.mloc = k - k_e;  // the query-aware part never takes more than k - k_e blocks
-  s.bpw = bpw_override > 0 ? bpw_override : decode_blocks_per_split(s.rows, k + 1);
-  s.splitsE = (k_e + 1 + s.bpw - 1) / s.bpw;  // eviction set + tail block
-  s.splitsQ = (k - k_e + s.bpw - 1) / s.bpw;
-  const size_t parts = (size_t)s.rows * (s.splitsE + s.splitsQ);
-  s.off_rowctl = 256;
-  s.off_stats = round_up(s.off_rowctl + (size_t)s.rows * kRowWords * 4, 256);
-  s.off_lse = round_up(s.off_stats + (size_t)s.rows * s.chunks * G * 8, 256);
-  s.off_cand = round_up(s.off_lse + (size_t)s.rows * G * 8, 256);
-  s.off_elist = round_up(s.off_cand + (size_t)s.rows * s.chunks * s.mloc * 8, 256);
-  s.off_qlist = round_up(s.off_elist + (size_t)s.rows * (k_e > 0 ? k_e : 1) * 4, 256);
-  s.off_ml = round_up(s.off_qlist + (size_t)s.rows * k * 4, 256);
-  s.off_acc = round_up(s.off_ml + parts * G * 8, 256);
-  s.bytes = round_up(s.off_acc + parts * G * D * 4, 256);
-  const size_t lds_e = (size_t)(k_e + s.nb_max) * 4 + (size_t)2 * k_e * 4;
-  const size_t lds_a = (size_t)2 * s.chunks * s.mloc * 4 + (size_t)k * 4 + round_up(s.nb_max, 4);
-  s.dyn_lds = round_up(lds_e > lds_a ? lds_e : lds_a, 16);
+  s.mloc_max = k - k_e > 0 ? k - k_e : 1;  // the query-aware part takes at most k - k_e
+  const size_t members = (size_t)s.rows * kMaxGang;
+  s.off_words = 256;
+  s.off_stats = round_up(s.off_words + (size_t)s.rows * kGangWords * 4, 256);
+  s.off_cand = round_up(s.off_stats + members * G * 8, 256);
+  s.off_ml = round_up(s.off_cand + members * s.mloc_max * 8, 256);
+  s.off_acc = round_up(s.off_ml + members * G * 8, 256);
+  s.bytes = round_up(s.off_acc + members * G * D * 4, 256);
   return s;
+}
+
+// Dynamic shared memory of a member: the eviction set, then the larger of
+// the eviction update (keys of old set + new blocks, old set) and the
+// selection (all members' candidates, the query-aware list, block flags).
+inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e, int C, int mloc = 0) {
+  const int ml = mloc > 0 ? mloc : lay.mloc_max;
+  const size_t eids = (size_t)(k_e > 0 ? k_e : 1) * 4;
+  const size_t upd = (size_t)(k_e + lay.nb_max) * 4 + (size_t)k_e * 4;
+  const size_t sel = (size_t)C * ml * 8 + (size_t)k * 4 + round_up((size_t)lay.nb_max, 4);
+  return round_up(eids + (upd > sel ? upd : sel), 16);
+}
+
+struct GangPlan {
+  int C, gangs, per_wg, mloc;
+  size_t dyn_lds;
+};
+
+// Gang size: enough members to hold the longest row's representatives in
+// registers, and as many as the resident workgroups allow across the rows (at
+// most kMaxGang).  Rows beyond the resident gangs are taken in turn.
+inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int c_override,
+                      GangPlan* p) {
+  const int nsub = 4 * lay.nb_max;
+  const int c_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
+  const int c_cap = capacity < kMaxGang ? capacity : kMaxGang;
+  if (c_min > c_cap) return false;
+  int C = c_override > 0 ? c_override : capacity / (lay.rows > 0 ? lay.rows : 1);
+  C = C < c_min ? c_min : (C > c_cap ? c_cap : C);
+  p->C = C;
+  p->gangs = capacity / C < lay.rows ? capacity / C : lay.rows;
+  if (p->gangs < 1) return false;
+  const int per = nsub > 0 ? (nsub + C - 1) / C : 4;
+  p->per_wg = (int)round_up((size_t)per, 4);
+  const int blocks = p->per_wg / 4;
+  p->mloc = k - k_e < blocks ? (k - k_e > 0 ? k - k_e : 1) : blocks;
+  p->dyn_lds = gang_dyn_lds(lay, k, k_e, C, p->mloc);
+  return true;
 }
 
 struct StepLaunch {
@@ -214,6 +247,8 @@ struct StepLaunch {
   void* workspace;
   int B, Hkv, max_blocks, k, k_e;
   float scale;
+  int gang_override;  // 0: from capacity
+  int e_first_pct;    // share of the eviction-set attention done before the normaliser wait
   StepLayout lay;
 };
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream);

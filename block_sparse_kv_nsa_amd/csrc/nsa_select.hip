@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   // eviction set: the k_e best of (old set U newly full blocks) by E.  With
   // no newly full block the candidates are the old set itself: unchanged.
   __shared__ int s_ne;
-  __shared__ __align__(16) uint32_t hist[256];
+  __shared__ TopSmem top;
   if (threadIdx.x == 0) s_ne = 0;
   if (a.k_e > 0 && !a.ordered) {
     int seen = a.evict_seen[row];
@@ -231,11 +231,10 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
         keys[i] = order_key(Er[id]);
       }
       __syncthreads();
-      if (wave == 0 && n_e > 0) {
-        wave_top_m(keys, ncand, n_e, hist, [&](int i, int pos) {
+      if (n_e > 0)
+        wg_top_m(keys, ncand, n_e, top, [&](int i, int pos) {
           ev_new[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
         });
-      }
     }
     if (threadIdx.x == 0) s_ne = n_e;
     __syncthreads();
@@ -295,22 +294,20 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   }
   __syncthreads();
 
-  // query-aware part (or the ordered list) on wave 0, no workgroup barriers
+  // query-aware part (or the ordered list)
   const int mq = a.ordered ? min(a.k, nb) : min(a.k - n_e, nb - n_e);
   int32_t* out = a.selected + (int64_t)row * a.k;
   __shared__ int s_count;
+  if (mq > 0) {
+    const bool ordered = a.ordered != 0;
+    wg_top_m(keys, nb, mq, top, [&](int i, int pos) {
+      if (ordered) ord[pos] = i;
+      else flags[i] = 1;
+    });
+  }
   if (wave == 0) {
-    if (mq > 0) {
-      const bool ordered = a.ordered != 0;
-      wave_top_m(keys, nb, mq, hist, [&](int i, int pos) {
-        if (ordered) ord[pos] = i;
-        else flags[i] = 1;
-      });
-    }
     if (!a.ordered) {
       // selected = flagged blocks, ascending
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
       int taken = 0;
       const uint64_t below = (1ull << lane) - 1ull;
       for (int base = 0; base < nb; base += 8 * kWave) {

@@ -1,34 +1,35 @@
 // Fused decode step: eviction-set update, block scoring, selection and sparse
-// attention of one decode step in a single persistent launch.
+// attention of one decode step in a single cooperative launch.
 //
 // The step is the same computation as nsa_select_blocks followed by
 // nsa_sparse_decode (NOSA technical summary, "Mecanismo de Doble Selección",
 // "Implementación Basada en Bloques"; SparDA technical summary, "Kompakter
-// Forecast-Indexer"); only the schedule differs.  Workgroups pull tasks from
-// an in-order queue:
+// Forecast-Indexer"); only the schedule differs.  Each row (sequence b, KV
+// head g) is handled by a gang of C workgroups, all resident at once (the
+// launch is cooperative).  Member c of the gang
+//   1. streams its contiguous share of the row's sub-block representatives
+//      and keeps the logits q.r in registers;
+//   2. publishes its softmax statistics (group-softmax mode);
+//   3. derives the row's eviction set (it depends on the eviction scores
+//      only, never on the query) and attends part of its share of those
+//      blocks and of the partial tail block while the other members finish
+//      streaming;
+//   4. once every member's statistics are in, forms the row normaliser,
+//      scores its own blocks and publishes its best candidates for the
+//      query-aware part (the row's best blocks are among the members' best),
+//      then attends the rest of its eviction-set share;
+//   5. once every member's candidates are in, selects the row's query-aware
+//      blocks itself (every member reaches the same set) and attends its
+//      share of them;
+//   6. stores its partial; the last member to arrive merges the C partials
+//      into the output.
+// Member 0 writes the eviction state and the selected list for the caller.
 //
-//   E(r)     eviction set of row r.  It depends on the eviction scores only,
-//            never on the query, so it is known before any scoring.
-//   A(r,c)   chunk c of row r's sub-block representatives: logits in
-//            registers, chunk softmax statistics, then (once the row's
-//            normaliser is published) block scores from those registers and
-//            the chunk's own best candidates for the query-aware part.  The
-//            row's last chunk merges the candidates (the row's best blocks
-//            are among the chunks' best) and publishes the query-aware set.
-//   DE(r,s)  attention over split s of the eviction set and the tail block
-//            (runs while scoring and selection are still in progress).
-//   DQ(r,s)  attention over split s of the query-aware set.
-// The last attention task of a row merges the row's partials.
-//
-// A task only ever waits for tasks that were dequeued before it, and every
-// dequeued task runs on a resident workgroup, so waits always end (a row's
-// chunk count is capped below the grid size, which covers the only wait
-// between tasks of the same kind).  Each wait is still bounded: on expiry the
-// workgroup records an error word and goes on.
-//
-// Data handed between tasks is written with agent-scope stores and read with
-// agent-scope loads; a hand-off flag is raised only after the writer's stores
-// have completed (see last_arrival in nsa_device.hpp).
+// Hand-offs between members use agent-scope stores and loads and 32-bit
+// arrival words per row (see gang_arrive); the last member of a row resets
+// the row's words, so the workspace is left as it was found.  Every wait is
+// bounded in time: on expiry the workgroup records a sticky error word, later
+// waits of the launch return at once, and the launch ends.
 #include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
@@ -36,12 +37,9 @@
 namespace nsa {
 namespace {
 
-// A wait gives up after 0.2 s of the constant-rate wall clock; once any wait
-// has given up, later waits of the launch return at once, so a broken
-// hand-off ends the launch quickly with the error word set.
-constexpr int kWaitMs = 200;
+constexpr int kWaitMs = 200;  // longest a member waits for its gang
 
-struct StepArgs {
+struct GangArgs {
   const void* query;  // group-softmax: [B][Hq][D]; forecast: [B][Hkv][D]
   const void* q;      // [B][Hq][D]
   const void* reps;
@@ -55,20 +53,16 @@ struct StepArgs {
   int32_t* selected;
   int32_t* num_selected;
   void* out;
-  uint32_t* ctrl;    // [kCtrlWords]
-  uint32_t* rowctl;  // [rows][kRowWords]
-  float* stats;      // [rows][chunks][G] (m, s)
-  float* lse;        // [rows][G] (m, 1/s)
-  uint32_t* cand;    // [rows][chunks][mloc] (key, block)
-  int32_t* elist;    // [rows][k_e]
-  int32_t* qlist;    // [rows][k]
-  float* part_ml;    // [rows][splits][G] (m, l)
-  float* part_acc;   // [rows][splits][G][D]
-  int Hkv, max_blocks, nb_max, k, k_e, chunks, mloc, bpw, splitsE, splitsQ;
-  int nE, nA, nDE, nDQ;
+  uint32_t* err;     // sticky error word
+  uint32_t* words;   // [rows][kGangWords] arrival words
+  float* stats;      // [rows][kMaxGang][G] (m, s)
+  uint32_t* cand;    // [rows][kMaxGang][mloc_max] (key, block)
+  float* part_ml;    // [rows][kMaxGang][G] (m, l)
+  float* part_acc;   // [rows][kMaxGang][G][D]
+  int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg, mloc, mloc_max, e_first_pct;
   float qscale_sel, qscale_att;
-  uint64_t wait_ticks;  // wall-clock ticks before a wait gives up
-  uint32_t stats_bytes, lse_bytes, cand_bytes, elist_bytes, qlist_bytes, ml_bytes, acc_bytes;
+  uint64_t wait_ticks;
+  uint32_t stats_bytes, cand_bytes, ml_bytes, acc_bytes;
 };
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
@@ -78,11 +72,25 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Whole workgroup: wait until *p >= target (bounded in time).
-__device__ void wait_word(uint32_t* p, uint32_t target, uint32_t* err, uint64_t wait_ticks) {
-  if (threadIdx.x == 0 && ld_agent(p) < target) {
+// Whole workgroup: record this member's arrival at a row's word once every
+// store it issued has completed.  Returns whether it was the last of the C.
+__device__ bool gang_arrive(uint32_t* word, int C, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = prev + 1 == (uint32_t)C;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Whole workgroup: wait until all C members arrived at `word` (bounded).
+__device__ void gang_wait(const uint32_t* word, int C, uint32_t* err, uint64_t wait_ticks) {
+  if (threadIdx.x == 0 && ld_agent(word) < (uint32_t)C) {
     const uint64_t t0 = (uint64_t)wall_clock64();
-    while (ld_agent(p) < target) {
+    while (ld_agent(word) < (uint32_t)C) {
       if (ld_agent(err) != 0u) break;
       if ((uint64_t)wall_clock64() - t0 > wait_ticks) {
         st_agent(err, 1u);
@@ -94,98 +102,53 @@ __device__ void wait_word(uint32_t* p, uint32_t target, uint32_t* err, uint64_t 
   __syncthreads();
 }
 
-// Whole workgroup: raise *p after every thread's agent-scope stores completed.
-__device__ void publish(uint32_t* p) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) st_agent(p, 1u);
-}
-
 template <typename T, int D, int G, bool FORECAST>
-struct Step {
+struct Gang {
   using Q = Quad<T, D>;
   static constexpr int NLD = Q::NLD;
   static constexpr int GS = FORECAST ? 1 : G;
   static constexpr int KEEP = GS >= 4 ? GS / 4 : 1;
   static constexpr int DUP = GS >= 4 ? 1 : 4 / GS;
-  static constexpr int U = 8;                      // representative slots per lane
-  static constexpr int RPI = kThreads / 4;         // representatives per slot (64)
-  static constexpr int CHUNK = U * RPI;            // representatives per A task (512)
-  static constexpr int CBLK = CHUNK / kSubs;       // blocks per A task (128)
+  static constexpr int RPI = kThreads / 4;        // representatives per load slot (64)
+  static constexpr int U = kGangReps / RPI;       // slots per lane
+  static constexpr int CBLK = kGangReps / kSubs;  // most blocks a member scores
 
   struct Smem {
     AttendSmem<T, D, G> att;
+    WgAcc<D, G> acc;
+    TopSmem top;
+    float lgs[U][KEEP][kThreads];  // the logits, parked during attention
     float sM[G], sInvZ[G];
     float red_m[kWaves][4][KEEP], red_s[kWaves][4][KEEP];
-    uint32_t ckeys[CBLK];
-    uint32_t hist[256] __attribute__((aligned(16)));
-    int s_int[4];
+    uint32_t ckeys[CBLK] __attribute__((aligned(16)));
+    int s_int[8];
   };
 
-  // ---------------------------------------------------------------- E(r)
-  static __device__ void task_E(const StepArgs& a, int row, Smem& sm, uint32_t* dyn) {
-    const int b = row / a.Hkv;
-    const int nb = min(a.seq_lens[b] / kBlock, a.nb_max);
-    uint32_t* rc = a.rowctl + (int64_t)row * kRowWords;
-    int n_e = 0;
-    if (a.k_e > 0) {
-      uint32_t* keys = dyn;                                           // k_e + nb_max
-      int* ev_old = reinterpret_cast<int*>(keys + a.k_e + a.nb_max);  // k_e
-      int* ev_new = ev_old + a.k_e;                                   // k_e
-      int seen = a.evict_seen[row];
-      if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
-      const int nprev = min(a.k_e, seen);
-      for (int i = threadIdx.x; i < nprev; i += kThreads)
-        ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
-      __syncthreads();
-      const int ncand = nprev + nb - seen;
-      n_e = min(a.k_e, ncand);
-      if (seen == nb) {
-        for (int i = threadIdx.x; i < n_e; i += kThreads) ev_new[i] = ev_old[i];
-      } else {
-        const float* Er = a.E + (int64_t)row * a.max_blocks;
-        for (int i = threadIdx.x; i < ncand; i += kThreads) {
-          const int id = i < nprev ? ev_old[i] : seen + i - nprev;
-          keys[i] = order_key(Er[id]);
-        }
-        __syncthreads();
-        if (threadIdx.x < kWave && n_e > 0)
-          wave_top_m(keys, ncand, n_e, sm.hist, [&](int i, int pos) {
-            ev_new[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
-          });
-      }
-      __syncthreads();
-      const __amdgpu_buffer_rsrc_t er = make_rsrc(a.elist, a.elist_bytes);
-      for (int i = threadIdx.x; i < a.k_e; i += kThreads) {
-        const int v = i < n_e ? ev_new[i] : -1;
-        a.evict_set[(int64_t)row * a.k_e + i] = v;
-        if (i < n_e)
-          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, er,
-                                                (int)(((int64_t)row * a.k_e + i) * 4), 0, kSC1);
-      }
-      if (threadIdx.x == 0) a.evict_seen[row] = nb;
-    }
-    if (threadIdx.x == 0) st_agent(rc + kNE, (uint32_t)n_e);
-    publish(rc + kFlagE);
-    __syncthreads();
-  }
-
-  // -------------------------------------------------------------- A(r,c)
-  static __device__ void task_A(const StepArgs& a, int row, int chunk, Smem& sm, uint32_t* dyn) {
+  static __device__ __attribute__((always_inline)) void row_step(const GangArgs& a, int row, int c,
+                                                                 Smem& sm, uint32_t* dyn) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int q = lane & 3, r = lane >> 2;
     const int b = row / a.Hkv, g = row % a.Hkv;
-    const int nb = min(a.seq_lens[b] / kBlock, a.nb_max);
+    const int C = a.C;
+    const int L = a.seq_lens[b];
+    const int nb = min(L / kBlock, a.nb_max);
+    const int tail = L - nb * kBlock;
     const int nsub = nb * kSubs;
-    const int j0 = chunk * CHUNK;
-    const int j1 = min(j0 + CHUNK, nsub);
+    const int j0 = min(c * a.per_wg, nsub);
+    const int j1 = min(j0 + a.per_wg, nsub);
     const int h0 = GS >= 4 ? q * KEEP : q / DUP;
     const bool canon = (q % DUP) == 0;
-    uint32_t* rc = a.rowctl + (int64_t)row * kRowWords;
-    uint32_t* err = a.ctrl + kErr;
+    uint32_t* words = a.words + (int64_t)row * kGangWords;
+    int* eids = reinterpret_cast<int*>(dyn);             // k_e: the eviction set
+    uint32_t* scratch = dyn + (a.k_e > 0 ? a.k_e : 1);   // per-phase scratch
+    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
+    const T* kp = static_cast<const T*>(a.k_pool);
+    const T* vp = static_cast<const T*>(a.v_pool);
 
-    // ---- logits of the chunk, kept in registers
+    wg_acc_init(sm.acc);
+
+    // ---- 1. logits of this member's representatives, in registers
     float lg[U][KEEP];
     {
       QSlice<T, D> qs[GS];
@@ -194,9 +157,9 @@ struct Step {
 #pragma unroll
       for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
       const T* rb = static_cast<const T*>(a.reps) + (int64_t)row * a.max_blocks * kSubs * D;
-      // slots in flight per lane: all 8 at small group sizes, 4 + 4 when the
-      // query slices of 4 or 8 heads already take many registers
-      constexpr int USL = GS >= 4 ? 4 : U;
+      // slots in flight per lane: 8 at small group sizes, 4 when the query
+      // slices of 4 or 8 heads already take many registers
+      constexpr int USL = GS >= 4 ? 4 : 8;
 #pragma unroll
       for (int u0 = 0; u0 < U; u0 += USL) {
         uint4 x[USL][NLD];
@@ -222,7 +185,8 @@ struct Step {
       }
     }
 
-    // ---- group softmax: chunk statistics, row normaliser
+    // ---- 2. softmax statistics of this member's logits (group softmax)
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
     if constexpr (!FORECAST) {
       float m[KEEP], s[KEEP];
 #pragma unroll
@@ -249,22 +213,84 @@ struct Step {
         }
       }
       __syncthreads();
-      const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
       if (threadIdx.x < G) {
         const int h = threadIdx.x;
         const int qq = G >= 4 ? h / KEEP : h * DUP, kk = G >= 4 ? h % KEEP : 0;
         float M = sm.red_m[0][qq][kk], S = sm.red_s[0][qq][kk];
         for (int w = 1; w < kWaves; ++w) merge_ms(M, S, sm.red_m[w][qq][kk], sm.red_s[w][qq][kk]);
-        store_agent_f32x2(srs, (uint32_t)((((int64_t)row * a.chunks + chunk) * G + h) * 8),
+        store_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + c) * G + h) * 8),
                           f32x2{M, S});
       }
-      const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse, a.lse_bytes);
-      if (last_arrival(rc + kCntA, a.chunks, &sm.s_int[0])) {
-        // normaliser per head from all chunk statistics
-        const int nstat = a.chunks * G;
+      gang_arrive(words + 0, C, &sm.s_int[0]);
+    }
+    // the logits wait in shared memory while this member attends
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) sm.lgs[u][kk][threadIdx.x] = lg[u][kk];
+    }
+
+    // ---- 3. the eviction set: the k_e best of (old set U blocks that became
+    // full since the last call) by eviction score, ties to the lower id
+    int n_e = 0;
+    if (a.k_e > 0) {
+      int seen = a.evict_seen[row];
+      if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
+      const int nprev = min(a.k_e, seen);
+      const int ncand = nprev + nb - seen;
+      n_e = min(a.k_e, ncand);
+      if (seen == nb) {
+        for (int i = threadIdx.x; i < n_e; i += kThreads)
+          eids[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+      } else {
+        uint32_t* keys = scratch;                                       // ncand
+        int* ev_old = reinterpret_cast<int*>(keys + a.k_e + a.nb_max);  // k_e
+        for (int i = threadIdx.x; i < nprev; i += kThreads)
+          ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+        __syncthreads();
+        const float* Er = a.E + (int64_t)row * a.max_blocks;
+        for (int i = threadIdx.x; i < ncand; i += kThreads) {
+          const int id = i < nprev ? ev_old[i] : seen + i - nprev;
+          keys[i] = order_key(Er[id]);
+        }
+        __syncthreads();
+        if (n_e > 0)
+          wg_top_m(keys, ncand, n_e, sm.top, [&](int i, int pos) {
+            eids[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
+          });
+      }
+    }
+    __syncthreads();
+
+    // ---- attention over this member's share of the eviction set + tail:
+    // items c, c + C, c + 2C, ... of [eviction set..., tail]
+    auto e_item = [&](int it) {
+      const int idx = c + it * C;
+      const int blk = idx < n_e ? eids[idx] : nb;
+      const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
+      Item x;
+      x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
+      x.valid = idx < n_e ? kBlock : tail;
+      x.logits = nullptr;
+      return x;
+    };
+    const int n_eitems = n_e + (tail > 0);
+    const int e_mine = n_eitems > c ? (n_eitems - c + C - 1) / C : 0;
+    const int e_first = (e_mine * a.e_first_pct + 99) / 100;
+    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att,
+                                       sm.acc);
+
+    // ---- 4. row normaliser from every member's statistics
+    uint32_t* err = a.err;
+    if constexpr (!FORECAST) {
+      gang_wait(words + 0, C, err, a.wait_ticks);
+      if (threadIdx.x < kWave) {
+        // lane: members lane / G, + 64 / G, ...; head lane % G
         float M = -INFINITY, S = 0.f;
-        for (int i = threadIdx.x; i < nstat; i += kThreads) {
-          const f32x2 st = load_agent_f32x2(srs, (uint32_t)(((int64_t)row * nstat + i) * 8));
+        const int h = lane % G;
+        for (int m2 = lane / G; m2 < C; m2 += kWave / G) {
+          const f32x2 st =
+              load_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + m2) * G + h) * 8));
           merge_ms(M, S, st.x, st.y);
         }
 #pragma unroll
@@ -274,55 +300,32 @@ struct Step {
           merge_ms(M, S, m2, s2);
         }
         if (lane < G) {
-          sm.att.wm[wave][lane] = M;
-          sm.att.wl[wave][lane] = S;
+          sm.sM[lane] = M;
+          sm.sInvZ[lane] = S > 0.f ? 1.f / S : 0.f;
         }
-        __syncthreads();
-        if (threadIdx.x < G) {
-          const int h = threadIdx.x;
-          float Mh = sm.att.wm[0][h], Sh = sm.att.wl[0][h];
-          for (int w = 1; w < kWaves; ++w) merge_ms(Mh, Sh, sm.att.wm[w][h], sm.att.wl[w][h]);
-          store_agent_f32x2(lr, (uint32_t)(((int64_t)row * G + h) * 8),
-                            f32x2{Mh, Sh > 0.f ? 1.f / Sh : 0.f});
-        }
-        publish(rc + kFlagLse);
-      }
-      wait_word(rc + kFlagLse, 1u, err, a.wait_ticks);
-      if (threadIdx.x < G) {
-        const f32x2 v = load_agent_f32x2(lr, (uint32_t)(((int64_t)row * G + threadIdx.x) * 8));
-        sm.sM[threadIdx.x] = v.x;
-        sm.sInvZ[threadIdx.x] = v.y;
       }
     }
 
-    // ---- eviction set of the row (excluded from the query-aware part)
-    wait_word(rc + kFlagE, 1u, err, a.wait_ticks);
-    const int n_e = (int)ld_agent(rc + kNE);
+    // ---- 5. scores of this member's blocks; its best candidates
     const int blk0 = j0 / kSubs;
     for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
     __syncthreads();
-    {
-      const __amdgpu_buffer_rsrc_t er = make_rsrc(a.elist, a.elist_bytes);
-      for (int i = threadIdx.x; i < n_e; i += kThreads) {
-        const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(
-            er, (int)(((int64_t)row * a.k_e + i) * 4), 0, kSC1);
-        if (id >= blk0 && id < blk0 + CBLK) sm.ckeys[id - blk0] = 0u;
-      }
+    for (int i = threadIdx.x; i < n_e; i += kThreads) {
+      const int id = eids[i];
+      if (id >= blk0 && id < blk0 + CBLK) sm.ckeys[id - blk0] = 0u;
     }
     __syncthreads();
-
-    // ---- block scores from the registers: sum the heads of a sub-block
-    // (quad), maximum over the block's 4 sub-blocks (4 quads of a DPP row)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float v = 0.f;
       if constexpr (FORECAST) {
-        v = lg[u][0];
+        v = sm.lgs[u][0][threadIdx.x];
       } else {
 #pragma unroll
-        for (int kk = 0; kk < KEEP; ++kk)
-          if (canon && lg[u][kk] != -INFINITY)
-            v += exp2f(lg[u][kk] - sm.sM[h0 + kk]) * sm.sInvZ[h0 + kk];
+        for (int kk = 0; kk < KEEP; ++kk) {
+          const float l = sm.lgs[u][kk][threadIdx.x];
+          if (canon && l != -INFINITY) v += exp2f(l - sm.sM[h0 + kk]) * sm.sInvZ[h0 + kk];
+        }
         v += quad_partner<2>(v);
         v += quad_partner<1>(v);
       }
@@ -331,187 +334,161 @@ struct Step {
       if ((lane & 15) == 0) {
         const int bl = u * 16 + wave * 4 + (lane >> 4);
         const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
-        const bool valid = j < j1;
-        sm.ckeys[bl] = (valid && sm.ckeys[bl] != 0u) ? order_key(v) : 0u;
+        sm.ckeys[bl] = (j < j1 && sm.ckeys[bl] != 0u) ? order_key(v) : 0u;
       }
     }
     __syncthreads();
 
-    // ---- the chunk's best candidates for the query-aware part
+    // a block's rank is the number of this member's blocks ahead of it
+    // (higher key, or equal key and lower id); slot r of the member's list
+    // gets the block of rank r, slots past its count an empty entry
     const int m_row = max(0, min(a.k - n_e, nb - n_e));
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.cand, a.cand_bytes);
-    const int64_t cbase = ((int64_t)row * a.chunks + chunk) * a.mloc;
-    if (threadIdx.x < kWave) {
-      int nz = 0;
-      for (int i = lane; i < CBLK; i += kWave) nz += sm.ckeys[i] != 0u;
+    {
+      const int64_t cbase = ((int64_t)row * kMaxGang + c) * a.mloc_max;
+      const int t = threadIdx.x;
+      const uint64_t mine = t < CBLK ? top_pack(sm.ckeys[t], t) : 0ull;
+      const int nz = __syncthreads_count(mine != 0ull);
+      const int mc = min(min(m_row, nz), a.mloc);
+      if (mine != 0ull) {
+        // 16 keys per batch (four 16-byte reads) before the compares
+        int ahead = 0;
+        for (int j0 = 0; j0 < CBLK; j0 += 16) {
+          uint4 kv[4];
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) nz += __shfl_xor(nz, off, kWave);
-      const int mc = min(m_row, nz);
-      for (int i = lane; i < a.mloc; i += kWave)
+          for (int v4 = 0; v4 < 4; ++v4) kv[v4] = *reinterpret_cast<const uint4*>(&sm.ckeys[j0 + 4 * v4]);
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            ahead += top_pack(kv[v4].x, j0 + 4 * v4) > mine;
+            ahead += top_pack(kv[v4].y, j0 + 4 * v4 + 1) > mine;
+            ahead += top_pack(kv[v4].z, j0 + 4 * v4 + 2) > mine;
+            ahead += top_pack(kv[v4].w, j0 + 4 * v4 + 3) > mine;
+          }
+        }
+        if (ahead < mc)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[t], (uint32_t)(blk0 + t)}, cr,
+                                                (int)((cbase + ahead) * 8), 0, kSC1);
+      }
+      for (int i = mc + t; i < a.mloc; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, cr, (int)((cbase + i) * 8), 0, kSC1);
-      __builtin_amdgcn_s_waitcnt(0);
-      if (mc > 0)
-        wave_top_m(sm.ckeys, CBLK, mc, sm.hist, [&](int i, int pos) {
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[i], (uint32_t)(blk0 + i)}, cr,
-                                                (int)((cbase + pos) * 8), 0, kSC1);
-        });
     }
-    if (!last_arrival(rc + kCntS, a.chunks, &sm.s_int[1])) return;
+    gang_arrive(words + 1, C, &sm.s_int[1]);
 
-    // ---- the row's last chunk: query-aware set from all chunk candidates
-    const int ncand = a.chunks * a.mloc;
-    uint32_t* ckey = dyn;                                   // ncand
-    int* cid = reinterpret_cast<int*>(ckey + ncand);        // ncand
-    int* qsel = cid + ncand;                                // k
+    // ---- the rest of this member's eviction-set share
+    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att,
+                                       sm.acc);
+
+    // ---- 6. the row's query-aware set from every member's candidates
+    gang_wait(words + 1, C, err, a.wait_ticks);
+    const int ncand = C * a.mloc;
+    uint32_t* ckey = scratch;                                 // ncand
+    int* cid = reinterpret_cast<int*>(ckey + ncand);          // ncand
+    int* qsel = cid + ncand;                                  // k
     uint8_t* flags = reinterpret_cast<uint8_t*>(qsel + a.k);  // nb_max
     for (int i = threadIdx.x; i < ncand; i += kThreads) {
+      const int m2 = i / a.mloc, s = i % a.mloc;
       const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(
-          cr, (int)((((int64_t)row * a.chunks) * a.mloc + i) * 8), 0, kSC1);
+          cr, (int)(((((int64_t)row * kMaxGang + m2) * a.mloc_max) + s) * 8), 0, kSC1);
       ckey[i] = e.x;
       cid[i] = (int)e.y;
     }
-    for (int i = threadIdx.x; i < nb; i += kThreads) flags[i] = 0;
+    if (c == 0)
+      for (int i = threadIdx.x; i < nb; i += kThreads) flags[i] = 0;
     __syncthreads();
-    if (threadIdx.x < kWave && m_row > 0)
-      wave_top_m(ckey, ncand, m_row, sm.hist, [&](int i, int pos) { qsel[pos] = cid[i]; });
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.qlist, a.qlist_bytes);
-    const __amdgpu_buffer_rsrc_t er = make_rsrc(a.elist, a.elist_bytes);
-    for (int i = threadIdx.x; i < m_row; i += kThreads) {
-      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)qsel[i], qr,
-                                            (int)(((int64_t)row * a.k + i) * 4), 0, kSC1);
-      flags[qsel[i]] = 1;
-    }
-    for (int i = threadIdx.x; i < n_e; i += kThreads)
-      flags[(int)__builtin_amdgcn_raw_buffer_load_b32(er, (int)(((int64_t)row * a.k_e + i) * 4),
-                                                      0, kSC1)] = 1;
-    if (threadIdx.x == 0) st_agent(rc + kNQ, (uint32_t)m_row);
-    publish(rc + kFlagQ);
-    __syncthreads();
-    // the union, ascending, for the caller
-    if (threadIdx.x < kWave) {
-      int32_t* out = a.selected + (int64_t)row * a.k;
-      int taken = 0;
-      const uint64_t below = (1ull << lane) - 1ull;
-      for (int base = 0; base < nb; base += 8 * kWave) {
-        bool f[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = base + j * kWave + lane;
-          f[j] = i < nb && flags[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint64_t bm = __ballot(f[j]);
-          if (f[j]) out[taken + __popcll(bm & below)] = base + j * kWave + lane;
-          taken += __popcll(bm);
-        }
-      }
-      for (int i = taken + lane; i < a.k; i += kWave) out[i] = -1;
-      if (lane == 0) a.num_selected[row] = taken;
-    }
-    __syncthreads();
-  }
+    if (m_row > 0)
+      wg_top_m(ckey, ncand, m_row, sm.top, [&](int i, int pos) { qsel[pos] = cid[i]; });
 
-  // ------------------------------------------------------- DE(r,s) / DQ(r,s)
-  template <bool EVICT>
-  static __device__ void task_D(const StepArgs& a, int row, int split, Smem& sm) {
-    const int b = row / a.Hkv, g = row % a.Hkv;
-    const int L = a.seq_lens[b];
-    const int nb = L / kBlock;
-    const int tail = L - nb * kBlock;
-    uint32_t* rc = a.rowctl + (int64_t)row * kRowWords;
-    uint32_t* err = a.ctrl + kErr;
-    wait_word(rc + (EVICT ? kFlagE : kFlagQ), 1u, err, a.wait_ticks);
-    const int nlist = (int)ld_agent(rc + (EVICT ? kNE : kNQ));
-    const int n_items = nlist + (EVICT && tail > 0);
-    const int i0 = split * a.bpw;
-    const int i1 = min(i0 + a.bpw, n_items);
-    const __amdgpu_buffer_rsrc_t lr =
-        EVICT ? make_rsrc(a.elist, a.elist_bytes) : make_rsrc(a.qlist, a.qlist_bytes);
-    const int stride = EVICT ? a.k_e : a.k;
-    auto item = [&](int it) {
-      int blk = nb;
-      if (it < nlist)
-        blk = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (int)(((int64_t)row * stride + it) * 4),
-                                                        0, kSC1);
+    if (c == 0) {
+      // the caller's outputs: eviction state and the selected ids, ascending
+      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
+        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
+      if (threadIdx.x == 0 && a.k_e > 0) a.evict_seen[row] = nb;
+      for (int i = threadIdx.x; i < m_row; i += kThreads) flags[qsel[i]] = 1;
+      for (int i = threadIdx.x; i < n_e; i += kThreads) flags[eids[i]] = 1;
+      __syncthreads();
+      if (threadIdx.x < kWave) {
+        int32_t* out = a.selected + (int64_t)row * a.k;
+        int taken = 0;
+        const uint64_t below = (1ull << lane) - 1ull;
+        for (int base = 0; base < nb; base += 8 * kWave) {
+          bool f[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int i = base + jj * kWave + lane;
+            f[jj] = i < nb && flags[i];
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const uint64_t bm = __ballot(f[jj]);
+            if (f[jj]) out[taken + __popcll(bm & below)] = base + jj * kWave + lane;
+            taken += __popcll(bm);
+          }
+        }
+        for (int i = taken + lane; i < a.k; i += kWave) out[i] = -1;
+        if (lane == 0) a.num_selected[row] = taken;
+      }
+    }
+
+    // ---- attention over this member's share of the query-aware set
+    auto q_item = [&](int it) {
+      const int blk = qsel[c + it * C];
       const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
       Item x;
       x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
-      x.valid = it < nlist ? kBlock : tail;
+      x.valid = kBlock;
       x.logits = nullptr;
       return x;
     };
-    const int nparts = a.splitsE + a.splitsQ;
+    const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
+    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
+                                       sm.acc);
+
+    // ---- 7. partials; the last member merges them into the output
     const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
     const __amdgpu_buffer_rsrc_t acr = make_rsrc(a.part_acc, a.acc_bytes);
-    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
-    attend_items<T, D, G, false>(qrow, static_cast<const T*>(a.k_pool),
-                                 static_cast<const T*>(a.v_pool), a.qscale_att, i0, i1, item,
-                                 sm.att, mlr, acr,
-                                 (int64_t)row * nparts + (EVICT ? split : a.splitsE + split));
-    if (!last_arrival(rc + kCntD, nparts, &sm.s_int[2])) return;
-    T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
-    combine_partials<T, D, G>((int64_t)row * nparts, nparts, mlr, acr, out);
-    // every task of the row is done: clear its flags for the next step
-    if (threadIdx.x == 0) {
-      st_agent(rc + kFlagLse, 0u);
-      st_agent(rc + kFlagQ, 0u);
-      st_agent(rc + kFlagE, 0u);
-      st_agent(rc + kNE, 0u);
-      st_agent(rc + kNQ, 0u);
-    }
     __syncthreads();
+    wg_acc_store(sm.acc, mlr, acr, (int64_t)row * kMaxGang + c);
+    if (!gang_arrive(words + 2, C, &sm.s_int[2])) return;
+    T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
+    combine_partials<T, D, G>((int64_t)row * kMaxGang, C, mlr, acr, out);
+    // every member has passed every wait of this row: reset its words
+    if (threadIdx.x < kGangWords) st_agent(words + threadIdx.x, 0u);
   }
 };
 
+// Two workgroups per compute unit (256 VGPRs per lane) for bf16 up to 4 heads
+// per KV head; eight heads' query slices and accumulators (and float32 keys
+// of 128 elements) need the register file of one workgroup per compute unit.
+template <typename T, int D, int G>
+constexpr int gang_wgs_per_cu() {
+  return (G >= 8 || (sizeof(T) == 4 && D == 128)) ? 1 : 2;
+}
+
 template <typename T, int D, int G, bool FORECAST>
-__global__ __launch_bounds__(kThreads, 2) void step_kernel(StepArgs a) {
-  using S = Step<T, D, G, FORECAST>;
+__global__ __launch_bounds__(kThreads, (gang_wgs_per_cu<T, D, G>())) void gang_kernel(
+    const GangArgs a) {
+  using S = Gang<T, D, G, FORECAST>;
   __shared__ typename S::Smem sm;
   extern __shared__ uint32_t dyn[];
-  __shared__ int s_task;
-  const int total = a.nE + a.nA + a.nDE + a.nDQ;
-  while (true) {
-    if (threadIdx.x == 0)
-      s_task = (int)__hip_atomic_fetch_add(a.ctrl + kHead, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+  const int gang = blockIdx.x / a.C, c = blockIdx.x % a.C;
+  for (int row = gang; row < a.rows; row += a.gangs) {
+    S::row_step(a, row, c, sm, dyn);
     __syncthreads();
-    int t = s_task;
-    __syncthreads();
-    if (t >= total) break;
-    if (t < a.nE) {
-      S::task_E(a, t, sm, dyn);
-      continue;
-    }
-    t -= a.nE;
-    if (t < a.nA) {
-      S::task_A(a, t / a.chunks, t % a.chunks, sm, dyn);
-      continue;
-    }
-    t -= a.nA;
-    if (t < a.nDE) {
-      S::template task_D<true>(a, t / a.splitsE, t % a.splitsE, sm);
-      continue;
-    }
-    t -= a.nDE;
-    S::template task_D<false>(a, t / a.splitsQ, t % a.splitsQ, sm);
-  }
-  // the last workgroup out resets the queue for the next launch
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(a.ctrl + kExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev + 1 == gridDim.x) {
-      st_agent(a.ctrl + kHead, 0u);
-      st_agent(a.ctrl + kExit, 0u);
-    }
   }
 }
 
 template <typename T, int D, int G, bool FORECAST>
 hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   const StepLayout& lay = L.lay;
-  StepArgs a{};
+  const void* fn = reinterpret_cast<const void*>(gang_kernel<T, D, G, FORECAST>);
+  // capacity with the shared memory of the largest gang, then the plan
+  GridInfo gi;
+  hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e, kMaxGang), &gi);
+  if (e != hipSuccess) return e;
+  GangPlan plan;
+  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, &plan))
+    return hipErrorLaunchOutOfResources;
+  GangArgs a{};
   a.query = L.query;
   a.q = L.q;
   a.reps = L.reps;
@@ -526,57 +503,34 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.num_selected = L.num_selected;
   a.out = L.out;
   char* ws = static_cast<char*>(L.workspace);
-  a.ctrl = reinterpret_cast<uint32_t*>(ws);
-  a.rowctl = reinterpret_cast<uint32_t*>(ws + lay.off_rowctl);
+  a.err = reinterpret_cast<uint32_t*>(ws) + kErr;
+  a.words = reinterpret_cast<uint32_t*>(ws + lay.off_words);
   a.stats = reinterpret_cast<float*>(ws + lay.off_stats);
-  a.lse = reinterpret_cast<float*>(ws + lay.off_lse);
   a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
-  a.elist = reinterpret_cast<int32_t*>(ws + lay.off_elist);
-  a.qlist = reinterpret_cast<int32_t*>(ws + lay.off_qlist);
   a.part_ml = reinterpret_cast<float*>(ws + lay.off_ml);
   a.part_acc = reinterpret_cast<float*>(ws + lay.off_acc);
+  a.rows = lay.rows;
   a.Hkv = L.Hkv;
   a.max_blocks = L.max_blocks;
   a.nb_max = lay.nb_max;
   a.k = L.k;
   a.k_e = L.k_e;
-  a.chunks = lay.chunks;
-  a.mloc = lay.mloc;
-  a.bpw = lay.bpw;
-  a.splitsE = lay.splitsE;
-  a.splitsQ = lay.splitsQ;
-  a.nE = lay.rows;
-  a.nA = lay.rows * lay.chunks;
-  a.nDE = lay.rows * lay.splitsE;
-  a.nDQ = lay.rows * lay.splitsQ;
+  a.C = plan.C;
+  a.gangs = plan.gangs;
+  a.per_wg = plan.per_wg;
+  a.mloc = plan.mloc;
+  a.mloc_max = lay.mloc_max;
+  a.e_first_pct = L.e_first_pct;
   a.qscale_sel = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;
   a.qscale_att = L.scale * 1.4426950408889634f;
-  a.stats_bytes = (uint32_t)(lay.off_lse - lay.off_stats);
-  a.lse_bytes = (uint32_t)(lay.off_cand - lay.off_lse);
-  a.cand_bytes = (uint32_t)(lay.off_elist - lay.off_cand);
-  a.elist_bytes = (uint32_t)(lay.off_qlist - lay.off_elist);
-  a.qlist_bytes = (uint32_t)(lay.off_ml - lay.off_qlist);
+  a.wait_ticks = (uint64_t)(gi.wall_khz > 0 ? gi.wall_khz : 1) * kWaitMs;
+  a.stats_bytes = (uint32_t)(lay.off_cand - lay.off_stats);
+  a.cand_bytes = (uint32_t)(lay.off_ml - lay.off_cand);
   a.ml_bytes = (uint32_t)(lay.off_acc - lay.off_ml);
   a.acc_bytes = (uint32_t)(lay.bytes - lay.off_acc);
-  const size_t dyn = lay.dyn_lds;
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(step_kernel<T, D, G, FORECAST>), kThreads, dyn);
-  if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-    return e;
-  int wall_khz = 0;
-  if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
-    return e;
-  a.wait_ticks = (uint64_t)max(wall_khz, 1) * kWaitMs;
-  const int nwg = max(1, per_cu) * max(1, cus);
-  // every scoring task of a row waits for the row's other scoring tasks, so a
-  // row's chunks must all be resident at once
-  if (lay.chunks > nwg) return hipErrorLaunchOutOfResources;
-  step_kernel<T, D, G, FORECAST><<<nwg, kThreads, dyn, stream>>>(a);
-  return hipGetLastError();
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(fn, dim3(plan.gangs * plan.C), dim3(kThreads), args,
+                                    (unsigned)plan.dyn_lds, stream);
 }
 
 template <typename T, int D, int G>
