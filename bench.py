@@ -5,8 +5,8 @@
 One step = one pass of the decode hot path for one attention layer over one
 batch: block representatives of blocks that filled (none at the measured
 workload's steps), then scoring, selection and the sparse decode, either as
-nsa_select_blocks + nsa_sparse_decode (default, --path split) or as the one
-fused launch nsa_decode_step (--path fused).  Inputs are seeded synthetic tensors already
+the one fused launch nsa_decode_step (default) or as nsa_select_blocks +
+nsa_sparse_decode (--path split).  Inputs are seeded synthetic tensors already
 resident in HBM when timing starts.  Steps rotate over R independent layer
 instances (own pools, representatives, state and workspaces; R x working set
 >= 1 GiB) so that the ~256 MB Infinity Cache cannot hold the step's bytes and
@@ -15,9 +15,11 @@ the figures are HBM figures.
 Prints one JSON line (rank 0, N = 1 only):
   value          decode tokens/s (batch / step time)
   roofline       the dominant kernel's algorithmic bytes per launch / its mean
-                 launch duration from HIP events on its stream, against the
-                 8 TB/s HBM peak; traffic = measured HBM bytes per launch from
-                 rocprofv3 FETCH_SIZE + WRITE_SIZE when a summary for the
+                 launch duration from HIP events around each launch on its
+                 stream (a second pass over the same steps, after the timed
+                 one), against the 8 TB/s HBM peak; traffic = measured HBM
+                 bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE
+                 (scaled by a copy kernel of known size) when a record for the
                  current kernel source exists under profiles/, else null
   cpu_baseline   the CPU oracle (float64 NumPy) timed on a bounded sample of
                  the same workload's rows and steps, scaled to tokens/s
@@ -55,7 +57,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle leg")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows sampled by the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="split", choices=("fused", "split"),
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one float32 scale-by-one of MIB MiB (reads and writes MIB MiB) "
+                         "before timing, the reference kernel for HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of a "
+                         "--copy-calibration run into profiles/<kernel>_<workload>_traffic.json")
+    ap.add_argument("--calibration-mib", type=int, default=256,
+                    help="the MIB of the --copy-calibration run read by --traffic-from")
+    ap.add_argument("--path", default="fused", choices=("fused", "split"),
                     help="fused: one nsa_decode_step launch; split: nsa_select_blocks + "
                          "nsa_sparse_decode")
     return ap.parse_args()
@@ -190,22 +200,38 @@ def gpu_leg(args, cfg):
         if ev is not None:
             ev[2].record(stream)
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the K timed steps: nothing but the steps between the two events
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
-    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    # per-kernel durations: the same steps again with events around each launch
+    # on the launch stream (an event between launches adds a small gap, so
+    # this pass is kept apart from the timed one)
+    n_ev = min(args.steps, 1000)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ev
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_ev
 
     n_sel = layers[0].num_selected.float().mean().item()
     L_mid = cfg.seq_len(steps // 2)
@@ -231,38 +257,98 @@ def cpu_leg(args, cfg):
         threads = 1
     rows = [(b, g) for b in range(cfg.batch) for g in range(cfg.num_kv_heads)]
     rng = np.random.default_rng(5)
-    order = [rows[i] for i in rng.permutation(len(rows))]
-    spent, done = 0.0, 0
-    used_rows = []
-    for (b, g) in order[:args.cpu_rows]:
+    order = [rows[i] for i in rng.permutation(len(rows))][:args.cpu_rows]
+    # inputs and prefill of the sampled rows, outside the timed steps
+    sample = []
+    for (b, g) in order:
         ri = W.row_inputs(cfg, b, g)
         row = O.OracleRow(W.stored_to_f64(ri.keys, cfg.dtype), W.stored_to_f64(ri.values, cfg.dtype),
                           ri.logits.astype(np.float64), cfg.dtype, 1.0 / math.sqrt(cfg.head_dim),
                           mode=cfg.mode, k=cfg.k, k_e=cfg.k_e, ordered=cfg.ordered, tau=cfg.tau)
-        row.reps(cfg.nb0)                       # prefill state, outside the timed step
+        row.reps(cfg.nb0)
         if cfg.k_e:
             row.eviction_scores(cfg.nb0)
-        used_rows.append((b, g))
-        for t in range(cfg.steps):
-            q = W.stored_to_f64(W.query_row(cfg, b, g, t), cfg.dtype)
-            f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode == "forecast" else None
-            t0 = time.perf_counter()
-            row.step(cfg.seq_len(t), q, f=f)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent >= args.cpu_seconds:
-                break
-        if spent >= args.cpu_seconds:
-            break
+        qs = [W.stored_to_f64(W.query_row(cfg, b, g, t), cfg.dtype) for t in range(cfg.steps)]
+        f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode == "forecast" else None
+        sample.append((row, qs, f))
+    # the workload's decode steps on the sampled rows, repeated until the
+    # budget is spent (a repeated step does the same work: no block fills)
+    spent, done, passes = 0.0, 0, 0
+    while spent < args.cpu_seconds:
+        for row, qs, f in sample:
+            for t in range(cfg.steps):
+                t0 = time.perf_counter()
+                row.step(cfg.seq_len(t), qs[t], f=f)
+                spent += time.perf_counter() - t0
+                done += 1
+        passes += 1
     per_row_step = spent / done
     step_s = per_row_step * cfg.rows
     return {"value": cfg.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} row-steps over {len(used_rows)} of {cfg.rows} rows "
-                      f"(float64 NumPy, one row at a time), {spent:.1f}s; scaled to all rows"}
+            "sample": f"{done} row-steps ({passes} passes over the {cfg.steps} decode steps of "
+                      f"{len(sample)} of {cfg.rows} rows; float64 NumPy, one row at a time), "
+                      f"{spent:.1f}s timed; scaled to all rows"}
+
+
+KERNEL_SYMBOLS = {"step": "gang_kernel", "select": "score_select_kernel", "decode": "decode_kernel"}
+CALIBRATION_SYMBOL = "MulFunctor"
+
+
+def counter_per_dispatch(path: str, counter: str):
+    """{kernel name: [value per dispatch]} of one counter from a rocprofv3
+    counter-collection CSV (values summed over the rows of a dispatch)."""
+    import csv
+    per = {}
+    with open(path, newline="") as fh:
+        for rec in csv.DictReader(fh):
+            if rec.get("Counter_Name") != counter:
+                continue
+            key = (rec["Kernel_Name"], rec.get("Dispatch_Id") or rec.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(rec["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def traffic_mode(args) -> int:
+    fetch = counter_per_dispatch(args.traffic_from[0], "FETCH_SIZE")
+    write = counter_per_dispatch(args.traffic_from[1], "WRITE_SIZE")
+    known = args.calibration_mib * (1 << 20)
+
+    def pick(table, sym):
+        vals = [v for name, vs in table.items() if sym in name for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named *{sym}* in the counter file")
+        return sum(vals) / len(vals)
+
+    f_cal, w_cal = pick(fetch, CALIBRATION_SYMBOL) * 1024, pick(write, CALIBRATION_SYMBOL) * 1024
+    kernel = "step" if args.path == "fused" else "select"
+    kernels = [kernel] if args.path == "fused" else ["select", "decode"]
+    for kern in kernels:
+        sym = KERNEL_SYMBOLS[kern]
+        f_k, w_k = pick(fetch, sym) * 1024, pick(write, sym) * 1024
+        rec = {
+            "kernel": kern, "symbol": sym, "workload": args.workload,
+            "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
+            "calibration": {"kernel": CALIBRATION_SYMBOL, "bytes_each_way": known,
+                            "fetch_bytes_raw": f_cal, "write_bytes_raw": w_cal,
+                            "fetch_scale": known / f_cal, "write_scale": known / w_cal},
+            "bytes_per_launch": f_k * known / f_cal + w_k * known / w_cal,
+            "source_hash": source_hash(KERNEL_SOURCES[kern]),
+            "files": list(args.traffic_from),
+        }
+        path = os.path.join(ROOT, "profiles", f"{kern}_{args.workload}_traffic.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+    return 0
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        return traffic_mode(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this path shards by rows with no exchange, see the design notes)", file=sys.stderr)

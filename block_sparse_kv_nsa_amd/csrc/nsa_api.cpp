@@ -414,7 +414,7 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
   L.scale = scale_of(shape);
   L.gang_override = env_int("NSA_STEP_GANG");
   const int pct = env_int("NSA_STEP_EFIRST");
-  L.e_first_pct = pct > 0 ? (pct > 100 ? 100 : pct) : 50;
+  L.e_first_pct = pct > 0 ? (pct > 100 ? 100 : pct) : 25;
   L.lay = lay;
   if (env_trace())
     std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d mloc_max=%d gang=%d efirst=%d%%\n", lay.rows,

@@ -74,7 +74,7 @@ __device__ void wg_acc_store(const WgAcc<D, G>& acc, __amdgpu_buffer_rsrc_t mlr,
   }
 }
 
-template <typename T, int D, int G, bool PRE, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                             ItemFn item, AttendSmem<T, D, G>& sm);
 
@@ -85,7 +85,7 @@ template <typename T, int D, int G, bool PRE, typename ItemFn>
 __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                              ItemFn item, AttendSmem<T, D, G>& sm, __amdgpu_buffer_rsrc_t mlr,
                              __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
-  attend_core<T, D, G, PRE>(qrow, kp, vp, qscale, i0, i1, item, sm);
+  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1)>(qrow, kp, vp, qscale, i0, i1, item, sm);
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
     float M = sm.wm[0][h];
@@ -111,13 +111,14 @@ __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qsca
 }
 
 // Accumulate items [i0, i1) into the workgroup's running partial `acc`
-// (shared memory).  Ends with a barrier.
-template <typename T, int D, int G, bool PRE, typename ItemFn>
+// (shared memory).  BUF: slabs in flight per workgroup (1 or 2).  Ends with a
+// barrier.
+template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
 __device__ void attend_items_merge(const T* qrow, const T* kp, const T* vp, float qscale, int i0,
                                    int i1, ItemFn item, AttendSmem<T, D, G>& sm,
                                    WgAcc<D, G>& acc) {
   if (i0 >= i1) return;  // uniform
-  attend_core<T, D, G, PRE>(qrow, kp, vp, qscale, i0, i1, item, sm);
+  attend_core<T, D, G, PRE, BUF>(qrow, kp, vp, qscale, i0, i1, item, sm);
   float nm = -INFINITY, nl = 0.f;
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
@@ -162,7 +163,7 @@ __device__ void attend_items_merge(const T* qrow, const T* kp, const T* vp, floa
   __syncthreads();
 }
 
-template <typename T, int D, int G, bool PRE, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                             ItemFn item, AttendSmem<T, D, G>& sm) {
   using Q = Quad<T, D>;
@@ -279,7 +280,7 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     }
   };
 
-  if constexpr (G < 8) {
+  if constexpr (BUF >= 2) {
     // next slab's loads in flight while the current one is consumed
     uint4 ka[NLD], va[NLV], kb[NLD], vb[NLV];
     Item ia, ib;
@@ -293,7 +294,8 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
       }
     }
   } else {
-    // 8 heads: the query slices and accumulators leave no room for a second slab
+    // one slab at a time (8 heads: the query slices and accumulators leave
+    // no room for a second one)
     for (int it = i0; it < i1; ++it) {
       uint4 ka[NLD], va[NLV];
       Item ia;

@@ -132,243 +132,166 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 // ---------------------------------------------------------------------------
-// single-wave top-m selection over keys in LDS (no workgroup barriers)
+// threshold of the m largest keys by bisection (one wave)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+// The m-th largest of the nonzero keys[0..n) (n <= 64 * KPL; a zero key marks
+// an excluded entry), found bit by bit from the top: T grows while at least
+// m keys are >= T.  Each probe costs KPL ballots and scalar adds, all keys
+// stay in registers.  *take_eq receives how many of the entries equal to T
+// belong to the m largest (the rest of the m are > T).  Requires
+// 1 <= m <= number of nonzero keys; called by all 64 lanes.
+template <int KPL>
+__device__ __attribute__((always_inline)) uint32_t wave_kth_key(const uint32_t* keys, int n, int m, int* take_eq) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t k[KPL];
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, kWave);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  for (int j = 0; j < KPL; ++j) {
+    const int i = j * kWave + lane;
+    k[j] = i < n ? keys[i] : 0u;
+  }
+  auto count_ge = [&](uint32_t x) {  // x >= 1, so zero keys never count
+    int c = 0;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v &= (uint32_t)__shfl_xor((int)v, off, kWave);
-  return v;
+    for (int j = 0; j < KPL; ++j) c += __popcll(__ballot(k[j] >= x));
+    return c;
+  };
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (count_ge(c) >= m) T = c;
+  }
+  *take_eq = m - (T == ~0u ? 0 : count_ge(T + 1u));
+  return T;
 }
 
-// Called by all 64 lanes of one wave.  Finds the m-th largest of keys[0..n)
-// (1 <= m <= number of nonzero keys; a zero key marks an excluded entry and
-// is never chosen) with an MSD radix select whose first digit starts at the
-// highest bit where the keys differ (scores of one row share their top bits,
-// so a fixed first digit would send every key to one histogram bin), then
-// visits the chosen entries in index order -- all keys above the threshold
-// and the lowest-index entries equal to it -- calling emit(i, rank).
-// Keys are taken kTile per lane at a time into registers (index
-// tile*64*kTile + j*64 + lane), so LDS latency is paid once per tile and the
-// histogram atomics issue back to back.  hist: 256 words of LDS for this wave.
-template <typename Emit>
-__device__ void wave_top_m(const uint32_t* keys, int n, int m, uint32_t* hist, Emit emit) {
-  constexpr int kTile = 32;
-  constexpr int kSpan = kTile * kWave;
+// The same threshold for any n, counting from shared memory at every probe
+// (32 probes of n / 64 ballots each).
+__device__ __attribute__((always_inline)) uint32_t wave_kth_key_lds(const uint32_t* keys, int n,
+                                                                    int m, int* take_eq) {
   const int lane = threadIdx.x & (kWave - 1);
-  auto load_tile = [&](int t0, uint32_t (&kr)[kTile]) {
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const int i = t0 + j * kWave + lane;
-      kr[j] = i < n ? keys[i] : 0u;
+  auto count_ge = [&](uint32_t x) {
+    int c = 0;
+    for (int base = 0; base < n; base += kWave) {
+      const int i = base + lane;
+      c += __popcll(__ballot(i < n && keys[i] >= x));
     }
+    return c;
   };
-  uint32_t kor = 0u, kand = ~0u;
-  for (int t0 = 0; t0 < n; t0 += kSpan) {
-    uint32_t kr[kTile];
-    load_tile(t0, kr);
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      if (kr[j] != 0u) {  // 0 marks an excluded entry
-        kor |= kr[j];
-        kand &= kr[j];
-      }
-    }
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (count_ge(c) >= m) T = c;
   }
-  kor = wave_or(kor);
-  kand = wave_and(kand);
-  uint32_t T, prefix = 0u, mask = 0u;
-  int take_eq = m;
-  const uint32_t diff = kor ^ kand;
-  if (diff == 0u) {
-    T = kor;  // all candidate keys equal: the lowest m indices
-  } else {
-    int hi = 31 - __builtin_clz(diff);
-    mask = hi == 31 ? 0u : ~((2u << hi) - 1u);
-    prefix = kand & mask;
-    int remaining = m;
-    while (true) {
-      const int lo = hi >= 7 ? hi - 7 : 0;
-      const uint32_t dmask = (2u << (hi - lo)) - 1u;
-#pragma unroll
-      for (int i = 0; i < 256 / kWave; ++i) hist[i * kWave + lane] = 0u;
-      __builtin_amdgcn_wave_barrier();
-      for (int t0 = 0; t0 < n; t0 += kSpan) {
-        uint32_t kr[kTile];
-        load_tile(t0, kr);
-#pragma unroll
-        for (int j = 0; j < kTile; ++j)
-          if (kr[j] != 0u && (kr[j] & mask) == prefix) atomicAdd(&hist[(kr[j] >> lo) & dmask], 1u);
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
-      // lane l owns digits 4l..4l+3: entries with a larger digit, then pick
-      const uint4 c = *reinterpret_cast<const uint4*>(hist + 4 * lane);
-      const int mine = (int)(c.x + c.y + c.z + c.w);
-      int x = mine;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_down(x, off, kWave);
-        if (lane + off < kWave) x += t;
-      }
-      int above = x - mine;
-      int found_digit = -1, found_above = 0;
-      const int cs[4] = {(int)c.x, (int)c.y, (int)c.z, (int)c.w};
-#pragma unroll
-      for (int qd = 3; qd >= 0; --qd) {
-        if (above < remaining && remaining <= above + cs[qd]) {
-          found_digit = 4 * lane + qd;
-          found_above = above;
-        }
-        above += cs[qd];
-      }
-      const uint64_t who = __ballot(found_digit >= 0);
-      const int src = __builtin_ctzll(who);
-      const int digit = __shfl(found_digit, src, kWave);
-      const int abv = __shfl(found_above, src, kWave);
-      prefix |= (uint32_t)digit << lo;
-      mask |= dmask << lo;
-      remaining -= abv;
-      if (lo == 0) break;
-      hi = lo - 1;
-    }
-    T = prefix;
-    take_eq = remaining;
-  }
-  // emit in index order
-  int eq_seen = 0, taken = 0;
+  *take_eq = m - (T == ~0u ? 0 : count_ge(T + 1u));
+  return T;
+}
+
+// The m-th largest key with KPL chosen from n (n <= 1024).
+__device__ __forceinline__ uint32_t wave_kth_key_n(const uint32_t* keys, int n, int m,
+                                                    int* take_eq) {
+  if (n <= 64) return wave_kth_key<1>(keys, n, m, take_eq);
+  if (n <= 128) return wave_kth_key<2>(keys, n, m, take_eq);
+  if (n <= 256) return wave_kth_key<4>(keys, n, m, take_eq);
+  if (n <= 512) return wave_kth_key<8>(keys, n, m, take_eq);
+  return wave_kth_key<16>(keys, n, m, take_eq);
+}
+
+// One wave: visit, in index order, the entries of keys[0..n) above T and the
+// first take_eq entries equal to T, calling emit(i, rank).
+template <typename Emit>
+__device__ __attribute__((always_inline)) void wave_emit_top(const uint32_t* keys, int n, uint32_t T, int take_eq, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int t0 = 0; t0 < n; t0 += kSpan) {
-    uint32_t kr[kTile];
-    load_tile(t0, kr);
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const bool gt = kr[j] > T;
-      const bool eq = kr[j] == T && kr[j] != 0u;
-      const uint64_t eqm = __ballot(eq);
-      const int eq_rank = eq_seen + __popcll(eqm & below);
-      const bool take = gt || (eq && eq_rank < take_eq);
-      const uint64_t tk = __ballot(take);
-      if (take) emit(t0 + j * kWave + lane, taken + __popcll(tk & below));
-      eq_seen += __popcll(eqm);
-      taken += __popcll(tk);
-    }
+  int eq_seen = 0, taken = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    const uint32_t key = i < n ? keys[i] : 0u;
+    const bool eq = key == T && key != 0u;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = (key > T) || (eq && eq_seen + __popcll(eqm & below) < take_eq);
+    const uint64_t tk = __ballot(take);
+    if (take) emit(i, taken + __popcll(tk & below));
+    eq_seen += __popcll(eqm);
+    taken += __popcll(tk);
   }
 }
 
 // ---------------------------------------------------------------------------
 // workgroup top-m
 // ---------------------------------------------------------------------------
-// The same selection as wave_top_m (the m largest keys, ties to the lower
-// index, emitted in index order with emit(i, rank)), computed by all kThreads
-// threads, without atomics on shared histogram bins.  Each entry is packed as
-// (key << 32) | ~index, so packed values are distinct and order by key, then
-// by lower index; the m-th largest packed value Tm is the exact threshold.
-//  1. Every thread takes the maximum of its entries i = t, t+256, ...; the
-//     m-th largest of these 256 maxima, T0, is <= Tm (m distinct entries are
-//     >= T0), and only the threads whose maximum is >= T0 -- at most m of
-//     them -- hold entries >= T0, so there are at most m * ceil(n/256)
-//     candidates.
-//  2. Candidates (packed >= T0) are gathered and Tm is found by counting,
-//     for each candidate, the candidates above it.
-//  3. One wave visits the entries in index order and emits packed >= Tm.
-// More than kTopCap candidates (large m, or many entries per thread) falls
-// back to wave_top_m.  Called by all threads; ends with a barrier.
+// The m largest keys of keys[0..n) (1 <= m <= number of nonzero keys; a zero
+// key is excluded), ties to the lower index, visited in index order with
+// emit(i, rank); computed by all kThreads threads.
+//  1. Every thread takes the maximum key of its entries i = t, t+256, ...;
+//     the m-th largest of these 256 maxima, T0, is <= the m-th largest key
+//     overall (m entries are >= T0), so every entry of the m largest is >= T0.
+//  2. Entries >= T0 are gathered (they sit in the threads whose maximum is
+//     >= T0: about m threads, so about m * ceil(n/256) entries).
+//  3. One wave finds the exact threshold among them by bisection and visits
+//     the entries in index order.
+// Up to kTopCap entries skip steps 1-2.  With more than kTopCap gathered
+// entries (many equal keys) step 3 counts over all entries instead.  Called
+// by all threads; ends with a barrier.
 constexpr int kTopCap = 1024;
 
 struct TopSmem {
-  uint64_t tmax[kThreads];
-  uint64_t cand[kTopCap];
-  uint64_t t0, tm;
+  uint32_t tmax[kThreads];
+  uint32_t cand[kTopCap];
+  uint32_t t0;
   int count;
-  uint32_t hist[256];  // for the fallback
 };
 
-__device__ __forceinline__ uint64_t top_pack(uint32_t key, int i) {
-  return key != 0u ? ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)i) : 0ull;
-}
-
 template <typename Emit>
-__device__ void wg_top_m(const uint32_t* keys, int n, int m, TopSmem& ts, Emit emit) {
+__device__ __attribute__((always_inline)) void wg_top_m(const uint32_t* keys, int n, int m, TopSmem& ts, Emit emit) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
-  uint64_t mx = 0ull;
-  for (int i = t; i < n; i += kThreads) {
-    const uint64_t p = top_pack(keys[i], i);
-    mx = p > mx ? p : mx;
-  }
-  ts.tmax[t] = mx;
-  if (t == 0) {
-    ts.t0 = 1ull;  // fewer than m nonzero maxima: every entry is a candidate
-    ts.tm = ~0ull;
-    ts.count = 0;
-  }
-  __syncthreads();
-  if (mx != 0ull) {
-    // 16 maxima per batch, all loads issued before the compares
-    int above = 0;
-    for (int j0 = 0; j0 < kThreads; j0 += 16) {
-      uint64_t v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = ts.tmax[j0 + j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) above += v[j] > mx;
+  if (n <= kTopCap) {  // uniform: one wave bisects over all entries
+    if (wave == 0) {
+      int take_eq;
+      const uint32_t T = wave_kth_key_n(keys, n, m, &take_eq);
+      wave_emit_top(keys, n, T, take_eq, emit);
     }
-    if (above == m - 1) ts.t0 = mx;
+    __syncthreads();
+    return;
+  }
+  uint32_t mx = 0u;
+  for (int i = t; i < n; i += kThreads) mx = max(mx, keys[i]);
+  ts.tmax[t] = mx;
+  if (t == 0) ts.count = 0;
+  __syncthreads();
+  if (wave == 0) {
+    const int nz = __popcll(__ballot(ts.tmax[lane] != 0u)) +
+                   __popcll(__ballot(ts.tmax[64 + lane] != 0u)) +
+                   __popcll(__ballot(ts.tmax[128 + lane] != 0u)) +
+                   __popcll(__ballot(ts.tmax[192 + lane] != 0u));
+    int te;
+    // fewer than m threads hold a nonzero key: every nonzero entry is gathered
+    const uint32_t t0 = nz < m ? 1u : wave_kth_key<4>(ts.tmax, kThreads, m, &te);
+    if (lane == 0) ts.t0 = t0;
   }
   __syncthreads();
-  const uint64_t t0 = ts.t0;
+  const uint32_t t0 = ts.t0;
   const uint64_t below = (1ull << lane) - 1ull;
   for (int base = 0; base < n; base += kThreads) {
     const int i = base + t;
-    const uint64_t p = i < n ? top_pack(keys[i], i) : 0ull;
-    const bool c = p >= t0;
+    const uint32_t key = i < n ? keys[i] : 0u;
+    const bool c = key >= t0;
     const uint64_t bm = __ballot(c);
     int pos0 = 0;
     if (lane == 0 && bm != 0ull) pos0 = atomicAdd(&ts.count, __popcll(bm));
     pos0 = __shfl(pos0, 0, kWave);
     const int pos = pos0 + __popcll(bm & below);
-    if (c && pos < kTopCap) ts.cand[pos] = p;
+    if (c && pos < kTopCap) ts.cand[pos] = key;
   }
   __syncthreads();
   const int nc = ts.count;
-  if (nc > kTopCap) {
-    if (wave == 0) wave_top_m(keys, n, m, ts.hist, emit);
-    __syncthreads();
-    return;
-  }
-  // candidates past nc read as 0 (below every candidate)
-  const int nc16 = (nc + 15) & ~15;
-  for (int i = nc + t; i < nc16; i += kThreads) ts.cand[i] = 0ull;
-  __syncthreads();
-  for (int ci = t; ci < nc; ci += kThreads) {
-    const uint64_t mine = ts.cand[ci];
-    int above = 0;
-    for (int j0 = 0; j0 < nc16; j0 += 16) {
-      uint64_t v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = ts.cand[j0 + j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) above += v[j] > mine;
-    }
-    if (above == m - 1) ts.tm = mine;
-  }
-  __syncthreads();
   if (wave == 0) {
-    const uint64_t tm = ts.tm;
-    int taken = 0;
-    for (int base = 0; base < n; base += kWave) {
-      const int i = base + lane;
-      const bool take = i < n && top_pack(keys[i], i) >= tm;
-      const uint64_t bm = __ballot(take);
-      if (take) emit(i, taken + __popcll(bm & below));
-      taken += __popcll(bm);
-    }
+    int take_eq;
+    // more than kTopCap gathered entries (many equal keys): count over all
+    const uint32_t T = nc <= kTopCap ? wave_kth_key_n(ts.cand, nc, m, &take_eq)
+                                     : wave_kth_key_lds(keys, n, m, &take_eq);
+    wave_emit_top(keys, n, T, take_eq, emit);
   }
   __syncthreads();
 }

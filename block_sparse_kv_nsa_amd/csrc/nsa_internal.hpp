@@ -191,12 +191,22 @@ inline StepLayout step_layout(int B, int Hkv, int G, int D, int k, int k_e, int 
   return s;
 }
 
-// Dynamic shared memory of a member: the eviction set, then the larger of
-// the eviction update (keys of old set + new blocks, old set) and the
-// selection (all members' candidates, the query-aware list, block flags).
+constexpr int kTblMaxWords = 4096;  // longest table row kept in shared memory
+
+// Words of shared memory for the row's block table (full blocks and the tail
+// block, staged 64 entries at a time), or 0 when the row is longer than
+// kTblMaxWords and the table is read from global memory.
+inline int gang_tbl_words(const StepLayout& lay) {
+  const int w = (lay.nb_max + 1 + 63) / 64 * 64;
+  return w <= kTblMaxWords ? w : 0;
+}
+
+// Dynamic shared memory of a member: the eviction set, the table row, then the
+// larger of the eviction update (keys of old set + new blocks, old set) and
+// the selection (all members' candidates, the query-aware list, block flags).
 inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e, int C, int mloc = 0) {
   const int ml = mloc > 0 ? mloc : lay.mloc_max;
-  const size_t eids = (size_t)(k_e > 0 ? k_e : 1) * 4;
+  const size_t eids = (size_t)(k_e > 0 ? k_e : 1) * 4 + (size_t)gang_tbl_words(lay) * 4;
   const size_t upd = (size_t)(k_e + lay.nb_max) * 4 + (size_t)k_e * 4;
   const size_t sel = (size_t)C * ml * 8 + (size_t)k * 4 + round_up((size_t)lay.nb_max, 4);
   return round_up(eids + (upd > sel ? upd : sel), 16);

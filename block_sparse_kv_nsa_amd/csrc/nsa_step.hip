@@ -1,12 +1,15 @@
 // Fused decode step: eviction-set update, block scoring, selection and sparse
-// attention of one decode step in a single cooperative launch.
+// attention of one decode step in a single launch.
 //
 // The step is the same computation as nsa_select_blocks followed by
 // nsa_sparse_decode (NOSA technical summary, "Mecanismo de Doble Selección",
 // "Implementación Basada en Bloques"; SparDA technical summary, "Kompakter
 // Forecast-Indexer"); only the schedule differs.  Each row (sequence b, KV
-// head g) is handled by a gang of C workgroups, all resident at once (the
-// launch is cooperative).  Member c of the gang
+// head g) is handled by a gang of C workgroups that run at the same time: the
+// grid never exceeds the workgroups the device holds resident at once, so on
+// a device not shared with other streams every workgroup starts with the
+// launch.  (A cooperative launch would guarantee this but costs about 17 us
+// per launch on this part.)  Member c of the gang
 //   1. streams its contiguous share of the row's sub-block representatives
 //      and keeps the logits q.r in registers;
 //   2. publishes its softmax statistics (group-softmax mode);
@@ -38,6 +41,7 @@ namespace nsa {
 namespace {
 
 constexpr int kWaitMs = 200;  // longest a member waits for its gang
+constexpr int kGangBuf = 1;   // slabs in flight per member during attention
 
 struct GangArgs {
   const void* query;  // group-softmax: [B][Hq][D]; forecast: [B][Hkv][D]
@@ -60,6 +64,7 @@ struct GangArgs {
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
   int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg, mloc, mloc_max, e_first_pct;
+  int tbl_words;  // table row kept in shared memory (nb_max + 1 words), or 0
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
   uint32_t stats_bytes, cand_bytes, ml_bytes, acc_bytes;
@@ -140,13 +145,28 @@ struct Gang {
     const int h0 = GS >= 4 ? q * KEEP : q / DUP;
     const bool canon = (q % DUP) == 0;
     uint32_t* words = a.words + (int64_t)row * kGangWords;
-    int* eids = reinterpret_cast<int*>(dyn);             // k_e: the eviction set
-    uint32_t* scratch = dyn + (a.k_e > 0 ? a.k_e : 1);   // per-phase scratch
+    int* eids = reinterpret_cast<int*>(dyn);                   // k_e: the eviction set
+    int* tbl = eids + (a.k_e > 0 ? a.k_e : 1);                 // nb_max + 1: the table row
+    uint32_t* scratch = reinterpret_cast<uint32_t*>(tbl) + a.tbl_words;  // per-phase scratch
+    const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
     const T* kp = static_cast<const T*>(a.k_pool);
     const T* vp = static_cast<const T*>(a.v_pool);
 
     wg_acc_init(sm.acc);
+
+    // ---- the row's block table and eviction state, requested now and used
+    // after the streaming below (their latency overlaps it); the table goes
+    // straight to shared memory (64 entries per wave and instruction)
+    if (a.tbl_words > 0) {
+      // entries past the row's last block (the tail's, which exists only when
+      // the row is not full) are clamped into the row
+      const int last = min(nb, a.max_blocks - 1);
+      for (int base = wave * kWave; base <= last; base += kThreads)
+        __builtin_amdgcn_global_load_lds(trow + min(base + lane, last), tbl + base, 4, 0, 0);
+    }
+    const int seen_pre = a.k_e > 0 ? a.evict_seen[row] : 0;
+    const int ev_pre = (int)threadIdx.x < a.k_e ? a.evict_set[(int64_t)row * a.k_e + threadIdx.x] : 0;
 
     // ---- 1. logits of this member's representatives, in registers
     float lg[U][KEEP];
@@ -230,23 +250,28 @@ struct Gang {
       for (int kk = 0; kk < KEEP; ++kk) sm.lgs[u][kk][threadIdx.x] = lg[u][kk];
     }
 
+    __builtin_amdgcn_s_waitcnt(0);  // the table has landed
+    __syncthreads();
+
     // ---- 3. the eviction set: the k_e best of (old set U blocks that became
     // full since the last call) by eviction score, ties to the lower id
     int n_e = 0;
     if (a.k_e > 0) {
-      int seen = a.evict_seen[row];
+      int seen = seen_pre;
       if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
       const int nprev = min(a.k_e, seen);
       const int ncand = nprev + nb - seen;
       n_e = min(a.k_e, ncand);
+      auto old_id = [&](int i) {  // entry i of the old set, i < nprev
+        const int v = i < kThreads ? ev_pre : a.evict_set[(int64_t)row * a.k_e + i];
+        return min(max(v, 0), nb - 1);
+      };
       if (seen == nb) {
-        for (int i = threadIdx.x; i < n_e; i += kThreads)
-          eids[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+        for (int i = threadIdx.x; i < n_e; i += kThreads) eids[i] = old_id(i);
       } else {
         uint32_t* keys = scratch;                                       // ncand
         int* ev_old = reinterpret_cast<int*>(keys + a.k_e + a.nb_max);  // k_e
-        for (int i = threadIdx.x; i < nprev; i += kThreads)
-          ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+        for (int i = threadIdx.x; i < nprev; i += kThreads) ev_old[i] = old_id(i);
         __syncthreads();
         const float* Er = a.E + (int64_t)row * a.max_blocks;
         for (int i = threadIdx.x; i < ncand; i += kThreads) {
@@ -267,7 +292,7 @@ struct Gang {
     auto e_item = [&](int it) {
       const int idx = c + it * C;
       const int blk = idx < n_e ? eids[idx] : nb;
-      const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
+      const int64_t phys = a.tbl_words > 0 ? tbl[blk] : trow[blk];
       Item x;
       x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
       x.valid = idx < n_e ? kBlock : tail;
@@ -277,7 +302,7 @@ struct Gang {
     const int n_eitems = n_e + (tail > 0);
     const int e_mine = n_eitems > c ? (n_eitems - c + C - 1) / C : 0;
     const int e_first = (e_mine * a.e_first_pct + 99) / 100;
-    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att,
+    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att,
                                        sm.acc);
 
     // ---- 4. row normaliser from every member's statistics
@@ -339,43 +364,32 @@ struct Gang {
     }
     __syncthreads();
 
-    // a block's rank is the number of this member's blocks ahead of it
-    // (higher key, or equal key and lower id); slot r of the member's list
-    // gets the block of rank r, slots past its count an empty entry
+    // this member's best mc blocks (ties to the lower id) fill slots
+    // 0..mc-1 of its list in block order; the remaining slots get an empty
+    // entry
     const int m_row = max(0, min(a.k - n_e, nb - n_e));
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.cand, a.cand_bytes);
-    {
+    if (threadIdx.x < kWave) {
       const int64_t cbase = ((int64_t)row * kMaxGang + c) * a.mloc_max;
-      const int t = threadIdx.x;
-      const uint64_t mine = t < CBLK ? top_pack(sm.ckeys[t], t) : 0ull;
-      const int nz = __syncthreads_count(mine != 0ull);
+      int nz = 0;
+#pragma unroll
+      for (int j = 0; j < CBLK / kWave; ++j) nz += __popcll(__ballot(sm.ckeys[j * kWave + lane] != 0u));
       const int mc = min(min(m_row, nz), a.mloc);
-      if (mine != 0ull) {
-        // 16 keys per batch (four 16-byte reads) before the compares
-        int ahead = 0;
-        for (int j0 = 0; j0 < CBLK; j0 += 16) {
-          uint4 kv[4];
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) kv[v4] = *reinterpret_cast<const uint4*>(&sm.ckeys[j0 + 4 * v4]);
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            ahead += top_pack(kv[v4].x, j0 + 4 * v4) > mine;
-            ahead += top_pack(kv[v4].y, j0 + 4 * v4 + 1) > mine;
-            ahead += top_pack(kv[v4].z, j0 + 4 * v4 + 2) > mine;
-            ahead += top_pack(kv[v4].w, j0 + 4 * v4 + 3) > mine;
-          }
-        }
-        if (ahead < mc)
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[t], (uint32_t)(blk0 + t)}, cr,
-                                                (int)((cbase + ahead) * 8), 0, kSC1);
+      if (mc > 0) {
+        int take_eq;
+        const uint32_t thr = wave_kth_key<CBLK / kWave>(sm.ckeys, CBLK, mc, &take_eq);
+        wave_emit_top(sm.ckeys, CBLK, thr, take_eq, [&](int i, int pos) {
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[i], (uint32_t)(blk0 + i)}, cr,
+                                                (int)((cbase + pos) * 8), 0, kSC1);
+        });
       }
-      for (int i = mc + t; i < a.mloc; i += kThreads)
+      for (int i = mc + lane; i < a.mloc; i += kWave)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, cr, (int)((cbase + i) * 8), 0, kSC1);
     }
     gang_arrive(words + 1, C, &sm.s_int[1]);
 
     // ---- the rest of this member's eviction-set share
-    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att,
+    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att,
                                        sm.acc);
 
     // ---- 6. the row's query-aware set from every member's candidates
@@ -432,7 +446,7 @@ struct Gang {
     // ---- attention over this member's share of the query-aware set
     auto q_item = [&](int it) {
       const int blk = qsel[c + it * C];
-      const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
+      const int64_t phys = a.tbl_words > 0 ? tbl[blk] : trow[blk];
       Item x;
       x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
       x.valid = kBlock;
@@ -440,7 +454,7 @@ struct Gang {
       return x;
     };
     const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
-    attend_items_merge<T, D, G, false>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
+    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
                                        sm.acc);
 
     // ---- 7. partials; the last member merges them into the output
@@ -520,6 +534,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.per_wg = plan.per_wg;
   a.mloc = plan.mloc;
   a.mloc_max = lay.mloc_max;
+  a.tbl_words = gang_tbl_words(lay);
   a.e_first_pct = L.e_first_pct;
   a.qscale_sel = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;
   a.qscale_att = L.scale * 1.4426950408889634f;
@@ -528,9 +543,8 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.cand_bytes = (uint32_t)(lay.off_ml - lay.off_cand);
   a.ml_bytes = (uint32_t)(lay.off_acc - lay.off_ml);
   a.acc_bytes = (uint32_t)(lay.bytes - lay.off_acc);
-  void* args[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(plan.gangs * plan.C), dim3(kThreads), args,
-                                    (unsigned)plan.dyn_lds, stream);
+  gang_kernel<T, D, G, FORECAST><<<plan.gangs * plan.C, kThreads, plan.dyn_lds, stream>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G>

@@ -224,20 +224,24 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  * (ascending mode: params->ordered must be 0).  Same inputs, state and
  * outputs as the two calls (selected / num_selected as nsa_select_blocks
  * writes them; out as nsa_sparse_decode writes it).  The computation is
- * identical; the schedule differs: the eviction set depends on the eviction
- * scores only (NOSA summary, "Mecanismo de Doble Seleccion"), so attention
- * over it proceeds while the query-aware part is still being scored and
- * selected, and one persistent grid runs every stage.
+ * identical; the schedule differs: each row is handled by a gang of
+ * workgroups that score their shares of the row's blocks, exchange softmax
+ * statistics and candidates, and attend shares of the selected blocks; the
+ * eviction set depends on the eviction scores only (NOSA summary, "Mecanismo
+ * de Doble Seleccion"), so attention over it proceeds while the query-aware
+ * part is still being scored and selected.
  *
  *   query  selector input: [B][Hq][D] (group softmax) or [B][Hkv][D]
  *          (forecast); q: attention queries [B][Hq][D] (may equal query)
- * The workspace follows the select workspace's counter rule (zero before
- * its first use; left zero by every completed call), except for 32-bit word
- * 2 (bytes 8-11): an error word, sticky, set nonzero when a wait between
- * stages expired (results of such a call are undefined).  The sequences'
- * scoring work must fit the grid at once: a call whose longest sequence
- * needs more 8192-token chunks than the device holds workgroups of this
- * kernel fails with NSA_ERR_HIP.
+ * The grid is sized to the workgroups the device holds at once and the
+ * members of a gang wait for one another, so the call expects the device's
+ * compute units to itself while it runs (work on other streams can stall a
+ * gang).  Every wait is bounded: the workspace follows the select
+ * workspace's counter rule (zero before its first use; left zero by every
+ * completed call), except for 32-bit word 2 (bytes 8-11), an error word,
+ * sticky, set nonzero when a wait expired (results of such a call are
+ * undefined; the two-call path gives them without the assumption).
+ * max_seq_len is limited to 524288 tokens (NSA_ERR_UNSUPPORTED above).
  * ------------------------------------------------------------------------ */
 nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
                                            int32_t max_seq_len, size_t* bytes);

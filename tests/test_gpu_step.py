@@ -119,6 +119,30 @@ def test_step_ragged_batch_edges(k, k_e):
             H.check_step(cfg, res, orow, b, g, 0, seq_len=int(lens[b]))
 
 
+def test_step_rows_filled_to_capacity():
+    """Sequences whose every block slot is full (no tail block): the table
+    row is read up to its last entry and no further."""
+    cfg = W.Config("full-rows", 51, batch=3, context=64 * 24 - 1, num_q_heads=8, num_kv_heads=2,
+                   head_dim=128, dtype="bf16", mode="group_softmax", k=8, k_e=4, steps=1)
+    cap = 64 * cfg.max_blocks
+    assert cap == cfg.total_tokens
+    lens = np.array([cap, cap - 64, 64 * 7], dtype=np.int32)
+    H.log(f"[case] fused, rows filled to capacity seq_lens {lens.tolist()}")
+    batch = W.build_batch(cfg)
+    layer = H.make_layer(cfg, batch)
+    first = torch.zeros(cfg.batch, dtype=torch.int32, device="cuda")
+    num = torch.from_numpy(lens // 64).to("cuda")
+    layer.update_reps(first, num, int((lens // 64).max()))
+    layer.seq_lens.copy_(torch.from_numpy(lens))
+    layer.step(H.device_query(cfg, 0), H.device_q(cfg, 0), int(lens.max()))
+    assert H.step_error_word(layer) == 0
+    res = H.fetch(layer)
+    for b in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            orow = H.oracle_row(cfg, b, g)
+            H.check_step(cfg, res, orow, b, g, 0, seq_len=int(lens[b]))
+
+
 def _two_layers(cfg):
     batch = W.build_batch(cfg)
     a, b = H.make_layer(cfg, batch), H.make_layer(cfg, batch)
