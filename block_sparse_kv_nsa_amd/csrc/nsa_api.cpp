@@ -413,8 +413,10 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
   L.k_e = params->k_e;
   L.scale = scale_of(shape);
   L.gang_override = env_int("NSA_STEP_GANG");
-  const int pct = env_int("NSA_STEP_EFIRST");
-  L.e_first_pct = pct > 0 ? (pct > 100 ? 100 : pct) : 25;
+  L.streamer_override = env_int("NSA_STEP_STREAMERS");
+  const char* efirst = std::getenv("NSA_STEP_EFIRST");
+  const int pct = efirst ? std::atoi(efirst) : 25;
+  L.e_first_pct = pct < 0 ? 0 : (pct > 100 ? 100 : pct);
   L.lay = lay;
   if (env_trace())
     std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d mloc_max=%d gang=%d efirst=%d%%\n", lay.rows,

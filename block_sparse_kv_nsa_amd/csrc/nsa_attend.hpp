@@ -37,8 +37,40 @@ struct Item {
   const float* logits;   // precomputed logits [G][64] (early-stop pass 2), else null
 };
 
+// One 64-token slab of K and V (this lane's pieces of it) with its item.
+template <typename T, int D>
+struct Slab {
+  uint4 k[Quad<T, D>::NLD];
+  uint4 v[VGeo<T, D>::NLV];
+  Item it;
+};
+
+// Issue the loads of item itm into s, in the layouts attend_core consumes.
+template <typename T, int D, bool PRE>
+__device__ __forceinline__ void slab_issue(Slab<T, D>& s, const Item& itm, const T* kp,
+                                           const T* vp) {
+  using Q = Quad<T, D>;
+  using V = VGeo<T, D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int q = lane & 3, r = lane >> 2;
+  const int sl = lane % V::LPR, grp = lane / V::LPR;
+  const int tk = wave * kSub + r;
+  s.it = itm;
+  if constexpr (!PRE) {
+#pragma unroll
+    for (int ld = 0; ld < Q::NLD; ++ld)
+      s.k[ld] = load16_stream(kp + itm.base + (int64_t)tk * D + Q::elem(ld, q));
+  }
+#pragma unroll
+  for (int u = 0; u < V::NLV; ++u)
+    s.v[u] = load16_stream(vp + itm.base + (int64_t)(wave * kSub + u * V::TPL + grp) * D +
+                           sl * V::EPL);
+}
+
 template <typename T, int D, int G>
 struct AttendSmem {
+  T qlds[G][D] __attribute__((aligned(16)));  // the queries, when read per slab
   float p_lds[kWaves][kSub][G];
   float wm[kWaves][G], wl[kWaves][G];
   float wacc[kWaves][G][D];
@@ -74,9 +106,9 @@ __device__ void wg_acc_store(const WgAcc<D, G>& acc, __amdgpu_buffer_rsrc_t mlr,
   }
 }
 
-template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
-                            ItemFn item, AttendSmem<T, D, G>& sm);
+                            ItemFn item, AttendSmem<T, D, G>& sm, const Slab<T, D>* first);
 
 // Accumulate items [i0, i1) (item(it) -> Item) and store the workgroup's
 // (m, l) and acc[D] per head at partial index pidx with agent-scope stores.
@@ -85,7 +117,8 @@ template <typename T, int D, int G, bool PRE, typename ItemFn>
 __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                              ItemFn item, AttendSmem<T, D, G>& sm, __amdgpu_buffer_rsrc_t mlr,
                              __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
-  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1)>(qrow, kp, vp, qscale, i0, i1, item, sm);
+  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1), false, false>(qrow, kp, vp, qscale, i0, i1, item, sm,
+                                                          nullptr);
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
     float M = sm.wm[0][h];
@@ -111,14 +144,18 @@ __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qsca
 }
 
 // Accumulate items [i0, i1) into the workgroup's running partial `acc`
-// (shared memory).  BUF: slabs in flight per workgroup (1 or 2).  Ends with a
-// barrier.
-template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
+// (shared memory).  BUF: slabs in flight per workgroup (1 or 2); QL: read the
+// query slices from sm.qlds (filled by the caller, qrow unused) at every slab
+// instead of holding them in registers (frees G * D / 8 registers per lane
+// for bf16 at D = 128, room for the second slab).  Ends with a barrier.
+// PF: the first item's slab was issued by the caller (slab_issue) into
+// *first, so its loads overlapped the caller's work.
+template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF = false, typename ItemFn>
 __device__ void attend_items_merge(const T* qrow, const T* kp, const T* vp, float qscale, int i0,
                                    int i1, ItemFn item, AttendSmem<T, D, G>& sm,
-                                   WgAcc<D, G>& acc) {
+                                   WgAcc<D, G>& acc, const Slab<T, D>* first = nullptr) {
   if (i0 >= i1) return;  // uniform
-  attend_core<T, D, G, PRE, BUF>(qrow, kp, vp, qscale, i0, i1, item, sm);
+  attend_core<T, D, G, PRE, BUF, QL, PF>(qrow, kp, vp, qscale, i0, i1, item, sm, first);
   float nm = -INFINITY, nl = 0.f;
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
@@ -163,9 +200,9 @@ __device__ void attend_items_merge(const T* qrow, const T* kp, const T* vp, floa
   __syncthreads();
 }
 
-template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
-                            ItemFn item, AttendSmem<T, D, G>& sm) {
+                            ItemFn item, AttendSmem<T, D, G>& sm, const Slab<T, D>* first) {
   using Q = Quad<T, D>;
   using V = VGeo<T, D>;
   constexpr int NLD = Q::NLD, EPL = V::EPL, LPR = V::LPR, TPL = V::TPL, NLV = V::NLV;
@@ -180,8 +217,8 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
   const bool canon = (q % DUP) == 0;
   const int tk = wave * kSub + r;
 
-  QSlice<T, D> qs[G];
-  if constexpr (!PRE) {
+  QSlice<T, D> qs[QL ? 1 : G];
+  if constexpr (!PRE && !QL) {
 #pragma unroll
     for (int h = 0; h < G; ++h) qs[h].load(qrow + h * D, q);
   }
@@ -198,6 +235,14 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
   for (int kk = 0; kk < KEEP; ++kk) mref[kk] = -INFINITY;
 
   auto issue = [&](int it, uint4 (&kx)[NLD], uint4 (&vx)[NLV], Item& itm) {
+    if (PF && it == i0) {  // issued by the caller
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) kx[ld] = first->k[ld];
+#pragma unroll
+      for (int u = 0; u < NLV; ++u) vx[u] = first->v[u];
+      itm = first->it;
+      return;
+    }
     itm = item(it);
     if constexpr (!PRE) {
 #pragma unroll
@@ -213,8 +258,19 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     float lg[KEEP];
     if constexpr (!PRE) {
       float v[G];
+      if constexpr (QL) {
+        // one head's slice at a time; the empty asm keeps the loads in the
+        // loop (they would otherwise be hoisted back into registers)
 #pragma unroll
-      for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
+        for (int h = 0; h < G; ++h) {
+          asm volatile("" ::: "memory");
+          qs[0].load(&sm.qlds[h][0], q);
+          v[h] = qs[0].dot(kx);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
+      }
       quad_reduce<2, G>(v, q);
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) lg[kk] = v[kk] * qscale;
@@ -330,7 +386,7 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
 }
 
 // Merge partials [p0, p0 + nparts) (agent-scope loads) into out[G][D]:
-// 4 channels per thread, partials 4 at a time with their loads in flight
+// 4 channels per thread, partials 16 at a time with their loads in flight
 // together, merged with a running maximum.
 template <typename T, int D, int G>
 __device__ void combine_partials(int64_t p0, int nparts, __amdgpu_buffer_rsrc_t mlr,
@@ -339,7 +395,7 @@ __device__ void combine_partials(int64_t p0, int nparts, __amdgpu_buffer_rsrc_t 
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kB = 4;
+    constexpr int kB = 16;
     for (int s0 = 0; s0 < nparts; s0 += kB) {
       f32x2 ml[kB];
       f32x4 ac[kB];

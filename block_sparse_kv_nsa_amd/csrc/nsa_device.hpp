@@ -135,9 +135,9 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 // threshold of the m largest keys by bisection (one wave)
 // ---------------------------------------------------------------------------
 // The m-th largest of the nonzero keys[0..n) (n <= 64 * KPL; a zero key marks
-// an excluded entry), found bit by bit from the top: T grows while at least
-// m keys are >= T.  Each probe costs KPL ballots and scalar adds, all keys
-// stay in registers.  *take_eq receives how many of the entries equal to T
+// an excluded entry), found from the top two bits at a time: T grows while at
+// least m keys are >= T.  Each probe costs 3 KPL ballots and scalar adds, all
+// keys stay in registers.  *take_eq receives how many of the entries equal to T
 // belong to the m largest (the rest of the m are > T).  Requires
 // 1 <= m <= number of nonzero keys; called by all 64 lanes.
 template <int KPL>
@@ -155,10 +155,12 @@ __device__ __attribute__((always_inline)) uint32_t wave_kth_key(const uint32_t* 
     for (int j = 0; j < KPL; ++j) c += __popcll(__ballot(k[j] >= x));
     return c;
   };
+  // two bits per probe: the three candidates' counts are independent
   uint32_t T = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = T | (1u << bit);
-    if (count_ge(c) >= m) T = c;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+    const int n1 = count_ge(c1), n2 = count_ge(c2), n3 = count_ge(c3);
+    T = n3 >= m ? c3 : (n2 >= m ? c2 : (n1 >= m ? c1 : T));
   }
   *take_eq = m - (T == ~0u ? 0 : count_ge(T + 1u));
   return T;

@@ -167,7 +167,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 enum : int { kErr = 2, kCtrlWords = 4 };
 constexpr int kGangWords = 3;    // per row: statistics, candidates, partials
 constexpr int kMaxGang = 64;     // most workgroups per row
-constexpr int kGangReps = 512;   // most representatives a member scores (in registers)
+constexpr int kGangReps = 512;   // most representatives a streamer scores (in registers)
 
 struct StepLayout {
   int rows, G, D, nb_max, mloc_max;
@@ -213,25 +213,32 @@ inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e, int C, int mlo
 }
 
 struct GangPlan {
-  int C, gangs, per_wg, mloc;
+  int C, S, gangs, per_wg, mloc;
   size_t dyn_lds;
 };
 
-// Gang size: enough members to hold the longest row's representatives in
-// registers, and as many as the resident workgroups allow across the rows (at
-// most kMaxGang).  Rows beyond the resident gangs are taken in turn.
+// Gang size C: as many members as the resident workgroups allow across the
+// rows (at most kMaxGang), and at least enough streamers to hold the longest
+// row's representatives in registers.  Streamers S: every member by default;
+// with s_override < C the other C - S members attend the eviction set while
+// the streamers score (this lengthens the scoring path, which is the step's
+// critical path, more than it saves at the measured shapes).  Rows beyond the
+// resident gangs are taken in turn.
 inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int c_override,
-                      GangPlan* p) {
+                      int s_override, GangPlan* p) {
   const int nsub = 4 * lay.nb_max;
-  const int c_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
+  const int s_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
   const int c_cap = capacity < kMaxGang ? capacity : kMaxGang;
-  if (c_min > c_cap) return false;
+  if (s_min > c_cap) return false;
   int C = c_override > 0 ? c_override : capacity / (lay.rows > 0 ? lay.rows : 1);
-  C = C < c_min ? c_min : (C > c_cap ? c_cap : C);
+  C = C < s_min ? s_min : (C > c_cap ? c_cap : C);
+  int S = s_override > 0 ? s_override : C;
+  S = S < s_min ? s_min : (S > C ? C : S);
   p->C = C;
+  p->S = S;
   p->gangs = capacity / C < lay.rows ? capacity / C : lay.rows;
   if (p->gangs < 1) return false;
-  const int per = nsub > 0 ? (nsub + C - 1) / C : 4;
+  const int per = nsub > 0 ? (nsub + S - 1) / S : 4;
   p->per_wg = (int)round_up((size_t)per, 4);
   const int blocks = p->per_wg / 4;
   p->mloc = k - k_e < blocks ? (k - k_e > 0 ? k - k_e : 1) : blocks;
@@ -257,7 +264,8 @@ struct StepLaunch {
   void* workspace;
   int B, Hkv, max_blocks, k, k_e;
   float scale;
-  int gang_override;  // 0: from capacity
+  int gang_override;      // 0: from capacity
+  int streamer_override;  // 0: from the byte shares
   int e_first_pct;    // share of the eviction-set attention done before the normaliser wait
   StepLayout lay;
 };

@@ -41,7 +41,8 @@ namespace nsa {
 namespace {
 
 constexpr int kWaitMs = 200;  // longest a member waits for its gang
-constexpr int kGangBuf = 1;   // slabs in flight per member during attention
+constexpr int kGangBuf = 2;      // slabs in flight per member during attention
+constexpr bool kGangQLds = true;  // query slices read from shared memory per slab
 
 struct GangArgs {
   const void* query;  // group-softmax: [B][Hq][D]; forecast: [B][Hkv][D]
@@ -63,7 +64,7 @@ struct GangArgs {
   uint32_t* cand;    // [rows][kMaxGang][mloc_max] (key, block)
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
-  int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg, mloc, mloc_max, e_first_pct;
+  int rows, Hkv, max_blocks, nb_max, k, k_e, C, S, gangs, per_wg, mloc, mloc_max, e_first_pct;
   int tbl_words;  // table row kept in shared memory (nb_max + 1 words), or 0
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
@@ -82,6 +83,19 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
 __device__ bool gang_arrive(uint32_t* word, int C, int* s_flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = prev + 1 == (uint32_t)C;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Whole workgroup: record this member's arrival; the caller has already
+// waited for its stores (s_waitcnt 0 and a barrier).  Returns whether it was
+// the last of the C.
+__device__ bool gang_ticket(uint32_t* word, int C, int* s_flag) {
   if (threadIdx.x == 0) {
     const uint32_t prev =
         __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -136,12 +150,14 @@ struct Gang {
     const int q = lane & 3, r = lane >> 2;
     const int b = row / a.Hkv, g = row % a.Hkv;
     const int C = a.C;
+    const int NS = a.S;              // members 0..NS-1 stream the representatives
+    const bool streamer = c < NS;    // the others attend the eviction set meanwhile
     const int L = a.seq_lens[b];
     const int nb = min(L / kBlock, a.nb_max);
     const int tail = L - nb * kBlock;
     const int nsub = nb * kSubs;
-    const int j0 = min(c * a.per_wg, nsub);
-    const int j1 = min(j0 + a.per_wg, nsub);
+    const int j0 = streamer ? min(c * a.per_wg, nsub) : nsub;
+    const int j1 = streamer ? min(j0 + a.per_wg, nsub) : nsub;
     const int h0 = GS >= 4 ? q * KEEP : q / DUP;
     const bool canon = (q % DUP) == 0;
     uint32_t* words = a.words + (int64_t)row * kGangWords;
@@ -159,18 +175,31 @@ struct Gang {
     // after the streaming below (their latency overlaps it); the table goes
     // straight to shared memory (64 entries per wave and instruction)
     if (a.tbl_words > 0) {
-      // entries past the row's last block (the tail's, which exists only when
-      // the row is not full) are clamped into the row
+      // blocks 0..nb: the full ones and the tail's (which exists only when
+      // the row is not full)
       const int last = min(nb, a.max_blocks - 1);
       for (int base = wave * kWave; base <= last; base += kThreads)
-        __builtin_amdgcn_global_load_lds(trow + min(base + lane, last), tbl + base, 4, 0, 0);
+        if (base + lane <= last) __builtin_amdgcn_global_load_lds(trow + base + lane, tbl + base, 4, 0, 0);
+    }
+    {
+      // the attention queries, G x D, 4 bytes per lane and instruction
+      constexpr int kWords = G * D * (int)sizeof(T) / 4;
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qrow);
+      uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
+      for (int base = wave * kWave; base < kWords; base += kThreads)
+        if (base + lane < kWords) __builtin_amdgcn_global_load_lds(qw + base + lane, ql + base, 4, 0, 0);
     }
     const int seen_pre = a.k_e > 0 ? a.evict_seen[row] : 0;
     const int ev_pre = (int)threadIdx.x < a.k_e ? a.evict_set[(int64_t)row * a.k_e + threadIdx.x] : 0;
 
     // ---- 1. logits of this member's representatives, in registers
     float lg[U][KEEP];
-    {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) lg[u][kk] = -INFINITY;
+    }
+    if (streamer) {
       QSlice<T, D> qs[GS];
       const T* qb = static_cast<const T*>(a.query) +
                     (FORECAST ? (int64_t)row * D : ((int64_t)b * a.Hkv + g) * G * D);
@@ -207,7 +236,7 @@ struct Gang {
 
     // ---- 2. softmax statistics of this member's logits (group softmax)
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
-    if constexpr (!FORECAST) {
+    if (!FORECAST && streamer) {
       float m[KEEP], s[KEEP];
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) {
@@ -241,7 +270,6 @@ struct Gang {
         store_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + c) * G + h) * 8),
                           f32x2{M, S});
       }
-      gang_arrive(words + 0, C, &sm.s_int[0]);
     }
     // the logits wait in shared memory while this member attends
 #pragma unroll
@@ -250,7 +278,7 @@ struct Gang {
       for (int kk = 0; kk < KEEP; ++kk) sm.lgs[u][kk][threadIdx.x] = lg[u][kk];
     }
 
-    __builtin_amdgcn_s_waitcnt(0);  // the table has landed
+    __builtin_amdgcn_s_waitcnt(0);  // the table and queries have landed, the statistics are out
     __syncthreads();
 
     // ---- 3. the eviction set: the k_e best of (old set U blocks that became
@@ -287,10 +315,15 @@ struct Gang {
     }
     __syncthreads();
 
-    // ---- attention over this member's share of the eviction set + tail:
-    // items c, c + C, c + 2C, ... of [eviction set..., tail]
+    // ---- attention over this member's share of the eviction set + tail: the
+    // attenders take items (c - NS), (c - NS) + (C - NS), ... of [eviction
+    // set..., tail] at once; with no attenders every member takes items
+    // c, c + C, ..., part now and the rest after publishing its candidates
+    const int NA = C - NS;
+    const int e_rank = NA > 0 ? c - NS : c;
+    const int e_stride = NA > 0 ? NA : C;
     auto e_item = [&](int it) {
-      const int idx = c + it * C;
+      const int idx = e_rank + it * e_stride;
       const int blk = idx < n_e ? eids[idx] : nb;
       const int64_t phys = a.tbl_words > 0 ? tbl[blk] : trow[blk];
       Item x;
@@ -300,20 +333,25 @@ struct Gang {
       return x;
     };
     const int n_eitems = n_e + (tail > 0);
-    const int e_mine = n_eitems > c ? (n_eitems - c + C - 1) / C : 0;
-    const int e_first = (e_mine * a.e_first_pct + 99) / 100;
-    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att,
-                                       sm.acc);
+    const int e_mine = (NA > 0 && streamer) || e_rank >= n_eitems
+                           ? 0 : (n_eitems - e_rank + e_stride - 1) / e_stride;
+    const int e_first = NA > 0 ? e_mine : (e_mine * a.e_first_pct + 99) / 100;
+    // the first slab's loads go out before the arrival ticket's round trip
+    Slab<T, D> pf;
+    if (e_first > 0) slab_issue<T, D, false>(pf, e_item(0), kp, vp);
+    if (!FORECAST && streamer) gang_ticket(words + 0, NS, &sm.s_int[0]);
+    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds, true>(
+        qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att, sm.acc, &pf);
 
     // ---- 4. row normaliser from every member's statistics
     uint32_t* err = a.err;
-    if constexpr (!FORECAST) {
-      gang_wait(words + 0, C, err, a.wait_ticks);
+    if (!FORECAST && streamer) {
+      gang_wait(words + 0, NS, err, a.wait_ticks);
       if (threadIdx.x < kWave) {
         // lane: members lane / G, + 64 / G, ...; head lane % G
         float M = -INFINITY, S = 0.f;
         const int h = lane % G;
-        for (int m2 = lane / G; m2 < C; m2 += kWave / G) {
+        for (int m2 = lane / G; m2 < NS; m2 += kWave / G) {
           const f32x2 st =
               load_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + m2) * G + h) * 8));
           merge_ms(M, S, st.x, st.y);
@@ -331,70 +369,75 @@ struct Gang {
       }
     }
 
-    // ---- 5. scores of this member's blocks; its best candidates
-    const int blk0 = j0 / kSubs;
-    for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
-    __syncthreads();
-    for (int i = threadIdx.x; i < n_e; i += kThreads) {
-      const int id = eids[i];
-      if (id >= blk0 && id < blk0 + CBLK) sm.ckeys[id - blk0] = 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v = 0.f;
-      if constexpr (FORECAST) {
-        v = sm.lgs[u][0][threadIdx.x];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KEEP; ++kk) {
-          const float l = sm.lgs[u][kk][threadIdx.x];
-          if (canon && l != -INFINITY) v += exp2f(l - sm.sM[h0 + kk]) * sm.sInvZ[h0 + kk];
-        }
-        v += quad_partner<2>(v);
-        v += quad_partner<1>(v);
-      }
-      v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
-      v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
-      if ((lane & 15) == 0) {
-        const int bl = u * 16 + wave * 4 + (lane >> 4);
-        const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
-        sm.ckeys[bl] = (j < j1 && sm.ckeys[bl] != 0u) ? order_key(v) : 0u;
-      }
-    }
-    __syncthreads();
-
-    // this member's best mc blocks (ties to the lower id) fill slots
-    // 0..mc-1 of its list in block order; the remaining slots get an empty
-    // entry
+    // the second eviction-set phase's first slab: its loads land during the
+    // scoring below
+    if (e_first < e_mine) slab_issue<T, D, false>(pf, e_item(e_first), kp, vp);
     const int m_row = max(0, min(a.k - n_e, nb - n_e));
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.cand, a.cand_bytes);
-    if (threadIdx.x < kWave) {
-      const int64_t cbase = ((int64_t)row * kMaxGang + c) * a.mloc_max;
-      int nz = 0;
-#pragma unroll
-      for (int j = 0; j < CBLK / kWave; ++j) nz += __popcll(__ballot(sm.ckeys[j * kWave + lane] != 0u));
-      const int mc = min(min(m_row, nz), a.mloc);
-      if (mc > 0) {
-        int take_eq;
-        const uint32_t thr = wave_kth_key<CBLK / kWave>(sm.ckeys, CBLK, mc, &take_eq);
-        wave_emit_top(sm.ckeys, CBLK, thr, take_eq, [&](int i, int pos) {
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[i], (uint32_t)(blk0 + i)}, cr,
-                                                (int)((cbase + pos) * 8), 0, kSC1);
-        });
+    const int blk0 = j0 / kSubs;
+    if (streamer) {
+      // ---- 5. scores of this member's blocks; its best candidates
+      for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
+      __syncthreads();
+      for (int i = threadIdx.x; i < n_e; i += kThreads) {
+        const int id = eids[i];
+        if (id >= blk0 && id < blk0 + CBLK) sm.ckeys[id - blk0] = 0u;
       }
-      for (int i = mc + lane; i < a.mloc; i += kWave)
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, cr, (int)((cbase + i) * 8), 0, kSC1);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v = 0.f;
+        if constexpr (FORECAST) {
+          v = sm.lgs[u][0][threadIdx.x];
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KEEP; ++kk) {
+            const float l = sm.lgs[u][kk][threadIdx.x];
+            if (canon && l != -INFINITY) v += exp2f(l - sm.sM[h0 + kk]) * sm.sInvZ[h0 + kk];
+          }
+          v += quad_partner<2>(v);
+          v += quad_partner<1>(v);
+        }
+        v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+        v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+        if ((lane & 15) == 0) {
+          const int bl = u * 16 + wave * 4 + (lane >> 4);
+          const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
+          sm.ckeys[bl] = (j < j1 && sm.ckeys[bl] != 0u) ? order_key(v) : 0u;
+        }
+      }
+      __syncthreads();
+
+      // this member's best mc blocks (ties to the lower id) fill slots
+      // 0..mc-1 of its list in block order; the remaining slots get an empty
+      // entry
+      if (threadIdx.x < kWave) {
+        const int64_t cbase = ((int64_t)row * kMaxGang + c) * a.mloc_max;
+        int nz = 0;
+#pragma unroll
+        for (int j = 0; j < CBLK / kWave; ++j) nz += __popcll(__ballot(sm.ckeys[j * kWave + lane] != 0u));
+        const int mc = min(min(m_row, nz), a.mloc);
+        if (mc > 0) {
+          int take_eq;
+          const uint32_t thr = wave_kth_key<CBLK / kWave>(sm.ckeys, CBLK, mc, &take_eq);
+          wave_emit_top(sm.ckeys, CBLK, thr, take_eq, [&](int i, int pos) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[i], (uint32_t)(blk0 + i)}, cr,
+                                                  (int)((cbase + pos) * 8), 0, kSC1);
+          });
+        }
+        for (int i = mc + lane; i < a.mloc; i += kWave)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, cr, (int)((cbase + i) * 8), 0, kSC1);
+      }
+      gang_arrive(words + 1, NS, &sm.s_int[1]);
     }
-    gang_arrive(words + 1, C, &sm.s_int[1]);
 
     // ---- the rest of this member's eviction-set share
-    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att,
-                                       sm.acc);
+    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds, true>(
+        qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att, sm.acc, &pf);
 
     // ---- 6. the row's query-aware set from every member's candidates
-    gang_wait(words + 1, C, err, a.wait_ticks);
-    const int ncand = C * a.mloc;
+    gang_wait(words + 1, NS, err, a.wait_ticks);
+    const int ncand = NS * a.mloc;
     uint32_t* ckey = scratch;                                 // ncand
     int* cid = reinterpret_cast<int*>(ckey + ncand);          // ncand
     int* qsel = cid + ncand;                                  // k
@@ -454,7 +497,7 @@ struct Gang {
       return x;
     };
     const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
-    attend_items_merge<T, D, G, false, kGangBuf>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
+    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
                                        sm.acc);
 
     // ---- 7. partials; the last member merges them into the output
@@ -500,7 +543,8 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e, kMaxGang), &gi);
   if (e != hipSuccess) return e;
   GangPlan plan;
-  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, &plan))
+  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, L.streamer_override,
+                 &plan))
     return hipErrorLaunchOutOfResources;
   GangArgs a{};
   a.query = L.query;
@@ -530,6 +574,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.k = L.k;
   a.k_e = L.k_e;
   a.C = plan.C;
+  a.S = plan.S;
   a.gangs = plan.gangs;
   a.per_wg = plan.per_wg;
   a.mloc = plan.mloc;

@@ -86,6 +86,18 @@ def test_step_gang_sizes(gang, monkeypatch):
     H.run_and_check(cfg, rows=H.sample_rows(cfg, 5), fused=True)
 
 
+@pytest.mark.parametrize("gang,streamers", [("5", "2"), ("16", "9")])
+def test_step_attending_members(gang, streamers, monkeypatch):
+    """Gangs whose last members attend the eviction set while the others
+    stream and score give the oracle's answer."""
+    cfg = W.Config("step-roles", 75, batch=2, context=64 * 300 + 5, num_q_heads=8,
+                   num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=40,
+                   k_e=24, steps=2)
+    monkeypatch.setenv("NSA_STEP_GANG", gang)
+    monkeypatch.setenv("NSA_STEP_STREAMERS", streamers)
+    H.run_and_check(cfg, fused=True)
+
+
 @pytest.mark.parametrize("efirst", ["1", "100"])
 def test_step_eviction_attention_split(efirst, monkeypatch):
     """The eviction-set attention split before / after the normaliser wait
