@@ -334,9 +334,8 @@ static nsa_status step_layout_checked(const char* fn, const nsa_shape* shape,
     return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_seq_len %d outside [1, %d]", fn, max_seq_len,
                 shape->max_blocks_per_seq * 64);
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  *lay = nsa::step_layout(shape->batch, shape->num_kv_heads, G, shape->head_dim, params->k,
-                          params->k_e, max_seq_len);
-  const size_t lds = nsa::gang_dyn_lds(*lay, params->k, params->k_e, nsa::kMaxGang);
+  *lay = nsa::step_layout(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_seq_len);
+  const size_t lds = nsa::gang_dyn_lds(*lay, params->k, params->k_e);
   if (lds > 64 * 1024)
     return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 65536)", fn, lds);
   if (4 * lay->nb_max > nsa::kMaxGang * nsa::kGangReps)
@@ -413,14 +412,10 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
   L.k_e = params->k_e;
   L.scale = scale_of(shape);
   L.gang_override = env_int("NSA_STEP_GANG");
-  L.streamer_override = env_int("NSA_STEP_STREAMERS");
-  const char* efirst = std::getenv("NSA_STEP_EFIRST");
-  const int pct = efirst ? std::atoi(efirst) : 25;
-  L.e_first_pct = pct < 0 ? 0 : (pct > 100 ? 100 : pct);
   L.lay = lay;
   if (env_trace())
-    std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d mloc_max=%d gang=%d efirst=%d%%\n", lay.rows,
-                 lay.nb_max, lay.mloc_max, L.gang_override, L.e_first_pct);
+    std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d gang=%d (0: by occupancy)\n", lay.rows,
+                 lay.nb_max, L.gang_override);
   return launched(fn, nsa::launch_step(L, stream));
 }
 

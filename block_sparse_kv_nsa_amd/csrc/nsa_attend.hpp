@@ -362,14 +362,12 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
 
   // wave partial: l and acc summed over the value-layout token groups
   // (each group counted its own rows; m is wave-uniform)
+  static_assert(LPR >= 8 && LPR < kWave, "value layout");
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    l[h] = lanes_sum_from(l[h], LPR);
 #pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) {
-      l[h] += __shfl_xor(l[h], off, kWave);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, kWave);
-    }
+    for (int e = 0; e < EPL; ++e) acc[h][e] = lanes_sum_from(acc[h][e], LPR);
   }
   if (grp == 0) {
 #pragma unroll
@@ -383,6 +381,182 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     }
   }
   __syncthreads();
+}
+
+// Running online-softmax state of one wave over any number of slabs, for
+// the fused step: the same arithmetic as attend_core (lazy reference
+// maximum, weights moved to the value layout through shared memory), with
+// the slab loads issued by the caller (slab_issue) so that they can be in
+// flight across other work, and the query slices read from sm.qlds.
+template <typename T, int D, int G>
+struct AttnState {
+  using Q = Quad<T, D>;
+  using V = VGeo<T, D>;
+  static constexpr int KEEP = G >= 4 ? G / 4 : 1;
+  static constexpr int DUP = G >= 4 ? 1 : 4 / G;
+  float m[G], l[G], acc[G][V::EPL], mref[KEEP];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < V::EPL; ++e) acc[h][e] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KEEP; ++kk) mref[kk] = -INFINITY;
+  }
+
+  // Accumulate slab s (loads issued by slab_issue<T, D, false>).  The query
+  // slices come from sm.qlds, a batch of HB heads (at most 32 registers) per
+  // shared-memory round trip; the empty asm keeps the loads in this slab's
+  // code (they would otherwise be hoisted into registers for the whole run).
+  static constexpr int HB = (int)(128 / sizeof(QSlice<T, D>)) < 1 ? 1
+                            : ((int)(128 / sizeof(QSlice<T, D>)) < G ? (int)(128 / sizeof(QSlice<T, D>)) : G);
+  __device__ __forceinline__ void consume(const Slab<T, D>& s, AttendSmem<T, D, G>& sm,
+                                          float qscale) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int q = lane & 3, r = lane >> 2;
+    const int grp = lane / V::LPR;
+    const int h0 = G >= 4 ? q * KEEP : q / DUP;
+    const bool canon = (q % DUP) == 0;
+    const int tk = wave * kSub + r;
+    float v[G];
+#pragma unroll
+    for (int hb = 0; hb < G; hb += HB) {
+      asm volatile("" ::: "memory");
+      QSlice<T, D> qs[HB];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) qs[h].load(&sm.qlds[hb + h][0], q);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) v[hb + h] = qs[h].dot(s.k);
+    }
+    quad_reduce<2, G>(v, q);
+    float lg[KEEP];
+    bool over = false;
+#pragma unroll
+    for (int kk = 0; kk < KEEP; ++kk) {
+      lg[kk] = tk < s.it.valid ? v[kk] * qscale : -INFINITY;
+      over |= lg[kk] > mref[kk] + kLazyMax;
+    }
+    if (__any(over)) {  // wave-uniform: raise the reference, rescale
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < KEEP; ++kk)
+          if (h0 + kk == h) bm = fmaxf(bm, lg[kk]);
+        bm = wave_max(bm);
+        const float mn = fmaxf(m[h], bm);
+        if (mn > m[h]) {
+          const float alpha = m[h] == -INFINITY ? 0.f : exp2f(m[h] - mn);
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < V::EPL; ++e) acc[h][e] *= alpha;
+          m[h] = mn;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KEEP; ++kk)
+          if (h0 + kk == h) mref[kk] = m[h];
+      }
+    }
+    if (canon) {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk)
+        sm.p_lds[wave][r][h0 + kk] = lg[kk] == -INFINITY ? 0.f : fast_exp2(lg[kk] - mref[kk]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float pv[V::NLV][G];
+#pragma unroll
+    for (int u = 0; u < V::NLV; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[u][h] = sm.p_lds[wave][u * V::TPL + grp][h];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < V::NLV; ++u) {
+      float vf[V::EPL];
+      unpack<T>(s.v[u], vf);
+      // rows past the tail may hold anything (even NaN): keep them out of acc
+      if (wave * kSub + u * V::TPL + grp >= s.it.valid) {
+#pragma unroll
+        for (int e = 0; e < V::EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] += pv[u][h];
+#pragma unroll
+        for (int e = 0; e < V::EPL; ++e) acc[h][e] = fmaf(pv[u][h], vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // The wave's partial (l and acc summed over its value-layout token groups)
+  // into sm.wm / wl / wacc; ends with a barrier.
+  __device__ __forceinline__ void to_lds(AttendSmem<T, D, G>& sm) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int sl = lane % V::LPR, grp = lane / V::LPR;
+    static_assert(V::LPR >= 8 && V::LPR < kWave, "value layout");
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      l[h] = lanes_sum_from(l[h], V::LPR);
+#pragma unroll
+      for (int e = 0; e < V::EPL; ++e) acc[h][e] = lanes_sum_from(acc[h][e], V::LPR);
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < V::EPL; ++e) sm.wacc[wave][h][sl * V::EPL + e] = acc[h][e];
+        if (sl == 0) {
+          sm.wm[wave][h] = m[h];
+          sm.wl[wave][h] = l[h];
+        }
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// Merge the waves' partials (sm.wm / wl / wacc, after AttnState::to_lds) and
+// publish them as partial pidx: acc[G][D] first (agent-scope stores), then,
+// once every thread's stores have completed, (m, l) per head.  A reader that
+// sees a nonzero (m, l) pair therefore sees the whole partial: (m, l) of a
+// real partial is never all-zero bits (l >= 1 when m is finite, and m =
+// -inf otherwise).
+template <typename T, int D, int G>
+__device__ void wg_publish_partial(AttendSmem<T, D, G>& sm, f32x2* ml_lds,
+                                   __amdgpu_buffer_rsrc_t mlr, __amdgpu_buffer_rsrc_t acr,
+                                   int64_t pidx) {
+  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
+    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
+    float M = sm.wm[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][h]);
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (sm.wm[w][h] == -INFINITY) continue;
+        const float f = exp2f(sm.wm[w][h] - M);
+        A.x = fmaf(sm.wacc[w][h][c], f, A.x);
+        A.y = fmaf(sm.wacc[w][h][c + 1], f, A.y);
+        A.z = fmaf(sm.wacc[w][h][c + 2], f, A.z);
+        A.w = fmaf(sm.wacc[w][h][c + 3], f, A.w);
+        Ls = fmaf(sm.wl[w][h], f, Ls);
+      }
+    }
+    store_agent_f32x4(acr, (uint32_t)(((pidx * G + h) * D + c) * 4), A);
+    if (c == 0) ml_lds[h] = f32x2{M, Ls};
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's acc stores are complete
+  __syncthreads();                // ... and every other thread's
+  if (threadIdx.x < G)
+    store_agent_f32x2(mlr, (uint32_t)((pidx * G + threadIdx.x) * 8), ml_lds[threadIdx.x]);
 }
 
 // Merge partials [p0, p0 + nparts) (agent-scope loads) into out[G][D]:

@@ -299,6 +299,235 @@ __device__ __attribute__((always_inline)) void wg_top_m(const uint32_t* keys, in
 }
 
 // ---------------------------------------------------------------------------
+// workgroup radix select over keys in shared memory
+// ---------------------------------------------------------------------------
+// keys[0..n) in shared memory; keys <= 1 are not candidates.  The m-th
+// largest candidate is found 8 bits at a time: a 256-bin histogram (shared-
+// memory atomics) of the next digit of the candidates that match the digits
+// found so far, and one wave's scan of the bins from the top.  A pass whose
+// bin holds exactly the keys still needed ends the search early.  Thread t
+// takes indices t, t + kThreads, ...
+constexpr int kRadixChunks = 32;  // most keys per thread: 8192 per workgroup
+
+struct RadixSmem {
+  uint32_t hist[256];
+  uint32_t cnt[kRadixChunks][kWaves][2];
+  uint32_t res[4];
+};
+
+// inclusive prefix sum over the 64 lanes: DPP shifts within rows of 16
+// lanes, then the totals of the lower rows
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Threshold of the m largest candidates (1 <= m <= number of candidates,
+// n <= kThreads * kRadixChunks): they are the candidates with
+// (key >> *shift) > (*P >> *shift) and the first *take_eq, in index order,
+// with (key >> *shift) == (*P >> *shift).  Called by all threads.
+__device__ __attribute__((always_inline)) inline void wg_radix_top(const uint32_t* keys, int n,
+                                                                   int m, RadixSmem& rs,
+                                                                   uint32_t* P, int* shift,
+                                                                   int* take_eq) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  uint32_t prefix = 0u;
+  int need = m, sh = 24;
+  for (;; sh -= 8) {
+    rs.hist[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const uint32_t v = keys[i];
+      if (v > 1u && (sh == 24 || (v >> (sh + 8)) == (prefix >> (sh + 8))))
+        atomicAdd(&rs.hist[(v >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l: digits 255 - 4l .. 252 - 4l, from the top
+      uint32_t cb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cb[i] = rs.hist[255 - 4 * lane - i];
+      const uint32_t sum = cb[0] + cb[1] + cb[2] + cb[3];
+      const uint32_t inc = wave_incl_scan(sum);
+      const uint64_t ge = __ballot(inc >= (uint32_t)need);
+      const int ls = ge ? (int)__builtin_ctzll(ge) : kWave - 1;
+      if (lane == ls) {
+        // the highest digit at which the count from the top reaches need
+        uint32_t cum = inc - sum, above = 0u, in_bin = 0u;
+        int d = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (d < 0 && cum + cb[i] >= (uint32_t)need) {
+            d = 255 - 4 * lane - i;
+            above = cum;
+            in_bin = cb[i];
+          }
+          cum += cb[i];
+        }
+        if (d < 0) {  // fewer candidates than m (not a valid call): take them all
+          d = 0;
+          above = 0u;
+          in_bin = (uint32_t)need;
+        }
+        rs.res[0] = (uint32_t)d;
+        rs.res[1] = above;
+        rs.res[2] = in_bin;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = rs.res[0];
+    need -= (int)rs.res[1];
+    prefix |= d << sh;
+    if ((int)rs.res[2] == need || sh == 0) break;  // uniform
+  }
+  *P = prefix;
+  *shift = sh;
+  *take_eq = need;
+}
+
+// The m largest candidates (m <= 16) of keys held in registers, when few
+// keys come near them: kv[j] is the key of index t + kThreads * j (0 past the
+// end; keys <= 1 are not candidates).  Every 16-lane row's largest candidate
+// is >= T0, the least of the 16 row maxima, so at least 16 candidates are
+// >= T0 and the m largest are among them.  Those (at most 64, else the call
+// declines) are gathered in index order and ranked by (key descending, index
+// ascending); emit(index, rank in index order) for the m best.  Returns false
+// without emitting when it declines (m > 16, a row without candidates, or
+// more than 64 keys >= T0, e.g. many equal scores).  Called by all threads.
+struct SmallTopSmem {
+  uint32_t ck[64 + kThreads];  // the gathered keys, then one unused slot per thread
+  int cid[64 + kThreads];
+  uint32_t gmin[kWaves];
+  uint32_t cnt[kWaves][kRadixChunks];
+  int rk[kWaves][64];
+};
+
+template <int KPT, typename Emit>
+__device__ __attribute__((always_inline)) bool wg_top_small(const uint32_t (&kv)[KPT], int m,
+                                                            SmallTopSmem& ss, Emit emit) {
+  static_assert(KPT <= kRadixChunks && KPT <= kWave, "keys per thread");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) mx = max(mx, kv[j] > 1u ? kv[j] : 0u);
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x121, 0xF, 0xF, false));  // row_ror:1
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x122, 0xF, 0xF, false));  // row_ror:2
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x124, 0xF, 0xF, false));  // row_ror:4
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)mx, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)mx, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)mx, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)mx, 48);
+  ss.gmin[wave] = min(min(r0, r1), min(r2, r3));  // every lane writes the same value
+  __syncthreads();
+  const uint32_t t0 = min(min(ss.gmin[0], ss.gmin[1]), min(ss.gmin[2], ss.gmin[3]));
+  if (m > 16 || t0 <= 1u) return false;  // uniform
+  // keys >= t0 per chunk: lane j of each wave holds chunk j's count
+  uint32_t myc = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t c = (uint32_t)__popcll(__ballot(kv[j] >= t0));
+    myc = lane == j ? c : myc;
+  }
+  if (lane < KPT) ss.cnt[wave][lane] = myc;
+  __syncthreads();
+  // gather in index order (chunk, then wave, then lane), without branches
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int c0 = (int)ss.cnt[0][j], c1 = (int)ss.cnt[1][j], c2 = (int)ss.cnt[2][j],
+              c3 = (int)ss.cnt[3][j];
+    const int base = run + (wave > 0 ? c0 : 0) + (wave > 1 ? c1 : 0) + (wave > 2 ? c2 : 0);
+    run += c0 + c1 + c2 + c3;
+    const bool c = kv[j] >= t0;
+    int p = base + __popcll(__ballot(c) & below);
+    p = (c && p < 64) ? p : 64 + (int)threadIdx.x;
+    ss.ck[p] = kv[j];
+    ss.cid[p] = (int)threadIdx.x + kThreads * j;
+  }
+  const int total = run;  // uniform
+  if (total > 64) return false;
+  __syncthreads();
+  // rank among the gathered: wave w compares every key with keys 16w..16w+15
+  {
+    const uint32_t k = ss.ck[lane];
+    int part = 0;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * wave + jj;
+      const uint32_t kj = ss.ck[j];
+      part += (j < total) & ((kj > k) | ((kj == k) & (j < lane)));
+    }
+    ss.rk[wave][lane] = part;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int rank = ss.rk[0][lane] + ss.rk[1][lane] + ss.rk[2][lane] + ss.rk[3][lane];
+    const bool sel = lane < total && rank < m;
+    const uint64_t bs = __ballot(sel);
+    if (sel) emit(ss.cid[lane], __popcll(bs & below));
+  }
+  return true;
+}
+
+// Visit the m largest candidates selected by (P, shift, take_eq) from
+// wg_radix_top in index order: emit(index, rank in index order).  One
+// barrier; the caller synchronises before reading what emit wrote.
+template <typename Emit>
+__device__ __attribute__((always_inline)) void wg_radix_emit(const uint32_t* keys, int n,
+                                                             uint32_t P, int shift, int take_eq,
+                                                             RadixSmem& rs, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t ps = P >> shift;
+  const int chunks = (n + kThreads - 1) / kThreads;
+  for (int j = 0; j < chunks; ++j) {
+    const int i = threadIdx.x + kThreads * j;
+    const uint32_t v = i < n ? keys[i] : 0u;
+    const uint64_t bg = __ballot(v > 1u && (v >> shift) > ps);
+    const uint64_t be = __ballot(v > 1u && (v >> shift) == ps);
+    if (lane == 0) {
+      rs.cnt[j][wave][0] = (uint32_t)__popcll(bg);
+      rs.cnt[j][wave][1] = (uint32_t)__popcll(be);
+    }
+  }
+  __syncthreads();
+  int run_gt = 0, run_eq = 0;  // candidates of the chunks before j (every wave)
+  for (int j = 0; j < chunks; ++j) {
+    int base_gt = run_gt, base_eq = run_eq;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cg = (int)rs.cnt[j][w][0], ce = (int)rs.cnt[j][w][1];
+      if (w < wave) {
+        base_gt += cg;
+        base_eq += ce;
+      }
+      run_gt += cg;
+      run_eq += ce;
+    }
+    const int i = threadIdx.x + kThreads * j;
+    const uint32_t v = i < n ? keys[i] : 0u;
+    const bool gt = v > 1u && (v >> shift) > ps, eq = v > 1u && (v >> shift) == ps;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const int eq_before = base_eq + __popcll(be & below);
+    if (gt || (eq && eq_before < take_eq))
+      emit(i, base_gt + __popcll(bg & below) + min(eq_before, take_eq));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // cross-workgroup hand-off without cache-wide fences
 // ---------------------------------------------------------------------------
 // A workgroup that hands data to the last workgroup of its row writes that
@@ -399,11 +628,75 @@ __device__ __forceinline__ void quad_reduce(float* v, int q) {
   }
 }
 
+// The value of this lane and of the lane whose index differs in bit 4
+// (lane_pair<16>) or bit 5 (lane_pair<32>), as (lower lane's, upper lane's)
+// in both lanes of the pair: gfx950 lane swaps, no shared-memory round trip.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  static_assert(OFF == 16 || OFF == 32, "lane swap distance");
+  const int x = __builtin_bit_cast(int, v);
+  int r0, r1;
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+
+// Sum over the lanes i, i ^ OFF, i ^ 2 OFF, ... < 64 (OFF >= 8), in every lane.
+__device__ __forceinline__ float lanes_sum_from(float v, int off) {
+  if (off <= 8) v += dpp_mov<0x128>(v);  // row_ror:8 (i ^ 8 within the row)
+  if (off <= 16) {
+    float lo, hi;
+    lane_pair<16>(v, lo, hi);
+    v = lo + hi;
+  }
+  float lo, hi;
+  lane_pair<32>(v, lo, hi);
+  return lo + hi;
+}
+
+// Merge (m, s) pairs (see merge_ms) over the lanes i, i ^ off, i ^ 2 off,
+// ... < 64 (off a power of two), every lane ending with the merge.
+__device__ __forceinline__ void merge_ms_lanes(float& m, float& s, int off) {
+  if (off <= 1) merge_ms(m, s, dpp_mov<kDppQuadXor1>(m), dpp_mov<kDppQuadXor1>(s));
+  if (off <= 2) merge_ms(m, s, dpp_mov<kDppQuadXor2>(m), dpp_mov<kDppQuadXor2>(s));
+  // rotations by 4 and 8 within a row of 16 lanes: together a full merge of
+  // the row's lanes that agree in the lower bits
+  if (off <= 4) merge_ms(m, s, dpp_mov<0x124>(m), dpp_mov<0x124>(s));
+  if (off <= 8) merge_ms(m, s, dpp_mov<0x128>(m), dpp_mov<0x128>(s));
+  float ml, mh, sl, sh;
+  if (off <= 16) {
+    lane_pair<16>(m, ml, mh);
+    lane_pair<16>(s, sl, sh);
+    m = ml;
+    s = sl;
+    merge_ms(m, s, mh, sh);
+  }
+  lane_pair<32>(m, ml, mh);
+  lane_pair<32>(s, sl, sh);
+  m = ml;
+  s = sl;
+  merge_ms(m, s, mh, sh);
+}
+
 // max over all 64 lanes, result in every lane
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, dpp_mov<0x121>(v));  // row_ror:1
+  v = fmaxf(v, dpp_mov<0x122>(v));  // row_ror:2
+  v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+  float lo, hi;
+  lane_pair<16>(v, lo, hi);
+  v = fmaxf(lo, hi);
+  lane_pair<32>(v, lo, hi);
+  return fmaxf(lo, hi);
 }
 
 // ---------------------------------------------------------------------------

@@ -159,90 +159,72 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // fused step (one gang of workgroups per row):
-//   [control words | arrival words | member statistics | member candidates |
-//    member partial (m, l) | member partial acc]
-// Member buffers are sized for kMaxGang members so that the gang size can be
-// chosen at launch from the device's capacity.
+//   [control words | member statistics | member partial (m, l) | member
+//    partial acc | row block keys]
+// Member slots are sized for kMaxGang members so that the gang size can be
+// chosen at launch from the device's capacity.  Statistics, (m, l) and key
+// slots are all-zero until written and cleared again by the row's merging
+// member, so that the workspace needs zeroing only before its first use.
+// Only the keys depend on max_seq_len and they come last: calls with
+// different max_seq_len on one workspace never find partial data where
+// they look for a slot.
 // ---------------------------------------------------------------------------
-enum : int { kErr = 2, kCtrlWords = 4 };
-constexpr int kGangWords = 3;    // per row: statistics, candidates, partials
+enum : int { kErr = 2 };
 constexpr int kMaxGang = 64;     // most workgroups per row
-constexpr int kGangReps = 512;   // most representatives a streamer scores (in registers)
+constexpr int kGangReps = 512;   // most representatives a member scores (in registers)
 
 struct StepLayout {
-  int rows, G, D, nb_max, mloc_max;
-  size_t off_words, off_stats, off_cand, off_ml, off_acc, bytes;
+  int rows, G, D, nb_max;
+  size_t off_stats, off_ml, off_acc, off_keys, bytes;
 };
 
-inline StepLayout step_layout(int B, int Hkv, int G, int D, int k, int k_e, int max_seq_len) {
+inline StepLayout step_layout(int B, int Hkv, int G, int D, int max_seq_len) {
   StepLayout s{};
   s.rows = B * Hkv;
   s.G = G;
   s.D = D;
   s.nb_max = max_seq_len / 64;
-  s.mloc_max = k - k_e > 0 ? k - k_e : 1;  // the query-aware part takes at most k - k_e
   const size_t members = (size_t)s.rows * kMaxGang;
-  s.off_words = 256;
-  s.off_stats = round_up(s.off_words + (size_t)s.rows * kGangWords * 4, 256);
-  s.off_cand = round_up(s.off_stats + members * G * 8, 256);
-  s.off_ml = round_up(s.off_cand + members * s.mloc_max * 8, 256);
+  s.off_stats = 256;
+  s.off_ml = round_up(s.off_stats + members * G * 8, 256);
   s.off_acc = round_up(s.off_ml + members * G * 8, 256);
-  s.bytes = round_up(s.off_acc + members * G * D * 4, 256);
+  s.off_keys = round_up(s.off_acc + members * G * D * 4, 256);
+  s.bytes = round_up(s.off_keys + (size_t)s.rows * s.nb_max * 4, 256);
   return s;
 }
 
-constexpr int kTblMaxWords = 4096;  // longest table row kept in shared memory
-
-// Words of shared memory for the row's block table (full blocks and the tail
-// block, staged 64 entries at a time), or 0 when the row is longer than
-// kTblMaxWords and the table is read from global memory.
-inline int gang_tbl_words(const StepLayout& lay) {
-  const int w = (lay.nb_max + 1 + 63) / 64 * 64;
-  return w <= kTblMaxWords ? w : 0;
-}
-
-// Dynamic shared memory of a member: the eviction set, the table row, then the
-// larger of the eviction update (keys of old set + new blocks, old set) and
-// the selection (all members' candidates, the query-aware list, block flags).
-inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e, int C, int mloc = 0) {
-  const int ml = mloc > 0 ? mloc : lay.mloc_max;
-  const size_t eids = (size_t)(k_e > 0 ? k_e : 1) * 4 + (size_t)gang_tbl_words(lay) * 4;
-  const size_t upd = (size_t)(k_e + lay.nb_max) * 4 + (size_t)k_e * 4;
-  const size_t sel = (size_t)C * ml * 8 + (size_t)k * 4 + round_up((size_t)lay.nb_max, 4);
-  return round_up(eids + (upd > sel ? upd : sel), 16);
+// Dynamic shared memory of a member: the eviction set, the query-aware list,
+// then the larger of the eviction update's keys (old set and new blocks) and
+// old set, and the row's block keys.
+inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e) {
+  const size_t upd = (size_t)(k_e + lay.nb_max) + k_e;
+  const size_t words = (size_t)(k_e > 0 ? k_e : 1) + k + (upd > (size_t)lay.nb_max ? upd : lay.nb_max);
+  return round_up(words * 4, 16);
 }
 
 struct GangPlan {
-  int C, S, gangs, per_wg, mloc;
+  int C, gangs, per_wg;
   size_t dyn_lds;
 };
 
 // Gang size C: as many members as the resident workgroups allow across the
-// rows (at most kMaxGang), and at least enough streamers to hold the longest
-// row's representatives in registers.  Streamers S: every member by default;
-// with s_override < C the other C - S members attend the eviction set while
-// the streamers score (this lengthens the scoring path, which is the step's
-// critical path, more than it saves at the measured shapes).  Rows beyond the
+// rows (at most kMaxGang), and at least enough to hold the longest row's
+// representatives in registers (kGangReps per member).  Rows beyond the
 // resident gangs are taken in turn.
 inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int c_override,
-                      int s_override, GangPlan* p) {
+                      GangPlan* p) {
   const int nsub = 4 * lay.nb_max;
-  const int s_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
+  const int c_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
   const int c_cap = capacity < kMaxGang ? capacity : kMaxGang;
-  if (s_min > c_cap) return false;
+  if (c_min > c_cap) return false;
   int C = c_override > 0 ? c_override : capacity / (lay.rows > 0 ? lay.rows : 1);
-  C = C < s_min ? s_min : (C > c_cap ? c_cap : C);
-  int S = s_override > 0 ? s_override : C;
-  S = S < s_min ? s_min : (S > C ? C : S);
+  C = C < c_min ? c_min : (C > c_cap ? c_cap : C);
   p->C = C;
-  p->S = S;
   p->gangs = capacity / C < lay.rows ? capacity / C : lay.rows;
   if (p->gangs < 1) return false;
-  const int per = nsub > 0 ? (nsub + S - 1) / S : 4;
+  const int per = nsub > 0 ? (nsub + C - 1) / C : 4;
   p->per_wg = (int)round_up((size_t)per, 4);
-  const int blocks = p->per_wg / 4;
-  p->mloc = k - k_e < blocks ? (k - k_e > 0 ? k - k_e : 1) : blocks;
-  p->dyn_lds = gang_dyn_lds(lay, k, k_e, C, p->mloc);
+  p->dyn_lds = gang_dyn_lds(lay, k, k_e);
   return true;
 }
 
@@ -264,9 +246,7 @@ struct StepLaunch {
   void* workspace;
   int B, Hkv, max_blocks, k, k_e;
   float scale;
-  int gang_override;      // 0: from capacity
-  int streamer_override;  // 0: from the byte shares
-  int e_first_pct;    // share of the eviction-set attention done before the normaliser wait
+  int gang_override;  // 0: from capacity
   StepLayout lay;
 };
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream);

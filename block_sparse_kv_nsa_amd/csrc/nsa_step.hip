@@ -11,28 +11,32 @@
 // launch.  (A cooperative launch would guarantee this but costs about 17 us
 // per launch on this part.)  Member c of the gang
 //   1. streams its contiguous share of the row's sub-block representatives
-//      and keeps the logits q.r in registers;
-//   2. publishes its softmax statistics (group-softmax mode);
-//   3. derives the row's eviction set (it depends on the eviction scores
-//      only, never on the query) and attends part of its share of those
-//      blocks and of the partial tail block while the other members finish
-//      streaming;
-//   4. once every member's statistics are in, forms the row normaliser,
-//      scores its own blocks and publishes its best candidates for the
-//      query-aware part (the row's best blocks are among the members' best),
-//      then attends the rest of its eviction-set share;
-//   5. once every member's candidates are in, selects the row's query-aware
-//      blocks itself (every member reaches the same set) and attends its
-//      share of them;
-//   6. stores its partial; the last member to arrive merges the C partials
-//      into the output.
-// Member 0 writes the eviction state and the selected list for the caller.
+//      and keeps the logits q.r in registers; the eviction set depends on the
+//      eviction scores only, never on the query, so the loads of the member's
+//      first two eviction-set (or tail) slabs go out during the stream;
+//   2. publishes its softmax statistics (group-softmax mode) and attends
+//      those two slabs while the other members finish streaming;
+//   3. forms the row normaliser from every member's statistics, scores its
+//      own blocks and publishes their keys, then attends the rest of its
+//      eviction-set share while the other members publish theirs;
+//   4. selects the row's query-aware blocks from all the keys of the row (a
+//      radix select: every member reaches the same set) and attends its share
+//      of them;
+//   5. publishes its partial; member 0 merges the C partials into the output,
+//      writes the selected list and the eviction state, and clears the row's
+//      hand-off slots.
+// One online-softmax state per wave runs through steps 2-4, so the member's
+// attention is merged across its waves once.
 //
-// Hand-offs between members use agent-scope stores and loads and 32-bit
-// arrival words per row (see gang_arrive); the last member of a row resets
-// the row's words, so the workspace is left as it was found.  Every wait is
-// bounded in time: on expiry the workgroup records a sticky error word, later
-// waits of the launch return at once, and the launch ends.
+// Hand-offs carry their own presence: a slot is all-zero bits until it is
+// written, and no written value is all-zero (statistics (m, s) have s >= 1
+// or m = -inf; keys are stored plus one; partial (m, l) as statistics), so a
+// reader polls the data itself: one store and one load per hand-off, no
+// counters and no fences.  Member 0 clears the slots once every partial is
+// in (every member has then read every slot of the row), so a completed call
+// leaves them as it found them.  Every wait is bounded in time: on expiry the
+// workgroup records a sticky error word, later waits of the launch return at
+// once, and the launch ends.
 #include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
@@ -41,8 +45,6 @@ namespace nsa {
 namespace {
 
 constexpr int kWaitMs = 200;  // longest a member waits for its gang
-constexpr int kGangBuf = 2;      // slabs in flight per member during attention
-constexpr bool kGangQLds = true;  // query slices read from shared memory per slab
 
 struct GangArgs {
   const void* query;  // group-softmax: [B][Hq][D]; forecast: [B][Hkv][D]
@@ -59,17 +61,23 @@ struct GangArgs {
   int32_t* num_selected;
   void* out;
   uint32_t* err;     // sticky error word
-  uint32_t* words;   // [rows][kGangWords] arrival words
-  float* stats;      // [rows][kMaxGang][G] (m, s)
-  uint32_t* cand;    // [rows][kMaxGang][mloc_max] (key, block)
+  float* stats;      // [rows][kMaxGang][G] (m, s): max logit and sum of 2^(l - m)
+  uint32_t* keys;    // [rows][nb_max] block key + 1 (1: not a candidate)
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
-  int rows, Hkv, max_blocks, nb_max, k, k_e, C, S, gangs, per_wg, mloc, mloc_max, e_first_pct;
-  int tbl_words;  // table row kept in shared memory (nb_max + 1 words), or 0
+  int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg;
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
-  uint32_t stats_bytes, cand_bytes, ml_bytes, acc_bytes;
+  uint32_t stats_bytes, keys_bytes, ml_bytes, acc_bytes;
 };
+
+// A value that no workgroup of the launch writes, read at a wave-uniform
+// address: through the constant address space, i.e. a scalar load, whose
+// wait does not hold back the vector loads in flight.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
+  return ((ConstI32)p)[i];
+}
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -78,47 +86,57 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Whole workgroup: record this member's arrival at a row's word once every
-// store it issued has completed.  Returns whether it was the last of the C.
-__device__ bool gang_arrive(uint32_t* word, int C, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = prev + 1 == (uint32_t)C;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// Whole workgroup: record this member's arrival; the caller has already
-// waited for its stores (s_waitcnt 0 and a barrier).  Returns whether it was
-// the last of the C.
-__device__ bool gang_ticket(uint32_t* word, int C, int* s_flag) {
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = prev + 1 == (uint32_t)C;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// Whole workgroup: wait until all C members arrived at `word` (bounded).
-__device__ void gang_wait(const uint32_t* word, int C, uint32_t* err, uint64_t wait_ticks) {
-  if (threadIdx.x == 0 && ld_agent(word) < (uint32_t)C) {
-    const uint64_t t0 = (uint64_t)wall_clock64();
-    while (ld_agent(word) < (uint32_t)C) {
-      if (ld_agent(err) != 0u) break;
-      if ((uint64_t)wall_clock64() - t0 > wait_ticks) {
-        st_agent(err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+// Bounded wait of one thread: more() sleeps briefly and returns true while
+// the caller may keep waiting; false on a time out (recorded in the sticky
+// error word) or when another workgroup has recorded one.
+struct Patience {
+  uint64_t t0;
+  bool started;
+  __device__ __forceinline__ bool more(uint32_t* err, uint64_t ticks) {
+    if (ld_agent(err) != 0u) return false;
+    const uint64_t now = (uint64_t)wall_clock64();
+    if (!started) {
+      started = true;
+      t0 = now;
+    } else if (now - t0 > ticks) {
+      st_agent(err, 1u);
+      return false;
     }
+    __builtin_amdgcn_s_sleep(1);
+    return true;
   }
-  __syncthreads();
+};
+
+// One wave: poll n (<= 64 * NP) 64-bit slots at off0 (agent scope) until none
+// is all-zero bits, then merge(i, slot i) for the lane's slots i = lane,
+// lane + 64, ...
+template <int NP, typename Merge>
+__device__ __forceinline__ void wave_poll_pairs(__amdgpu_buffer_rsrc_t r, uint32_t off0, int n,
+                                                uint32_t* err, uint64_t ticks, Merge merge) {
+  const int lane = threadIdx.x & (kWave - 1);
+  u32x2 v[NP];
+  Patience pt{0, false};
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = lane + kWave * j;
+      v[j] = u32x2{0u, 0u};
+      if (i < n) {
+        v[j] = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off0 + i * 8), 0, kSC1);
+        ok &= (v[j].x | v[j].y) != 0u;
+      }
+    }
+    if (__all(ok)) break;
+    bool go = true;
+    if (lane == 0) go = pt.more(err, ticks);
+    if (!__shfl(go, 0, kWave)) break;
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int i = lane + kWave * j;
+    if (i < n) merge(i, __builtin_bit_cast(f32x2, v[j]));
+  }
 }
 
 template <typename T, int D, int G, bool FORECAST>
@@ -131,15 +149,23 @@ struct Gang {
   static constexpr int RPI = kThreads / 4;        // representatives per load slot (64)
   static constexpr int U = kGangReps / RPI;       // slots per lane
   static constexpr int CBLK = kGangReps / kSubs;  // most blocks a member scores
+  // slots in flight per lane: 8 for one query slice, 4 when the slices of
+  // several heads already take many registers
+  static constexpr int USL = GS >= 2 ? 4 : 8;
+  static constexpr int QWORDS = G * D * (int)sizeof(T) / 4;  // attention queries, 32-bit words
+  static constexpr int QPT = (QWORDS + kThreads - 1) / kThreads;
+  static constexpr int NP = kMaxGang * G / kWave;  // (m, s) slots per lane when polling
 
   struct Smem {
     AttendSmem<T, D, G> att;
-    WgAcc<D, G> acc;
+    RadixSmem rad;
+    SmallTopSmem small;
     TopSmem top;
     float lgs[U][KEEP][kThreads];  // the logits, parked during attention
     float sM[G], sInvZ[G];
     float red_m[kWaves][4][KEEP], red_s[kWaves][4][KEEP];
     uint32_t ckeys[CBLK] __attribute__((aligned(16)));
+    f32x2 ml[G];
     int s_int[8];
   };
 
@@ -150,47 +176,86 @@ struct Gang {
     const int q = lane & 3, r = lane >> 2;
     const int b = row / a.Hkv, g = row % a.Hkv;
     const int C = a.C;
-    const int NS = a.S;              // members 0..NS-1 stream the representatives
-    const bool streamer = c < NS;    // the others attend the eviction set meanwhile
-    const int L = a.seq_lens[b];
+    const int L = sload(a.seq_lens, b);
     const int nb = min(L / kBlock, a.nb_max);
-    const int tail = L - nb * kBlock;
+    // the partial block (none when the row's table is full: a longer L is
+    // outside the call's contract and attends nothing past the table)
+    const int tail = nb < a.max_blocks ? min(L - nb * kBlock, kBlock - 1) : 0;
     const int nsub = nb * kSubs;
-    const int j0 = streamer ? min(c * a.per_wg, nsub) : nsub;
-    const int j1 = streamer ? min(j0 + a.per_wg, nsub) : nsub;
+    const int j0 = min(c * a.per_wg, nsub);
+    const int j1 = min(j0 + a.per_wg, nsub);
+    const int blk0 = j0 / kSubs, nblk = (j1 - j0) / kSubs;
     const int h0 = GS >= 4 ? q * KEEP : q / DUP;
     const bool canon = (q % DUP) == 0;
-    uint32_t* words = a.words + (int64_t)row * kGangWords;
-    int* eids = reinterpret_cast<int*>(dyn);                   // k_e: the eviction set
-    int* tbl = eids + (a.k_e > 0 ? a.k_e : 1);                 // nb_max + 1: the table row
-    uint32_t* scratch = reinterpret_cast<uint32_t*>(tbl) + a.tbl_words;  // per-phase scratch
-    const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+    int* eids = reinterpret_cast<int*>(dyn);                      // k_e: the eviction set
+    int* qsel = eids + (a.k_e > 0 ? a.k_e : 1);                   // k: query-aware blocks
+    uint32_t* scratch = reinterpret_cast<uint32_t*>(qsel + a.k);  // eviction update
+    const int64_t tb = (int64_t)b * a.max_blocks;                 // the row's table entries
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
     const T* kp = static_cast<const T*>(a.k_pool);
     const T* vp = static_cast<const T*>(a.v_pool);
+    uint32_t* err = a.err;
 
-    wg_acc_init(sm.acc);
+    // the attention queries, parked in shared memory below
+    uint32_t qw[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int w = threadIdx.x + i * kThreads;
+      qw[i] = w < QWORDS ? reinterpret_cast<const uint32_t*>(qrow)[w] : 0u;
+    }
 
-    // ---- the row's block table and eviction state, requested now and used
-    // after the streaming below (their latency overlaps it); the table goes
-    // straight to shared memory (64 entries per wave and instruction)
-    if (a.tbl_words > 0) {
-      // blocks 0..nb: the full ones and the tail's (which exists only when
-      // the row is not full)
-      const int last = min(nb, a.max_blocks - 1);
-      for (int base = wave * kWave; base <= last; base += kThreads)
-        if (base + lane <= last) __builtin_amdgcn_global_load_lds(trow + base + lane, tbl + base, 4, 0, 0);
+    // ---- the eviction set: in the steady state no block became full since
+    // the last call and the set is the caller's state as it stands; otherwise
+    // the k_e best of (old set U new blocks) by eviction score, ties to the
+    // lower id, computed below into eids
+    int seen = a.k_e > 0 ? sload(a.evict_seen, row) : 0;
+    if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
+    const bool steady = a.k_e == 0 || seen == nb;
+    const int nprev = min(a.k_e, seen);
+    const int n_e = a.k_e > 0 ? min(a.k_e, nprev + nb - seen) : 0;
+    const int n_eitems = n_e + (tail > 0);  // the eviction set, then the tail block
+    const int e_mine = c < n_eitems ? (n_eitems - c + C - 1) / C : 0;  // items c, c + C, ...
+    auto e_item = [&](int it) {  // item it of this member's share (scalar loads)
+      const int idx = c + it * C;
+      int blk = nb;  // the tail block
+      if (idx < n_e) {
+        const int v = steady ? sload(a.evict_set, (int64_t)row * a.k_e + idx) : eids[idx];
+        blk = min(max(v, 0), nb - 1);
+      }
+      Item x;
+      x.base = ((int64_t)sload(a.table, tb + blk) * a.Hkv + g) * (int64_t)(kBlock * D);
+      x.valid = idx < n_e ? kBlock : tail;
+      x.logits = nullptr;
+      return x;
+    };
+    auto e_issue = [&](Slab<T, D>& s, int it) { slab_issue<T, D, false>(s, e_item(it), kp, vp); };
+    // the caller's eviction set, to shared memory below (steady state; a
+    // bounded buffer load, so that no branch waits for it here)
+    const int ev_pre = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(a.evict_set + (int64_t)row * a.k_e, (uint32_t)(steady ? n_e * 4 : 0)),
+        (int)threadIdx.x * 4, 0, 0);
+
+    if (!steady) {
+      // blocks became full since the last call: update the set (once per
+      // filled block, before the stream so that no loads wait behind it)
+      uint32_t* ekeys = scratch;                                       // ncand
+      int* ev_old = reinterpret_cast<int*>(ekeys + a.k_e + a.nb_max);  // k_e
+      const int ncand = nprev + nb - seen;
+      for (int i = threadIdx.x; i < nprev; i += kThreads)
+        ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+      __syncthreads();
+      const float* Er = a.E + (int64_t)row * a.max_blocks;
+      for (int i = threadIdx.x; i < ncand; i += kThreads) {
+        const int id = i < nprev ? ev_old[i] : seen + i - nprev;
+        ekeys[i] = order_key(Er[id]);
+      }
+      __syncthreads();
+      if (n_e > 0)
+        wg_top_m(ekeys, ncand, n_e, sm.top, [&](int i, int pos) {
+          eids[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
+        });
+      __syncthreads();
     }
-    {
-      // the attention queries, G x D, 4 bytes per lane and instruction
-      constexpr int kWords = G * D * (int)sizeof(T) / 4;
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qrow);
-      uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
-      for (int base = wave * kWave; base < kWords; base += kThreads)
-        if (base + lane < kWords) __builtin_amdgcn_global_load_lds(qw + base + lane, ql + base, 4, 0, 0);
-    }
-    const int seen_pre = a.k_e > 0 ? a.evict_seen[row] : 0;
-    const int ev_pre = (int)threadIdx.x < a.k_e ? a.evict_set[(int64_t)row * a.k_e + threadIdx.x] : 0;
 
     // ---- 1. logits of this member's representatives, in registers
     float lg[U][KEEP];
@@ -199,16 +264,15 @@ struct Gang {
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) lg[u][kk] = -INFINITY;
     }
-    if (streamer) {
+    Slab<T, D> sa, sb;
+    Item e0{}, e1{};
+    {
       QSlice<T, D> qs[GS];
       const T* qb = static_cast<const T*>(a.query) +
                     (FORECAST ? (int64_t)row * D : ((int64_t)b * a.Hkv + g) * G * D);
 #pragma unroll
       for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
       const T* rb = static_cast<const T*>(a.reps) + (int64_t)row * a.max_blocks * kSubs * D;
-      // slots in flight per lane: 8 at small group sizes, 4 when the query
-      // slices of 4 or 8 heads already take many registers
-      constexpr int USL = GS >= 4 ? 4 : 8;
 #pragma unroll
       for (int u0 = 0; u0 < U; u0 += USL) {
         uint4 x[USL][NLD];
@@ -219,6 +283,20 @@ struct Gang {
           for (int ld = 0; ld < NLD; ++ld)
             x[uu][ld] = j < j1 ? load16_stream(rb + (int64_t)j * D + Q::elem(ld, q))
                                : make_uint4(0, 0, 0, 0);
+        }
+        if (u0 == 0) {
+          // the first two eviction-set items' addresses (their scalar loads
+          // overlap the stream), the set itself and the attention queries to
+          // shared memory
+          if (e_mine > 0) e0 = e_item(0);
+          if (e_mine > 1) e1 = e_item(1);
+          if (steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
+          uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
+#pragma unroll
+          for (int i = 0; i < QPT; ++i) {
+            const int w = threadIdx.x + i * kThreads;
+            if (w < QWORDS) ql[w] = qw[i];
+          }
         }
 #pragma unroll
         for (int uu = 0; uu < USL; ++uu) {
@@ -233,10 +311,15 @@ struct Gang {
         }
       }
     }
+    // the first two eviction-set slabs: in flight while the statistics are
+    // formed and published
+    if (e_mine > 0) slab_issue<T, D, false>(sa, e0, kp, vp);
+    if (e_mine > 1) slab_issue<T, D, false>(sb, e1, kp, vp);
 
     // ---- 2. softmax statistics of this member's logits (group softmax)
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
-    if (!FORECAST && streamer) {
+    const uint32_t st_off = (uint32_t)(((int64_t)row * kMaxGang) * G * 8);
+    if constexpr (!FORECAST) {
       float m[KEEP], s[KEEP];
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) {
@@ -250,12 +333,7 @@ struct Gang {
             for (int u = 0; u < U; ++u) s[kk] += exp2f(lg[u][kk] - m[kk]);
           }
         }
-#pragma unroll
-        for (int off = 4; off < kWave; off <<= 1) {
-          const float m2 = __shfl_xor(m[kk], off, kWave);
-          const float s2 = __shfl_xor(s[kk], off, kWave);
-          merge_ms(m[kk], s[kk], m2, s2);
-        }
+        merge_ms_lanes(m[kk], s[kk], 4);  // the lanes of this slot's head(s)
         if (r == 0) {
           sm.red_m[wave][q][kk] = m[kk];
           sm.red_s[wave][q][kk] = s[kk];
@@ -267,8 +345,7 @@ struct Gang {
         const int qq = G >= 4 ? h / KEEP : h * DUP, kk = G >= 4 ? h % KEEP : 0;
         float M = sm.red_m[0][qq][kk], S = sm.red_s[0][qq][kk];
         for (int w = 1; w < kWaves; ++w) merge_ms(M, S, sm.red_m[w][qq][kk], sm.red_s[w][qq][kk]);
-        store_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + c) * G + h) * 8),
-                          f32x2{M, S});
+        store_agent_f32x2(srs, st_off + (uint32_t)((c * G + h) * 8), f32x2{M, S});
       }
     }
     // the logits wait in shared memory while this member attends
@@ -277,91 +354,29 @@ struct Gang {
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) sm.lgs[u][kk][threadIdx.x] = lg[u][kk];
     }
+    __syncthreads();  // the queries and the eviction set are in shared memory
 
-    __builtin_amdgcn_s_waitcnt(0);  // the table and queries have landed, the statistics are out
-    __syncthreads();
-
-    // ---- 3. the eviction set: the k_e best of (old set U blocks that became
-    // full since the last call) by eviction score, ties to the lower id
-    int n_e = 0;
-    if (a.k_e > 0) {
-      int seen = seen_pre;
-      if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
-      const int nprev = min(a.k_e, seen);
-      const int ncand = nprev + nb - seen;
-      n_e = min(a.k_e, ncand);
-      auto old_id = [&](int i) {  // entry i of the old set, i < nprev
-        const int v = i < kThreads ? ev_pre : a.evict_set[(int64_t)row * a.k_e + i];
-        return min(max(v, 0), nb - 1);
-      };
-      if (seen == nb) {
-        for (int i = threadIdx.x; i < n_e; i += kThreads) eids[i] = old_id(i);
-      } else {
-        uint32_t* keys = scratch;                                       // ncand
-        int* ev_old = reinterpret_cast<int*>(keys + a.k_e + a.nb_max);  // k_e
-        for (int i = threadIdx.x; i < nprev; i += kThreads) ev_old[i] = old_id(i);
-        __syncthreads();
-        const float* Er = a.E + (int64_t)row * a.max_blocks;
-        for (int i = threadIdx.x; i < ncand; i += kThreads) {
-          const int id = i < nprev ? ev_old[i] : seen + i - nprev;
-          keys[i] = order_key(Er[id]);
-        }
-        __syncthreads();
-        if (n_e > 0)
-          wg_top_m(keys, ncand, n_e, sm.top, [&](int i, int pos) {
-            eids[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
-          });
-      }
+    // ---- the first two eviction-set items (loaded during the stream)
+    AttnState<T, D, G> att;
+    att.init();
+    if (e_mine > 0) {
+      att.consume(sa, sm.att, a.qscale_att);
+      if (e_mine > 2) e_issue(sa, 2);
     }
-    __syncthreads();
+    if (e_mine > 1) {
+      att.consume(sb, sm.att, a.qscale_att);
+      if (e_mine > 3) e_issue(sb, 3);
+    }
 
-    // ---- attention over this member's share of the eviction set + tail: the
-    // attenders take items (c - NS), (c - NS) + (C - NS), ... of [eviction
-    // set..., tail] at once; with no attenders every member takes items
-    // c, c + C, ..., part now and the rest after publishing its candidates
-    const int NA = C - NS;
-    const int e_rank = NA > 0 ? c - NS : c;
-    const int e_stride = NA > 0 ? NA : C;
-    auto e_item = [&](int it) {
-      const int idx = e_rank + it * e_stride;
-      const int blk = idx < n_e ? eids[idx] : nb;
-      const int64_t phys = a.tbl_words > 0 ? tbl[blk] : trow[blk];
-      Item x;
-      x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
-      x.valid = idx < n_e ? kBlock : tail;
-      x.logits = nullptr;
-      return x;
-    };
-    const int n_eitems = n_e + (tail > 0);
-    const int e_mine = (NA > 0 && streamer) || e_rank >= n_eitems
-                           ? 0 : (n_eitems - e_rank + e_stride - 1) / e_stride;
-    const int e_first = NA > 0 ? e_mine : (e_mine * a.e_first_pct + 99) / 100;
-    // the first slab's loads go out before the arrival ticket's round trip
-    Slab<T, D> pf;
-    if (e_first > 0) slab_issue<T, D, false>(pf, e_item(0), kp, vp);
-    if (!FORECAST && streamer) gang_ticket(words + 0, NS, &sm.s_int[0]);
-    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds, true>(
-        qrow, kp, vp, a.qscale_att, 0, e_first, e_item, sm.att, sm.acc, &pf);
-
-    // ---- 4. row normaliser from every member's statistics
-    uint32_t* err = a.err;
-    if (!FORECAST && streamer) {
-      gang_wait(words + 0, NS, err, a.wait_ticks);
-      if (threadIdx.x < kWave) {
+    // ---- 3. row normaliser from every member's statistics
+    const int m_row = max(0, min(a.k - n_e, nb - n_e));
+    if constexpr (!FORECAST) {
+      if (m_row > 0 && wave == 0) {
         // lane: members lane / G, + 64 / G, ...; head lane % G
         float M = -INFINITY, S = 0.f;
-        const int h = lane % G;
-        for (int m2 = lane / G; m2 < NS; m2 += kWave / G) {
-          const f32x2 st =
-              load_agent_f32x2(srs, (uint32_t)((((int64_t)row * kMaxGang + m2) * G + h) * 8));
-          merge_ms(M, S, st.x, st.y);
-        }
-#pragma unroll
-        for (int off = G; off < kWave; off <<= 1) {
-          const float m2 = __shfl_xor(M, off, kWave);
-          const float s2 = __shfl_xor(S, off, kWave);
-          merge_ms(M, S, m2, s2);
-        }
+        wave_poll_pairs<NP>(srs, st_off, C * G, err, a.wait_ticks,
+                            [&](int, f32x2 st) { merge_ms(M, S, st.x, st.y); });
+        merge_ms_lanes(M, S, G);
         if (lane < G) {
           sm.sM[lane] = M;
           sm.sInvZ[lane] = S > 0.f ? 1.f / S : 0.f;
@@ -369,19 +384,15 @@ struct Gang {
       }
     }
 
-    // the second eviction-set phase's first slab: its loads land during the
-    // scoring below
-    if (e_first < e_mine) slab_issue<T, D, false>(pf, e_item(e_first), kp, vp);
-    const int m_row = max(0, min(a.k - n_e, nb - n_e));
-    const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.cand, a.cand_bytes);
-    const int blk0 = j0 / kSubs;
-    if (streamer) {
-      // ---- 5. scores of this member's blocks; its best candidates
+    // ---- scores of this member's blocks, published as keys (+1)
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.keys, a.keys_bytes);
+    const uint32_t key_off = (uint32_t)((int64_t)row * a.nb_max * 4);
+    if (m_row > 0) {
       for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
       __syncthreads();
       for (int i = threadIdx.x; i < n_e; i += kThreads) {
         const int id = eids[i];
-        if (id >= blk0 && id < blk0 + CBLK) sm.ckeys[id - blk0] = 0u;
+        if (id >= blk0 && id < blk0 + nblk) sm.ckeys[id - blk0] = 0u;
       }
       __syncthreads();
 #pragma unroll
@@ -407,109 +418,143 @@ struct Gang {
         }
       }
       __syncthreads();
-
-      // this member's best mc blocks (ties to the lower id) fill slots
-      // 0..mc-1 of its list in block order; the remaining slots get an empty
-      // entry
-      if (threadIdx.x < kWave) {
-        const int64_t cbase = ((int64_t)row * kMaxGang + c) * a.mloc_max;
-        int nz = 0;
-#pragma unroll
-        for (int j = 0; j < CBLK / kWave; ++j) nz += __popcll(__ballot(sm.ckeys[j * kWave + lane] != 0u));
-        const int mc = min(min(m_row, nz), a.mloc);
-        if (mc > 0) {
-          int take_eq;
-          const uint32_t thr = wave_kth_key<CBLK / kWave>(sm.ckeys, CBLK, mc, &take_eq);
-          wave_emit_top(sm.ckeys, CBLK, thr, take_eq, [&](int i, int pos) {
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{sm.ckeys[i], (uint32_t)(blk0 + i)}, cr,
-                                                  (int)((cbase + pos) * 8), 0, kSC1);
-          });
-        }
-        for (int i = mc + lane; i < a.mloc; i += kWave)
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, cr, (int)((cbase + i) * 8), 0, kSC1);
-      }
-      gang_arrive(words + 1, NS, &sm.s_int[1]);
+      if ((int)threadIdx.x < nblk)
+        __builtin_amdgcn_raw_buffer_store_b32(sm.ckeys[threadIdx.x] + 1u, krs,
+                                              (int)(key_off + (blk0 + threadIdx.x) * 4), 0, kSC1);
     }
 
     // ---- the rest of this member's eviction-set share
-    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds, true>(
-        qrow, kp, vp, a.qscale_att, e_first, e_mine, e_item, sm.att, sm.acc, &pf);
-
-    // ---- 6. the row's query-aware set from every member's candidates
-    gang_wait(words + 1, NS, err, a.wait_ticks);
-    const int ncand = NS * a.mloc;
-    uint32_t* ckey = scratch;                                 // ncand
-    int* cid = reinterpret_cast<int*>(ckey + ncand);          // ncand
-    int* qsel = cid + ncand;                                  // k
-    uint8_t* flags = reinterpret_cast<uint8_t*>(qsel + a.k);  // nb_max
-    for (int i = threadIdx.x; i < ncand; i += kThreads) {
-      const int m2 = i / a.mloc, s = i % a.mloc;
-      const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(
-          cr, (int)(((((int64_t)row * kMaxGang + m2) * a.mloc_max) + s) * 8), 0, kSC1);
-      ckey[i] = e.x;
-      cid[i] = (int)e.y;
-    }
-    if (c == 0)
-      for (int i = threadIdx.x; i < nb; i += kThreads) flags[i] = 0;
-    __syncthreads();
-    if (m_row > 0)
-      wg_top_m(ckey, ncand, m_row, sm.top, [&](int i, int pos) { qsel[pos] = cid[i]; });
-
-    if (c == 0) {
-      // the caller's outputs: eviction state and the selected ids, ascending
-      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
-        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
-      if (threadIdx.x == 0 && a.k_e > 0) a.evict_seen[row] = nb;
-      for (int i = threadIdx.x; i < m_row; i += kThreads) flags[qsel[i]] = 1;
-      for (int i = threadIdx.x; i < n_e; i += kThreads) flags[eids[i]] = 1;
-      __syncthreads();
-      if (threadIdx.x < kWave) {
-        int32_t* out = a.selected + (int64_t)row * a.k;
-        int taken = 0;
-        const uint64_t below = (1ull << lane) - 1ull;
-        for (int base = 0; base < nb; base += 8 * kWave) {
-          bool f[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int i = base + jj * kWave + lane;
-            f[jj] = i < nb && flags[i];
-          }
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const uint64_t bm = __ballot(f[jj]);
-            if (f[jj]) out[taken + __popcll(bm & below)] = base + jj * kWave + lane;
-            taken += __popcll(bm);
-          }
-        }
-        for (int i = taken + lane; i < a.k; i += kWave) out[i] = -1;
-        if (lane == 0) a.num_selected[row] = taken;
+    for (int it = 2; it < e_mine; it += 2) {
+      att.consume(sa, sm.att, a.qscale_att);
+      if (it + 2 < e_mine) e_issue(sa, it + 2);
+      if (it + 1 < e_mine) {
+        att.consume(sb, sm.att, a.qscale_att);
+        if (it + 3 < e_mine) e_issue(sb, it + 3);
       }
     }
 
-    // ---- attention over this member's share of the query-aware set
-    auto q_item = [&](int it) {
-      const int blk = qsel[c + it * C];
-      const int64_t phys = a.tbl_words > 0 ? tbl[blk] : trow[blk];
+    // ---- 4. the row's query-aware set from every member's keys, ascending
+    if (m_row > 0) {
+      // every member's keys (polled until none is missing), in registers for
+      // rows of up to kSmallKpt * kThreads blocks and in shared memory
+      constexpr int kSmallKpt = 8;
+      uint32_t* rkeys = scratch;  // nb
+      uint32_t kv[kSmallKpt];
+      Patience pt{0, false};
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < kSmallKpt; ++j) {
+          const int i = threadIdx.x + kThreads * j;
+          kv[j] = i < nb ? __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1)
+                         : 0u;
+          ok &= i >= nb || kv[j] != 0u;
+          if (i < nb) rkeys[i] = kv[j];
+        }
+        for (int i = threadIdx.x + kThreads * kSmallKpt; i < nb; i += kThreads) {
+          const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
+          rkeys[i] = v;
+          ok &= v != 0u;
+        }
+        const bool wave_ok = __all(ok);
+        if (lane == 0) sm.s_int[wave] = wave_ok;
+        __syncthreads();
+        const bool all = sm.s_int[0] && sm.s_int[1] && sm.s_int[2] && sm.s_int[3];
+        if (threadIdx.x == 0) sm.s_int[4] = all ? 0 : (int)pt.more(err, a.wait_ticks);
+        __syncthreads();
+        const bool again = !all && sm.s_int[4];
+        __syncthreads();  // every thread has read s_int before it is written again
+        if (!again) break;  // uniform
+      }
+      auto put = [&](int i, int pos) {
+        if (pos < m_row) qsel[pos] = i;
+      };
+      bool done = false;
+      if (nb <= kSmallKpt * kThreads) done = wg_top_small<kSmallKpt>(kv, m_row, sm.small, put);
+      if (!done) {
+        uint32_t P;
+        int shift, take_eq;
+        wg_radix_top(rkeys, nb, m_row, sm.rad, &P, &shift, &take_eq);
+        wg_radix_emit(rkeys, nb, P, shift, take_eq, sm.rad, put);
+      }
+      __syncthreads();
+    }
+
+    // ---- attention over this member's share of the query-aware set:
+    // positions c, c + C, ... of the ascending list
+    const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
+    auto q_issue = [&](Slab<T, D>& s, int it) {
+      const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * C]), 0), nb - 1);
       Item x;
-      x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
+      x.base = ((int64_t)sload(a.table, tb + blk) * a.Hkv + g) * (int64_t)(kBlock * D);
       x.valid = kBlock;
       x.logits = nullptr;
-      return x;
+      slab_issue<T, D, false>(s, x, kp, vp);
     };
-    const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
-    attend_items_merge<T, D, G, false, kGangBuf, kGangQLds>(qrow, kp, vp, a.qscale_att, 0, q_mine, q_item, sm.att,
-                                       sm.acc);
+    if (q_mine > 0) q_issue(sa, 0);
+    if (q_mine > 1) q_issue(sb, 1);
+    for (int it = 0; it < q_mine; it += 2) {
+      att.consume(sa, sm.att, a.qscale_att);
+      if (it + 2 < q_mine) q_issue(sa, it + 2);
+      if (it + 1 < q_mine) {
+        att.consume(sb, sm.att, a.qscale_att);
+        if (it + 3 < q_mine) q_issue(sb, it + 3);
+      }
+    }
 
-    // ---- 7. partials; the last member merges them into the output
+    // ---- 5. this member's partial; member 0 merges the row
     const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
     const __amdgpu_buffer_rsrc_t acr = make_rsrc(a.part_acc, a.acc_bytes);
+    att.to_lds(sm.att);
+    wg_publish_partial(sm.att, sm.ml, mlr, acr, (int64_t)row * kMaxGang + c);
+    if (c != 0) return;
+
+    if (wave == 0)
+      wave_poll_pairs<NP>(mlr, st_off, C * G, err, a.wait_ticks, [&](int, f32x2) {});
     __syncthreads();
-    wg_acc_store(sm.acc, mlr, acr, (int64_t)row * kMaxGang + c);
-    if (!gang_arrive(words + 2, C, &sm.s_int[2])) return;
     T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
     combine_partials<T, D, G>((int64_t)row * kMaxGang, C, mlr, acr, out);
-    // every member has passed every wait of this row: reset its words
-    if (threadIdx.x < kGangWords) st_agent(words + threadIdx.x, 0u);
+
+    // the caller's outputs: eviction state (when it changed) and the selected
+    // ids, ascending (the eviction set and the query-aware list are each
+    // ascending and disjoint: each id goes after the smaller ids of the other
+    // list)
+    if (!steady) {
+      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
+        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
+      if (threadIdx.x == 0) a.evict_seen[row] = nb;
+    }
+    int32_t* sel = a.selected + (int64_t)row * a.k;
+    auto below = [](const int* v, int n, int id) {  // entries < id of ascending v[0..n)
+      int lo = 0;
+      while (n > 0) {
+        const int half = n >> 1;
+        if (v[lo + half] < id) {
+          lo += half + 1;
+          n -= half + 1;
+        } else {
+          n = half;
+        }
+      }
+      return lo;
+    };
+    for (int t = threadIdx.x; t < n_e + m_row; t += kThreads) {
+      const bool ev = t < n_e;
+      const int id = ev ? eids[t] : qsel[t - n_e];
+      sel[(ev ? t : t - n_e) + (ev ? below(qsel, m_row, id) : below(eids, n_e, id))] = id;
+    }
+    for (int t = n_e + m_row + threadIdx.x; t < a.k; t += kThreads) sel[t] = -1;
+    if (threadIdx.x == 0) a.num_selected[row] = n_e + m_row;
+
+    // every member has read every slot of the row: clear them
+    if (!FORECAST)
+      for (int i = threadIdx.x; i < C * G; i += kThreads)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, srs, (int)(st_off + i * 8), 0, kSC1);
+    if (m_row > 0)
+      for (int i = threadIdx.x; i < nb; i += kThreads)
+        __builtin_amdgcn_raw_buffer_store_b32(0u, krs, (int)(key_off + i * 4), 0, kSC1);
+    for (int i = threadIdx.x; i < C * G; i += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, mlr, (int)(st_off + i * 8), 0, kSC1);
   }
 };
 
@@ -538,13 +583,11 @@ template <typename T, int D, int G, bool FORECAST>
 hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   const StepLayout& lay = L.lay;
   const void* fn = reinterpret_cast<const void*>(gang_kernel<T, D, G, FORECAST>);
-  // capacity with the shared memory of the largest gang, then the plan
   GridInfo gi;
-  hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e, kMaxGang), &gi);
+  hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e), &gi);
   if (e != hipSuccess) return e;
   GangPlan plan;
-  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, L.streamer_override,
-                 &plan))
+  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, &plan))
     return hipErrorLaunchOutOfResources;
   GangArgs a{};
   a.query = L.query;
@@ -562,9 +605,8 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.out = L.out;
   char* ws = static_cast<char*>(L.workspace);
   a.err = reinterpret_cast<uint32_t*>(ws) + kErr;
-  a.words = reinterpret_cast<uint32_t*>(ws + lay.off_words);
   a.stats = reinterpret_cast<float*>(ws + lay.off_stats);
-  a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
+  a.keys = reinterpret_cast<uint32_t*>(ws + lay.off_keys);
   a.part_ml = reinterpret_cast<float*>(ws + lay.off_ml);
   a.part_acc = reinterpret_cast<float*>(ws + lay.off_acc);
   a.rows = lay.rows;
@@ -574,20 +616,15 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.k = L.k;
   a.k_e = L.k_e;
   a.C = plan.C;
-  a.S = plan.S;
   a.gangs = plan.gangs;
   a.per_wg = plan.per_wg;
-  a.mloc = plan.mloc;
-  a.mloc_max = lay.mloc_max;
-  a.tbl_words = gang_tbl_words(lay);
-  a.e_first_pct = L.e_first_pct;
   a.qscale_sel = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;
   a.qscale_att = L.scale * 1.4426950408889634f;
   a.wait_ticks = (uint64_t)(gi.wall_khz > 0 ? gi.wall_khz : 1) * kWaitMs;
-  a.stats_bytes = (uint32_t)(lay.off_cand - lay.off_stats);
-  a.cand_bytes = (uint32_t)(lay.off_ml - lay.off_cand);
+  a.stats_bytes = (uint32_t)(lay.off_ml - lay.off_stats);
   a.ml_bytes = (uint32_t)(lay.off_acc - lay.off_ml);
-  a.acc_bytes = (uint32_t)(lay.bytes - lay.off_acc);
+  a.acc_bytes = (uint32_t)(lay.off_keys - lay.off_acc);
+  a.keys_bytes = (uint32_t)(lay.bytes - lay.off_keys);
   gang_kernel<T, D, G, FORECAST><<<plan.gangs * plan.C, kThreads, plan.dyn_lds, stream>>>(a);
   return hipGetLastError();
 }

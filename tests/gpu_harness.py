@@ -93,9 +93,12 @@ def prefill(layer, cfg: W.Config) -> None:
     layer.update_reps(first, num, nb0)
 
 
-def run_step(layer, cfg: W.Config, step: int, seq_lens=None, fused: bool = False) -> None:
+def run_step(layer, cfg: W.Config, step: int, seq_lens=None, fused: bool = False,
+             max_seq_len: int | None = None) -> None:
     """One decode step: (the token is already in the pool) reps of a block
-    that just filled, then select and decode (two calls, or the fused one)."""
+    that just filled, then select and decode (two calls, or the fused one).
+    max_seq_len: the bound passed to the fused call (default: the longest
+    sequence of the step)."""
     dev = layer.device
     L = cfg.seq_len(step)
     lens = np.full(cfg.batch, L, dtype=np.int32) if seq_lens is None else seq_lens
@@ -106,7 +109,8 @@ def run_step(layer, cfg: W.Config, step: int, seq_lens=None, fused: bool = False
         num = torch.from_numpy(filled.astype(np.int32)).to(dev)
         layer.update_reps(first, num, 1)
     if fused:
-        layer.step(device_query(cfg, step), device_q(cfg, step), int(lens.max()))
+        bound = int(lens.max()) if max_seq_len is None else max_seq_len
+        layer.step(device_query(cfg, step), device_q(cfg, step), bound)
         return
     layer.select(device_query(cfg, step), int(lens.max()))
     layer.decode(device_q(cfg, step))
@@ -116,6 +120,21 @@ def step_error_word(layer) -> int:
     """The fused step's sticky error word (workspace word 2)."""
     torch.cuda.synchronize()
     return int(layer.step_ws[8:12].view(torch.int32).item())
+
+
+def step_slot_words(layer, cfg: W.Config) -> torch.Tensor:
+    """The fused step's hand-off slots (member statistics, partial (m, l) and
+    row keys) as 32-bit words: all zero between calls.  The layout is the
+    library's: [256-byte control | stats | (m, l) | acc | keys], member slots
+    for 64 members per row, each region 256-byte aligned."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    members = cfg.rows * 64
+    off_ml = up(256 + members * cfg.group * 8)
+    off_acc = up(off_ml + members * cfg.group * 8)
+    off_keys = up(off_acc + members * cfg.group * cfg.head_dim * 4)
+    ws = layer.step_ws[:layer.step_ws_bytes]
+    return torch.cat([ws[256:off_acc], ws[off_keys:]]).view(torch.int32)
 
 
 @dataclass
@@ -249,8 +268,9 @@ def stop_ratio_near_tau(q, orow, order, L, tau, n) -> bool:
 
 
 def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, row_inputs=None,
-                  fused: bool = False):
-    """Prefill + every decode step of cfg; compare sampled rows each step."""
+                  fused: bool = False, max_len=None):
+    """Prefill + every decode step of cfg; compare sampled rows each step.
+    max_len: step -> max_seq_len of the fused call (default: the step's)."""
     log(f"[case] {cfg.name}: B={cfg.batch} ctx={cfg.context} Hq={cfg.num_q_heads} "
           f"Hkv={cfg.num_kv_heads} D={cfg.head_dim} {cfg.dtype} {cfg.mode} k={cfg.k} "
           f"k_e={cfg.k_e} ordered={cfg.ordered} steps={cfg.steps} fused={fused}")
@@ -265,7 +285,7 @@ def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, ro
     prev = {r: None for r in rows}
     stats = {"gamma_min": 1.0, "n_star": []}
     for t in range(cfg.steps):
-        run_step(layer, cfg, t, fused=fused)
+        run_step(layer, cfg, t, fused=fused, max_seq_len=None if max_len is None else max_len(t))
         if fused:
             assert step_error_word(layer) == 0, f"a stage wait expired at step {t}"
         if t % check_every and t != cfg.steps - 1:

@@ -86,27 +86,52 @@ def test_step_gang_sizes(gang, monkeypatch):
     H.run_and_check(cfg, rows=H.sample_rows(cfg, 5), fused=True)
 
 
-@pytest.mark.parametrize("gang,streamers", [("5", "2"), ("16", "9")])
-def test_step_attending_members(gang, streamers, monkeypatch):
-    """Gangs whose last members attend the eviction set while the others
-    stream and score give the oracle's answer."""
-    cfg = W.Config("step-roles", 75, batch=2, context=64 * 300 + 5, num_q_heads=8,
+def test_step_rows_beyond_2048_blocks():
+    """Rows of 2600 full blocks: every thread takes several of the row's keys
+    in the radix select, and the gang has many members."""
+    cfg = W.Config("step-long-rows", 78, batch=1, context=64 * 2600 + 11, num_q_heads=8,
                    num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=40,
                    k_e=24, steps=2)
-    monkeypatch.setenv("NSA_STEP_GANG", gang)
-    monkeypatch.setenv("NSA_STEP_STREAMERS", streamers)
     H.run_and_check(cfg, fused=True)
 
 
-@pytest.mark.parametrize("efirst", ["1", "100"])
-def test_step_eviction_attention_split(efirst, monkeypatch):
-    """The eviction-set attention split before / after the normaliser wait
-    does not change the result beyond fp32 rounding."""
-    cfg = W.Config("step-efirst", 74, batch=2, context=64 * 200 + 9, num_q_heads=8,
+def test_step_one_workspace_across_max_seq_len():
+    """One workspace, calls whose max_seq_len changes (the per-row key slots
+    change stride): every call still gives the oracle's answer."""
+    cfg = W.Config("step-maxlen", 79, batch=3, context=64 * 150 + 60, num_q_heads=8,
                    num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=24,
-                   k_e=16, steps=2)
-    monkeypatch.setenv("NSA_STEP_EFIRST", efirst)
-    H.run_and_check(cfg, fused=True)
+                   k_e=16, steps=6)
+    cap = 64 * cfg.max_blocks
+    bounds = [cfg.seq_len(0), cap, cfg.seq_len(2), cap, cfg.seq_len(4) + 64 * 3, cfg.seq_len(5)]
+    H.run_and_check(cfg, fused=True, max_len=lambda t: min(bounds[t], cap))
+
+
+def test_step_equal_scores_take_the_lowest_ids():
+    """Every key equal, so every block scores the same: the query-aware part is
+    the lowest-numbered blocks outside the eviction set (ties to the lower
+    id), and the fused call agrees with the two calls."""
+    cfg = W.Config("step-ties", 76, batch=2, context=64 * 600 + 5, num_q_heads=8, num_kv_heads=2,
+                   head_dim=128, dtype="bf16", mode="group_softmax", k=40, k_e=24, steps=1)
+    H.log("[case] fused step, all keys equal")
+    batch = W.build_batch(cfg)
+    batch.k_pool[...] = batch.k_pool.reshape(-1)[1]
+    split, fused = H.make_layer(cfg, batch), H.make_layer(cfg, batch)
+    H.prefill(split, cfg)
+    H.prefill(fused, cfg)
+    H.run_step(split, cfg, 0)
+    H.run_step(fused, cfg, 0, fused=True)
+    assert H.step_error_word(fused) == 0
+    rs, rf = H.fetch(split), H.fetch(fused)
+    nb = cfg.seq_len(0) // 64
+    assert np.array_equal(rs.evict_set, rf.evict_set)
+    for b in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            ev = set(int(x) for x in rf.evict_set[b, g, :cfg.k_e])
+            sel = [int(x) for x in rf.selected[b, g, :rf.num_selected[b, g]]]
+            want_q = [i for i in range(nb) if i not in ev][:cfg.k - cfg.k_e]
+            assert sorted(set(sel) - ev) == want_q, (b, g)
+            assert np.array_equal(rs.selected[b, g], rf.selected[b, g]), (b, g)
+    assert np.abs(rs.out - rf.out).max() <= 1e-2
 
 
 @pytest.mark.parametrize("k,k_e", [(8, 4), (8, 8), (8, 0)])
@@ -163,10 +188,10 @@ def _two_layers(cfg):
     return a, b
 
 
-def test_step_agrees_with_two_calls_and_resets_counters():
+def test_step_agrees_with_two_calls_and_clears_its_slots():
     """Same selection and eviction state as select + decode; outputs within
-    one bf16 rounding where the sets agree; the per-row arrival words back at
-    zero after every call (so the next call needs no clearing)."""
+    one bf16 rounding where the sets agree; the hand-off slots back at zero
+    after every call (so the next call needs no clearing)."""
     cfg = W.Config("step-vs-split", 71, batch=3, context=64 * 200 + 9, num_q_heads=8,
                    num_kv_heads=2, head_dim=128, dtype="bf16", mode="group_softmax", k=24,
                    k_e=16, steps=70)
@@ -177,9 +202,8 @@ def test_step_agrees_with_two_calls_and_resets_counters():
         H.run_step(split, cfg, t)
         H.run_step(fused, cfg, t, fused=True)
         assert H.step_error_word(fused) == 0
-        words = fused.step_ws[:fused.step_ws_bytes].view(torch.int32)
-        arrivals = words[64:64 + 3 * cfg.rows]  # per row: statistics, candidates, partials
-        assert int(arrivals.abs().sum()) == 0, "arrival words not reset"
+        slots = H.step_slot_words(fused, cfg)
+        assert int(torch.count_nonzero(slots)) == 0, "hand-off slots not cleared"
         rs, rf = H.fetch(split), H.fetch(fused)
         assert np.array_equal(rs.evict_set, rf.evict_set)
         for b in range(cfg.batch):
