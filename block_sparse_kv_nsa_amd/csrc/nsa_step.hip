@@ -149,9 +149,9 @@ struct Gang {
   static constexpr int RPI = kThreads / 4;        // representatives per load slot (64)
   static constexpr int U = kGangReps / RPI;       // slots per lane
   static constexpr int CBLK = kGangReps / kSubs;  // most blocks a member scores
-  // slots in flight per lane: 8 for one query slice, 4 when the slices of
-  // several heads already take many registers
-  static constexpr int USL = GS >= 2 ? 4 : 8;
+  // slots per batch (two batches in flight): 4 for one query slice, 2 when
+  // the slices of several heads already take many registers
+  static constexpr int USL = GS >= 2 ? 2 : 4;
   static constexpr int QWORDS = G * D * (int)sizeof(T) / 4;  // attention queries, 32-bit words
   static constexpr int QPT = (QWORDS + kThreads - 1) / kThreads;
   static constexpr int NP = kMaxGang * G / kWave;  // (m, s) slots per lane when polling
@@ -213,10 +213,14 @@ struct Gang {
     const bool steady = a.k_e == 0 || seen == nb;
     const int nprev = min(a.k_e, seen);
     const int n_e = a.k_e > 0 ? min(a.k_e, nprev + nb - seen) : 0;
-    const int n_eitems = n_e + (tail > 0);  // the eviction set, then the tail block
-    const int e_mine = c < n_eitems ? (n_eitems - c + C - 1) / C : 0;  // items c, c + C, ...
+    // this member's items: cr, cr + C, ... of [eviction set..., tail block],
+    // counted from the last member so that member 0, which also merges the
+    // row, never has more than the others
+    const int n_eitems = n_e + (tail > 0);
+    const int cr = C - 1 - c;
+    const int e_mine = cr < n_eitems ? (n_eitems - cr + C - 1) / C : 0;
     auto e_item = [&](int it) {  // item it of this member's share (scalar loads)
-      const int idx = c + it * C;
+      const int idx = cr + it * C;
       int blk = nb;  // the tail block
       if (idx < n_e) {
         const int v = steady ? sload(a.evict_set, (int64_t)row * a.k_e + idx) : eids[idx];
@@ -273,9 +277,10 @@ struct Gang {
 #pragma unroll
       for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
       const T* rb = static_cast<const T*>(a.reps) + (int64_t)row * a.max_blocks * kSubs * D;
-#pragma unroll
-      for (int u0 = 0; u0 < U; u0 += USL) {
-        uint4 x[USL][NLD];
+      // two batches of USL slots in flight: the next batch is requested
+      // before the current one is consumed, so the requests of the two
+      // workgroups sharing a compute unit interleave finely
+      auto issue = [&](uint4 (&x)[USL][NLD], int u0) {
 #pragma unroll
         for (int uu = 0; uu < USL; ++uu) {
           const int j = j0 + (u0 + uu) * RPI + wave * 16 + r;
@@ -284,20 +289,8 @@ struct Gang {
             x[uu][ld] = j < j1 ? load16_stream(rb + (int64_t)j * D + Q::elem(ld, q))
                                : make_uint4(0, 0, 0, 0);
         }
-        if (u0 == 0) {
-          // the first two eviction-set items' addresses (their scalar loads
-          // overlap the stream), the set itself and the attention queries to
-          // shared memory
-          if (e_mine > 0) e0 = e_item(0);
-          if (e_mine > 1) e1 = e_item(1);
-          if (steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
-          uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
-#pragma unroll
-          for (int i = 0; i < QPT; ++i) {
-            const int w = threadIdx.x + i * kThreads;
-            if (w < QWORDS) ql[w] = qw[i];
-          }
-        }
+      };
+      auto consume = [&](const uint4 (&x)[USL][NLD], int u0) {
 #pragma unroll
         for (int uu = 0; uu < USL; ++uu) {
           const int j = j0 + (u0 + uu) * RPI + wave * 16 + r;
@@ -309,6 +302,30 @@ struct Gang {
           for (int kk = 0; kk < KEEP; ++kk)
             lg[u0 + uu][kk] = j < j1 ? v[kk] * a.qscale_sel : -INFINITY;
         }
+      };
+      uint4 xa[USL][NLD], xb[USL][NLD];
+      issue(xa, 0);
+      {
+        // the first two eviction-set items' addresses (their scalar loads
+        // overlap the stream), the set itself and the attention queries to
+        // shared memory
+        if (e_mine > 0) e0 = e_item(0);
+        if (e_mine > 1) e1 = e_item(1);
+        if (steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
+        uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const int w = threadIdx.x + i * kThreads;
+          if (w < QWORDS) ql[w] = qw[i];
+        }
+      }
+      static_assert(U % (2 * USL) == 0, "slots per lane");
+#pragma unroll
+      for (int u0 = 0; u0 < U; u0 += 2 * USL) {
+        issue(xb, u0 + USL);
+        consume(xa, u0);
+        if (u0 + 2 * USL < U) issue(xa, u0 + 2 * USL);
+        consume(xb, u0 + USL);
       }
     }
     // the first two eviction-set slabs: in flight while the statistics are
@@ -546,7 +563,9 @@ struct Gang {
     for (int t = n_e + m_row + threadIdx.x; t < a.k; t += kThreads) sel[t] = -1;
     if (threadIdx.x == 0) a.num_selected[row] = n_e + m_row;
 
-    // every member has read every slot of the row: clear them
+    // every member has read every slot of the row, and this workgroup's
+    // merge (a subset of its waves) is done with the partials: clear them
+    __syncthreads();
     if (!FORECAST)
       for (int i = threadIdx.x; i < C * G; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, srs, (int)(st_off + i * 8), 0, kSC1);
