@@ -226,7 +226,7 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  * writes them; out as nsa_sparse_decode writes it).  The computation is
  * identical; the schedule differs: each row is handled by a gang of
  * workgroups that score their shares of the row's blocks, exchange softmax
- * statistics and candidates, and attend shares of the selected blocks; the
+ * statistics and block keys, and attend shares of the selected blocks; the
  * eviction set depends on the eviction scores only (NOSA summary, "Mecanismo
  * de Doble Seleccion"), so attention over it proceeds while the query-aware
  * part is still being scored and selected.
@@ -236,11 +236,14 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  * The grid is sized to the workgroups the device holds at once and the
  * members of a gang wait for one another, so the call expects the device's
  * compute units to itself while it runs (work on other streams can stall a
- * gang).  Every wait is bounded: the workspace follows the select
- * workspace's counter rule (zero before its first use; left zero by every
- * completed call), except for 32-bit word 2 (bytes 8-11), an error word,
+ * gang).  The workspace must be zero before its first use; every completed
+ * call leaves its hand-off slots zero again (partial accumulators may keep
+ * data, which is never read as a slot), so it is zeroed only once, and one
+ * workspace serves calls with any max_seq_len up to the one it was sized for.
+ * Every wait is bounded: 32-bit word 2 (bytes 8-11) is an error word,
  * sticky, set nonzero when a wait expired (results of such a call are
- * undefined; the two-call path gives them without the assumption).
+ * undefined, and the workspace must be zeroed again before the next call;
+ * the two-call path gives the results without the residency assumption).
  * max_seq_len is limited to 524288 tokens (NSA_ERR_UNSUPPORTED above).
  * ------------------------------------------------------------------------ */
 nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
