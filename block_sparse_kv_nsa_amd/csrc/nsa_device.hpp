@@ -398,17 +398,20 @@ __device__ __attribute__((always_inline)) inline void wg_radix_top(const uint32_
 // keys come near them: kv[j] is the key of index t + kThreads * j (0 past the
 // end; keys <= 1 are not candidates).  Every 16-lane row's largest candidate
 // is >= T0, the least of the 16 row maxima, so at least 16 candidates are
-// >= T0 and the m largest are among them.  Those (at most 64, else the call
-// declines) are gathered in index order and ranked by (key descending, index
-// ascending); emit(index, rank in index order) for the m best.  Returns false
-// without emitting when it declines (m > 16, a row without candidates, or
-// more than 64 keys >= T0, e.g. many equal scores).  Called by all threads.
+// >= T0 and the m largest are among them.  Those (at most kSmallCap, else the
+// call declines) are gathered in index order; thread t ranks gathered key t
+// by (key descending, index ascending) against all of them, and the m best
+// are emitted with emit(index, rank in index order).  Returns false without
+// emitting when it declines (m > 16, a row without candidates, or more than
+// kSmallCap keys >= T0: many equal scores).  Called by all threads.
+constexpr int kSmallCap = kThreads;
+
 struct SmallTopSmem {
-  uint32_t ck[64 + kThreads];  // the gathered keys, then one unused slot per thread
-  int cid[64 + kThreads];
+  uint32_t ck[kSmallCap + kThreads];  // the gathered keys, then one unused slot per thread
+  int cid[kSmallCap + kThreads];
   uint32_t gmin[kWaves];
   uint32_t cnt[kWaves][kRadixChunks];
-  int rk[kWaves][64];
+  int nsel[kWaves];
 };
 
 template <int KPT, typename Emit>
@@ -452,32 +455,35 @@ __device__ __attribute__((always_inline)) bool wg_top_small(const uint32_t (&kv)
     run += c0 + c1 + c2 + c3;
     const bool c = kv[j] >= t0;
     int p = base + __popcll(__ballot(c) & below);
-    p = (c && p < 64) ? p : 64 + (int)threadIdx.x;
+    p = (c && p < kSmallCap) ? p : kSmallCap + (int)threadIdx.x;
     ss.ck[p] = kv[j];
     ss.cid[p] = (int)threadIdx.x + kThreads * j;
   }
   const int total = run;  // uniform
-  if (total > 64) return false;
+  if (total > kSmallCap) return false;
   __syncthreads();
-  // rank among the gathered: wave w compares every key with keys 16w..16w+15
-  {
-    const uint32_t k = ss.ck[lane];
-    int part = 0;
+  // rank of gathered key t among all gathered keys, 16 per step
+  const int t = (int)threadIdx.x;
+  const uint32_t k = ss.ck[t];
+  int rank = 0;
+  for (int j0 = 0; j0 < total; j0 += 16) {
+    uint32_t kj[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) kj[jj] = ss.ck[j0 + jj];
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * wave + jj;
-      const uint32_t kj = ss.ck[j];
-      part += (j < total) & ((kj > k) | ((kj == k) & (j < lane)));
+      const int j = j0 + jj;
+      rank += (j < total) & ((kj[jj] > k) | ((kj[jj] == k) & (j < t)));
     }
-    ss.rk[wave][lane] = part;
   }
+  const bool sel = t < total && rank < m;
+  const uint64_t bs = __ballot(sel);
+  if (lane == 0) ss.nsel[wave] = __popcll(bs);
   __syncthreads();
-  if (wave == 0) {
-    const int rank = ss.rk[0][lane] + ss.rk[1][lane] + ss.rk[2][lane] + ss.rk[3][lane];
-    const bool sel = lane < total && rank < m;
-    const uint64_t bs = __ballot(sel);
-    if (sel) emit(ss.cid[lane], __popcll(bs & below));
-  }
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) base += w < wave ? ss.nsel[w] : 0;
+  if (sel) emit(ss.cid[t], base + __popcll(bs & below));
   return true;
 }
 

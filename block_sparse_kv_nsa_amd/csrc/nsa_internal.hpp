@@ -204,6 +204,7 @@ inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e) {
 
 struct GangPlan {
   int C, gangs, per_wg;
+  int split;  // gangs split across the two workgroup slots of the compute units
   size_t dyn_lds;
 };
 
@@ -211,8 +212,8 @@ struct GangPlan {
 // rows (at most kMaxGang), and at least enough to hold the longest row's
 // representatives in registers (kGangReps per member).  Rows beyond the
 // resident gangs are taken in turn.
-inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int c_override,
-                      GangPlan* p) {
+inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int per_cu,
+                      int c_override, GangPlan* p) {
   const int nsub = 4 * lay.nb_max;
   const int c_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
   const int c_cap = capacity < kMaxGang ? capacity : kMaxGang;
@@ -225,6 +226,9 @@ inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int c
   const int per = nsub > 0 ? (nsub + C - 1) / C : 4;
   p->per_wg = (int)round_up((size_t)per, 4);
   p->dyn_lds = gang_dyn_lds(lay, k, k_e);
+  // Split gangs when the grid fills exactly two workgroups per compute unit
+  // and C is even: half of every gang sits in each of the two slots.
+  p->split = (C % 2 == 0 && C >= 4 && per_cu == 2 && p->gangs * C == capacity) ? 1 : 0;
   return true;
 }
 

@@ -66,6 +66,7 @@ struct GangArgs {
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
   int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg;
+  int split;  // split gangs (see gang_kernel)
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
   uint32_t stats_bytes, keys_bytes, ml_bytes, acc_bytes;
@@ -213,14 +214,23 @@ struct Gang {
     const bool steady = a.k_e == 0 || seen == nb;
     const int nprev = min(a.k_e, seen);
     const int n_e = a.k_e > 0 ? min(a.k_e, nprev + nb - seen) : 0;
-    // this member's items: cr, cr + C, ... of [eviction set..., tail block],
-    // counted from the last member so that member 0, which also merges the
-    // row, never has more than the others
+    // this member's items of [eviction set..., tail block]: cr, cr + CE, ...
+    // for the CE attending members, counted from the last of them so that
+    // member 0, which also merges the row, never has more than the others.
+    // With a split gang (a.split) only the first half attends them: those
+    // members start first on their compute units and finish streaming
+    // earlier (a compute unit serves its two workgroups' loads in order), so
+    // the eviction-set work fills their wait for the second half.
     const int n_eitems = n_e + (tail > 0);
-    const int cr = C - 1 - c;
-    const int e_mine = cr < n_eitems ? (n_eitems - cr + C - 1) / C : 0;
+    const int CE = a.split ? C / 2 : C;
+    const int cr = CE - 1 - c;
+    const int e_mine = cr >= 0 && cr < n_eitems ? (n_eitems - cr + CE - 1) / CE : 0;
+    // items consumed before the statistics hand-off (the rest, at least one
+    // pair, after this member's keys are out); even, so that the slabs keep
+    // alternating
+    const int e_first = e_mine > 2 ? max(2, (e_mine - 2) & ~1) : e_mine;
     auto e_item = [&](int it) {  // item it of this member's share (scalar loads)
-      const int idx = cr + it * C;
+      const int idx = cr + it * CE;
       int blk = nb;  // the tail block
       if (idx < n_e) {
         const int v = steady ? sload(a.evict_set, (int64_t)row * a.k_e + idx) : eids[idx];
@@ -373,16 +383,16 @@ struct Gang {
     }
     __syncthreads();  // the queries and the eviction set are in shared memory
 
-    // ---- the first two eviction-set items (loaded during the stream)
+    // ---- this member's first eviction-set items (two slabs in flight)
     AttnState<T, D, G> att;
     att.init();
-    if (e_mine > 0) {
+    for (int it = 0; it < e_first; it += 2) {
       att.consume(sa, sm.att, a.qscale_att);
-      if (e_mine > 2) e_issue(sa, 2);
-    }
-    if (e_mine > 1) {
-      att.consume(sb, sm.att, a.qscale_att);
-      if (e_mine > 3) e_issue(sb, 3);
+      if (it + 2 < e_mine) e_issue(sa, it + 2);
+      if (it + 1 < e_first) {
+        att.consume(sb, sm.att, a.qscale_att);
+        if (it + 3 < e_mine) e_issue(sb, it + 3);
+      }
     }
 
     // ---- 3. row normaliser from every member's statistics
@@ -441,7 +451,7 @@ struct Gang {
     }
 
     // ---- the rest of this member's eviction-set share
-    for (int it = 2; it < e_mine; it += 2) {
+    for (int it = e_first; it < e_mine; it += 2) {
       att.consume(sa, sm.att, a.qscale_att);
       if (it + 2 < e_mine) e_issue(sa, it + 2);
       if (it + 1 < e_mine) {
@@ -591,7 +601,19 @@ __global__ __launch_bounds__(kThreads, (gang_wgs_per_cu<T, D, G>())) void gang_k
   using S = Gang<T, D, G, FORECAST>;
   __shared__ typename S::Smem sm;
   extern __shared__ uint32_t dyn[];
-  const int gang = blockIdx.x / a.C, c = blockIdx.x % a.C;
+  // split gangs: the first half of the grid (which the dispatcher places
+  // first on every compute unit) holds members 0 .. C/2 - 1 of every gang,
+  // the second half members C/2 .. C - 1
+  int gang, c;
+  if (a.split) {
+    const int hc = a.C / 2, half = a.gangs * hc;
+    const int b = (int)blockIdx.x < half ? (int)blockIdx.x : (int)blockIdx.x - half;
+    gang = b / hc;
+    c = b % hc + ((int)blockIdx.x < half ? 0 : hc);
+  } else {
+    gang = blockIdx.x / a.C;
+    c = blockIdx.x % a.C;
+  }
   for (int row = gang; row < a.rows; row += a.gangs) {
     S::row_step(a, row, c, sm, dyn);
     __syncthreads();
@@ -606,7 +628,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e), &gi);
   if (e != hipSuccess) return e;
   GangPlan plan;
-  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, L.gang_override, &plan))
+  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, gi.per_cu, L.gang_override, &plan))
     return hipErrorLaunchOutOfResources;
   GangArgs a{};
   a.query = L.query;
@@ -637,6 +659,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.C = plan.C;
   a.gangs = plan.gangs;
   a.per_wg = plan.per_wg;
+  a.split = plan.split;
   a.qscale_sel = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;
   a.qscale_att = L.scale * 1.4426950408889634f;
   a.wait_ticks = (uint64_t)(gi.wall_khz > 0 ? gi.wall_khz : 1) * kWaitMs;
