@@ -561,7 +561,8 @@ __device__ void wg_publish_partial(AttendSmem<T, D, G>& sm, f32x2* ml_lds,
 
 // Merge partials [p0, p0 + nparts) (agent-scope loads) into out[G][D]:
 // 4 channels per thread, partials 16 at a time with their loads in flight
-// together, merged with a running maximum.
+// together; per batch the largest m first, then one factor 2^(m_i - M) per
+// partial (native exp2: arguments <= 0).
 template <typename T, int D, int G>
 __device__ void combine_partials(int64_t p0, int nparts, __amdgpu_buffer_rsrc_t mlr,
                                  __amdgpu_buffer_rsrc_t acr, T* out) {
@@ -579,16 +580,19 @@ __device__ void combine_partials(int64_t p0, int nparts, __amdgpu_buffer_rsrc_t 
         ml[k] = load_agent_f32x2(mlr, (uint32_t)((pb * G + h) * 8));
         ac[k] = load_agent_f32x4(acr, (uint32_t)(((pb * G + h) * D + c) * 4));
       }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (s0 + k < nparts) bm = fmaxf(bm, ml[k].x);
+      if (bm == -INFINITY) continue;  // no tokens in this batch
+      const float mx = fmaxf(M, bm);
+      const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mx);
+      num *= sc;
+      den *= sc;
+      M = mx;
 #pragma unroll
       for (int k = 0; k < kB; ++k) {
-        if (s0 + k >= nparts || ml[k].x == -INFINITY) continue;
-        if (ml[k].x > M) {
-          const float sc = M == -INFINITY ? 0.f : exp2f(M - ml[k].x);
-          num *= sc;
-          den *= sc;
-          M = ml[k].x;
-        }
-        const float f = exp2f(ml[k].x - M);
+        const float f = (s0 + k < nparts && ml[k].x != -INFINITY) ? fast_exp2(ml[k].x - M) : 0.f;
         num += ac[k] * f;
         den = fmaf(ml[k].y, f, den);
       }

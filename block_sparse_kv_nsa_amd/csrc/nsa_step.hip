@@ -395,8 +395,19 @@ struct Gang {
       }
     }
 
-    // ---- 3. row normaliser from every member's statistics
+    // ---- exclusion flags of this member's blocks (the eviction set is never
+    // a query-aware candidate), set while the statistics come in
     const int m_row = max(0, min(a.k - n_e, nb - n_e));
+    if (m_row > 0) {
+      for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
+      __syncthreads();
+      for (int i = threadIdx.x; i < n_e; i += kThreads) {
+        const int id = eids[i];
+        if (id >= blk0 && id < blk0 + nblk) sm.ckeys[id - blk0] = 0u;
+      }
+    }
+
+    // ---- 3. row normaliser from every member's statistics
     if constexpr (!FORECAST) {
       if (m_row > 0 && wave == 0) {
         // lane: members lane / G, + 64 / G, ...; head lane % G
@@ -415,13 +426,7 @@ struct Gang {
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.keys, a.keys_bytes);
     const uint32_t key_off = (uint32_t)((int64_t)row * a.nb_max * 4);
     if (m_row > 0) {
-      for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
-      __syncthreads();
-      for (int i = threadIdx.x; i < n_e; i += kThreads) {
-        const int id = eids[i];
-        if (id >= blk0 && id < blk0 + nblk) sm.ckeys[id - blk0] = 0u;
-      }
-      __syncthreads();
+      __syncthreads();  // the normaliser and the exclusion flags
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float v = 0.f;
@@ -536,21 +541,9 @@ struct Gang {
     wg_publish_partial(sm.att, sm.ml, mlr, acr, (int64_t)row * kMaxGang + c);
     if (c != 0) return;
 
-    if (wave == 0)
-      wave_poll_pairs<NP>(mlr, st_off, C * G, err, a.wait_ticks, [&](int, f32x2) {});
-    __syncthreads();
-    T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
-    combine_partials<T, D, G>((int64_t)row * kMaxGang, C, mlr, acr, out);
-
-    // the caller's outputs: eviction state (when it changed) and the selected
-    // ids, ascending (the eviction set and the query-aware list are each
-    // ascending and disjoint: each id goes after the smaller ids of the other
-    // list)
-    if (!steady) {
-      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
-        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
-      if (threadIdx.x == 0) a.evict_seen[row] = nb;
-    }
+    // the selected ids, ascending, while the other partials arrive (the
+    // eviction set and the query-aware list are each ascending and disjoint:
+    // each id goes after the smaller ids of the other list)
     int32_t* sel = a.selected + (int64_t)row * a.k;
     auto below = [](const int* v, int n, int id) {  // entries < id of ascending v[0..n)
       int lo = 0;
@@ -573,15 +566,31 @@ struct Gang {
     for (int t = n_e + m_row + threadIdx.x; t < a.k; t += kThreads) sel[t] = -1;
     if (threadIdx.x == 0) a.num_selected[row] = n_e + m_row;
 
-    // every member has read every slot of the row, and this workgroup's
-    // merge (a subset of its waves) is done with the partials: clear them
+    if (wave == 0)
+      wave_poll_pairs<NP>(mlr, st_off, C * G, err, a.wait_ticks, [&](int, f32x2) {});
     __syncthreads();
+    // every member's partial is in, so every member is done with the row's
+    // statistics and keys: clear those slots (the partials' after the merge)
     if (!FORECAST)
       for (int i = threadIdx.x; i < C * G; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, srs, (int)(st_off + i * 8), 0, kSC1);
     if (m_row > 0)
       for (int i = threadIdx.x; i < nb; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b32(0u, krs, (int)(key_off + i * 4), 0, kSC1);
+    T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
+    combine_partials<T, D, G>((int64_t)row * kMaxGang, C, mlr, acr, out);
+
+    // the eviction state, when it changed: every member has read the old one
+    // (its partial is in)
+    if (!steady) {
+      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
+        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
+      if (threadIdx.x == 0) a.evict_seen[row] = nb;
+    }
+
+    // this workgroup's merge (a subset of its waves) is done with the
+    // partials: clear their (m, l) slots
+    __syncthreads();
     for (int i = threadIdx.x; i < C * G; i += kThreads)
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, mlr, (int)(st_off + i * 8), 0, kSC1);
   }
