@@ -399,25 +399,27 @@ __device__ __attribute__((always_inline)) inline void wg_radix_top(const uint32_
 // end; keys <= 1 are not candidates).  Every 16-lane row's largest candidate
 // is >= T0, the least of the 16 row maxima, so at least 16 candidates are
 // >= T0 and the m largest are among them.  Those (at most kSmallCap, else the
-// call declines) are gathered in index order; thread t ranks gathered key t
-// by (key descending, index ascending) against all of them, and the m best
-// are emitted with emit(index, rank in index order).  Returns false without
-// emitting when it declines (m > 16, a row without candidates, or more than
-// kSmallCap keys >= T0: many equal scores).  Called by all threads.
+// call declines) are gathered in index order as 64-bit composites (key, then
+// the complement of the position: one unsigned comparison orders by key
+// descending and index ascending); thread t ranks composite t against all of
+// them and the m best are emitted with emit(index, rank in index order).
+// Returns false without emitting when it declines (m > 16, a row without
+// candidates, or more than kSmallCap keys >= T0: many equal scores).  Called
+// by all threads.
 constexpr int kSmallCap = kThreads;
 
 struct SmallTopSmem {
-  uint32_t ck[kSmallCap + kThreads];  // the gathered keys, then one unused slot per thread
+  uint64_t cc[kSmallCap + kThreads];  // the gathered composites, then one unused slot per thread
   int cid[kSmallCap + kThreads];
   uint32_t gmin[kWaves];
-  uint32_t cnt[kWaves][kRadixChunks];
+  uint32_t cnt[kRadixChunks][kWaves];
   int nsel[kWaves];
 };
 
 template <int KPT, typename Emit>
 __device__ __attribute__((always_inline)) bool wg_top_small(const uint32_t (&kv)[KPT], int m,
                                                             SmallTopSmem& ss, Emit emit) {
-  static_assert(KPT <= kRadixChunks && KPT <= kWave, "keys per thread");
+  static_assert(KPT <= kRadixChunks && KPT <= 16, "keys per thread");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const uint64_t below = (1ull << lane) - 1ull;
@@ -443,38 +445,44 @@ __device__ __attribute__((always_inline)) bool wg_top_small(const uint32_t (&kv)
     const uint32_t c = (uint32_t)__popcll(__ballot(kv[j] >= t0));
     myc = lane == j ? c : myc;
   }
-  if (lane < KPT) ss.cnt[wave][lane] = myc;
+  if (lane < KPT) ss.cnt[lane][wave] = myc;
   __syncthreads();
-  // gather in index order (chunk, then wave, then lane), without branches
-  int run = 0;
+  // gather in index order (chunk, then wave, then lane): lane j < KPT forms
+  // chunk j's total and this wave's offset within it, a lane scan gives the
+  // chunks' starts, and every lane reads the KPT bases back
+  int base_j = 0, total;
+  {
+    const uint4 c4 = lane < KPT ? *reinterpret_cast<const uint4*>(&ss.cnt[lane][0])
+                                : make_uint4(0, 0, 0, 0);
+    const uint32_t tot_j = c4.x + c4.y + c4.z + c4.w;
+    const uint32_t own = (wave > 0 ? c4.x : 0u) + (wave > 1 ? c4.y : 0u) + (wave > 2 ? c4.z : 0u);
+    const uint32_t incl = wave_incl_scan(tot_j);
+    base_j = (int)(incl - tot_j + own);
+    total = __builtin_amdgcn_readlane((int)incl, KPT - 1);
+  }
+  if (total > kSmallCap) return false;  // uniform (many equal keys)
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int c0 = (int)ss.cnt[0][j], c1 = (int)ss.cnt[1][j], c2 = (int)ss.cnt[2][j],
-              c3 = (int)ss.cnt[3][j];
-    const int base = run + (wave > 0 ? c0 : 0) + (wave > 1 ? c1 : 0) + (wave > 2 ? c2 : 0);
-    run += c0 + c1 + c2 + c3;
+    const int bj = __builtin_amdgcn_readlane(base_j, j);
     const bool c = kv[j] >= t0;
-    int p = base + __popcll(__ballot(c) & below);
-    p = (c && p < kSmallCap) ? p : kSmallCap + (int)threadIdx.x;
-    ss.ck[p] = kv[j];
+    int p = bj + __popcll(__ballot(c) & below);
+    p = c ? p : kSmallCap + (int)threadIdx.x;
+    ss.cc[p] = ((uint64_t)kv[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
     ss.cid[p] = (int)threadIdx.x + kThreads * j;
   }
-  const int total = run;  // uniform
-  if (total > kSmallCap) return false;
+  const int padded = (total + 15) & ~15;
+  if ((int)threadIdx.x >= total && (int)threadIdx.x < padded) ss.cc[threadIdx.x] = 0ull;
   __syncthreads();
-  // rank of gathered key t among all gathered keys, 16 per step
+  // rank of composite t among all gathered (all distinct), 16 per step
   const int t = (int)threadIdx.x;
-  const uint32_t k = ss.ck[t];
+  const uint64_t k = ss.cc[t];
   int rank = 0;
-  for (int j0 = 0; j0 < total; j0 += 16) {
-    uint32_t kj[16];
+  for (int j0 = 0; j0 < padded; j0 += 16) {
+    uint64_t kj[16];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) kj[jj] = ss.ck[j0 + jj];
+    for (int jj = 0; jj < 16; ++jj) kj[jj] = ss.cc[j0 + jj];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = j0 + jj;
-      rank += (j < total) & ((kj[jj] > k) | ((kj[jj] == k) & (j < t)));
-    }
+    for (int jj = 0; jj < 16; ++jj) rank += kj[jj] > k;
   }
   const bool sel = t < total && rank < m;
   const uint64_t bs = __ballot(sel);
