@@ -193,12 +193,17 @@ inline StepLayout step_layout(int B, int Hkv, int G, int D, int max_seq_len) {
   return s;
 }
 
+constexpr int kTblLds = 2048;  // longest table row a member keeps in shared memory
+
 // Dynamic shared memory of a member: the eviction set, the query-aware list,
-// then the larger of the eviction update's keys (old set and new blocks) and
-// old set, and the row's block keys.
+// the table row (up to kTblLds entries), then the larger of the eviction
+// update's keys (old set and new blocks) and old set, and the row's block
+// keys.
 inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e) {
   const size_t upd = (size_t)(k_e + lay.nb_max) + k_e;
-  const size_t words = (size_t)(k_e > 0 ? k_e : 1) + k + (upd > (size_t)lay.nb_max ? upd : lay.nb_max);
+  const size_t tbl = (size_t)(lay.nb_max < kTblLds ? lay.nb_max : kTblLds);
+  const size_t words = (size_t)(k_e > 0 ? k_e : 1) + k + tbl +
+                       (upd > (size_t)lay.nb_max ? upd : lay.nb_max);
   return round_up(words * 4, 16);
 }
 

@@ -131,7 +131,7 @@ __device__ __forceinline__ void wave_poll_pairs(__amdgpu_buffer_rsrc_t r, uint32
     if (__all(ok)) break;
     bool go = true;
     if (lane == 0) go = pt.more(err, ticks);
-    if (!__shfl(go, 0, kWave)) break;
+    if (!__builtin_amdgcn_readfirstlane(go)) break;
   }
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
@@ -190,13 +190,24 @@ struct Gang {
     const bool canon = (q % DUP) == 0;
     int* eids = reinterpret_cast<int*>(dyn);                      // k_e: the eviction set
     int* qsel = eids + (a.k_e > 0 ? a.k_e : 1);                   // k: query-aware blocks
-    uint32_t* scratch = reinterpret_cast<uint32_t*>(qsel + a.k);  // eviction update
+    int* tbl = qsel + a.k;                                        // min(nb_max, kTblLds)
+    uint32_t* scratch = reinterpret_cast<uint32_t*>(tbl + min(a.nb_max, kTblLds));
     const int64_t tb = (int64_t)b * a.max_blocks;                 // the row's table entries
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
     const T* kp = static_cast<const T*>(a.k_pool);
     const T* vp = static_cast<const T*>(a.v_pool);
     uint32_t* err = a.err;
 
+    // the row's block table (full blocks) for the query-aware slabs, parked
+    // in shared memory below when it fits (bounded loads: no branches)
+    const bool tbl_lds = nb <= kTblLds;
+    uint32_t tv[kTblLds / kThreads];
+    {
+      const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.table + tb, (uint32_t)(tbl_lds ? nb * 4 : 0));
+#pragma unroll
+      for (int j = 0; j < kTblLds / kThreads; ++j)
+        tv[j] = __builtin_amdgcn_raw_buffer_load_b32(trs, (int)((threadIdx.x + kThreads * j) * 4), 0, 0);
+    }
     // the attention queries, parked in shared memory below
     uint32_t qw[QPT];
 #pragma unroll
@@ -322,6 +333,13 @@ struct Gang {
         if (e_mine > 0) e0 = e_item(0);
         if (e_mine > 1) e1 = e_item(1);
         if (steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
+        if (tbl_lds) {
+#pragma unroll
+          for (int j = 0; j < kTblLds / kThreads; ++j) {
+            const int i = threadIdx.x + kThreads * j;
+            if (i < nb) tbl[i] = (int)tv[j];
+          }
+        }
         uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
 #pragma unroll
         for (int i = 0; i < QPT; ++i) {
@@ -472,7 +490,7 @@ struct Gang {
       constexpr int kSmallKpt = 8;
       uint32_t* rkeys = scratch;  // nb
       uint32_t kv[kSmallKpt];
-      Patience pt{0, false};
+      Patience pt{0, false};  // each wave polls its own share
       for (;;) {
         bool ok = true;
 #pragma unroll
@@ -488,16 +506,12 @@ struct Gang {
           rkeys[i] = v;
           ok &= v != 0u;
         }
-        const bool wave_ok = __all(ok);
-        if (lane == 0) sm.s_int[wave] = wave_ok;
-        __syncthreads();
-        const bool all = sm.s_int[0] && sm.s_int[1] && sm.s_int[2] && sm.s_int[3];
-        if (threadIdx.x == 0) sm.s_int[4] = all ? 0 : (int)pt.more(err, a.wait_ticks);
-        __syncthreads();
-        const bool again = !all && sm.s_int[4];
-        __syncthreads();  // every thread has read s_int before it is written again
-        if (!again) break;  // uniform
+        if (__all(ok)) break;
+        bool go = true;
+        if (lane == 0) go = pt.more(err, a.wait_ticks);
+        if (!__builtin_amdgcn_readfirstlane(go)) break;
       }
+      __syncthreads();  // every wave's share is in
       auto put = [&](int i, int pos) {
         if (pos < m_row) qsel[pos] = i;
       };
@@ -518,7 +532,8 @@ struct Gang {
     auto q_issue = [&](Slab<T, D>& s, int it) {
       const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * C]), 0), nb - 1);
       Item x;
-      x.base = ((int64_t)sload(a.table, tb + blk) * a.Hkv + g) * (int64_t)(kBlock * D);
+      const int64_t phys = tbl_lds ? tbl[blk] : sload(a.table, tb + blk);
+      x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
       x.valid = kBlock;
       x.logits = nullptr;
       slab_issue<T, D, false>(s, x, kp, vp);
