@@ -87,19 +87,20 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait of one thread: more() sleeps briefly and returns true while
-// the caller may keep waiting; false on a time out (recorded in the sticky
-// error word) or when another workgroup has recorded one.
+// Bounded wait of a wave.  The caller reads the sticky error word in the
+// same round as the data it polls (one round trip per round); more() returns
+// false once an error is recorded or, looked at every 8th round, when the
+// time is up (then it records one itself).
 struct Patience {
   uint64_t t0;
-  bool started;
-  __device__ __forceinline__ bool more(uint32_t* err, uint64_t ticks) {
-    if (ld_agent(err) != 0u) return false;
-    const uint64_t now = (uint64_t)wall_clock64();
-    if (!started) {
-      started = true;
-      t0 = now;
-    } else if (now - t0 > ticks) {
+  uint32_t round;
+  __device__ __forceinline__ void start() {
+    t0 = (uint64_t)wall_clock64();
+    round = 0;
+  }
+  __device__ __forceinline__ bool more(uint32_t err_seen, uint32_t* err, uint64_t ticks) {
+    if (__builtin_amdgcn_readfirstlane(err_seen) != 0u) return false;
+    if ((++round & 7u) == 0u && (uint64_t)wall_clock64() - t0 > ticks) {
       st_agent(err, 1u);
       return false;
     }
@@ -116,7 +117,8 @@ __device__ __forceinline__ void wave_poll_pairs(__amdgpu_buffer_rsrc_t r, uint32
                                                 uint32_t* err, uint64_t ticks, Merge merge) {
   const int lane = threadIdx.x & (kWave - 1);
   u32x2 v[NP];
-  Patience pt{0, false};
+  Patience pt;
+  pt.start();
   for (;;) {
     bool ok = true;
 #pragma unroll
@@ -128,10 +130,9 @@ __device__ __forceinline__ void wave_poll_pairs(__amdgpu_buffer_rsrc_t r, uint32
         ok &= (v[j].x | v[j].y) != 0u;
       }
     }
+    const uint32_t e = ld_agent(err);
     if (__all(ok)) break;
-    bool go = true;
-    if (lane == 0) go = pt.more(err, ticks);
-    if (!__builtin_amdgcn_readfirstlane(go)) break;
+    if (!pt.more(e, err, ticks)) break;
   }
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
@@ -490,7 +491,8 @@ struct Gang {
       constexpr int kSmallKpt = 8;
       uint32_t* rkeys = scratch;  // nb
       uint32_t kv[kSmallKpt];
-      Patience pt{0, false};  // each wave polls its own share
+      Patience pt;  // each wave polls its own share
+      pt.start();
       for (;;) {
         bool ok = true;
 #pragma unroll
@@ -506,10 +508,9 @@ struct Gang {
           rkeys[i] = v;
           ok &= v != 0u;
         }
+        const uint32_t e = ld_agent(err);
         if (__all(ok)) break;
-        bool go = true;
-        if (lane == 0) go = pt.more(err, a.wait_ticks);
-        if (!__builtin_amdgcn_readfirstlane(go)) break;
+        if (!pt.more(e, err, a.wait_ticks)) break;
       }
       __syncthreads();  // every wave's share is in
       auto put = [&](int i, int pos) {
