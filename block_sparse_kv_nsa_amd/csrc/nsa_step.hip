@@ -446,27 +446,43 @@ struct Gang {
     const uint32_t key_off = (uint32_t)((int64_t)row * a.nb_max * 4);
     if (m_row > 0) {
       __syncthreads();  // the normaliser and the exclusion flags
+      // every shared-memory read first (one wait for all of them), then the
+      // arithmetic without branches; the 16 lanes of a block read its
+      // exclusion flag together
+      float lv[U][KEEP];
+      uint32_t ex[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int kk = 0; kk < KEEP; ++kk) lv[u][kk] = sm.lgs[u][kk][threadIdx.x];
+        ex[u] = sm.ckeys[u * 16 + wave * 4 + (lane >> 4)];
+      }
+      float mh[KEEP], iz[KEEP];
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) {
+        mh[kk] = FORECAST ? 0.f : sm.sM[h0 + kk];
+        iz[kk] = FORECAST ? 0.f : sm.sInvZ[h0 + kk];
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float v = 0.f;
         if constexpr (FORECAST) {
-          v = sm.lgs[u][0][threadIdx.x];
+          v = lv[u][0];
         } else {
 #pragma unroll
           for (int kk = 0; kk < KEEP; ++kk) {
-            const float l = sm.lgs[u][kk][threadIdx.x];
-            if (canon && l != -INFINITY) v += exp2f(l - sm.sM[h0 + kk]) * sm.sInvZ[h0 + kk];
+            const float l = lv[u][kk];
+            const float e = exp2f(l - mh[kk]) * iz[kk];
+            v += (canon && l != -INFINITY) ? e : 0.f;
           }
           v += quad_partner<2>(v);
           v += quad_partner<1>(v);
         }
         v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
         v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
-        if ((lane & 15) == 0) {
-          const int bl = u * 16 + wave * 4 + (lane >> 4);
-          const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
-          sm.ckeys[bl] = (j < j1 && sm.ckeys[bl] != 0u) ? order_key(v) : 0u;
-        }
+        const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
+        const uint32_t key = (j < j1 && ex[u] != 0u) ? order_key(v) : 0u;
+        if ((lane & 15) == 0) sm.ckeys[u * 16 + wave * 4 + (lane >> 4)] = key;
       }
       __syncthreads();
       if ((int)threadIdx.x < nblk)
