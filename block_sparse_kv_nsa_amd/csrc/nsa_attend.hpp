@@ -16,6 +16,7 @@
 // exceeds it by more than 8, so weights stay <= 2^8 and the common slab needs
 // no cross-lane maximum.
 #pragma once
+#include <cstddef>
 
 #include "nsa_device.hpp"
 
@@ -531,24 +532,32 @@ template <typename T, int D, int G>
 __device__ void wg_publish_partial(AttendSmem<T, D, G>& sm, f32x2* ml_lds,
                                    __amdgpu_buffer_rsrc_t mlr, __amdgpu_buffer_rsrc_t acr,
                                    int64_t pidx) {
+  using AS = AttendSmem<T, D, G>;
+  static_assert(offsetof(AS, wacc) % 16 == 0 && D % 4 == 0, "wacc chunks start on 16 bytes");
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
-    float M = sm.wm[0][h];
+    // every wave's values first (one wait), then the merge without branches
+    float wmv[kWaves], wlv[kWaves];
+    f32x4 wav[kWaves];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][h]);
+    for (int w = 0; w < kWaves; ++w) {
+      wmv[w] = sm.wm[w][h];
+      wlv[w] = sm.wl[w][h];
+      wav[w] = *reinterpret_cast<const f32x4*>(&sm.wacc[w][h][c]);
+    }
+    float M = wmv[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmv[w]);
     f32x4 A = {0.f, 0.f, 0.f, 0.f};
     float Ls = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (sm.wm[w][h] == -INFINITY) continue;
-        const float f = exp2f(sm.wm[w][h] - M);
-        A.x = fmaf(sm.wacc[w][h][c], f, A.x);
-        A.y = fmaf(sm.wacc[w][h][c + 1], f, A.y);
-        A.z = fmaf(sm.wacc[w][h][c + 2], f, A.z);
-        A.w = fmaf(sm.wacc[w][h][c + 3], f, A.w);
-        Ls = fmaf(sm.wl[w][h], f, Ls);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = wmv[w] == -INFINITY ? 0.f : exp2f(wmv[w] - M);
+      A.x = fmaf(wav[w].x, f, A.x);
+      A.y = fmaf(wav[w].y, f, A.y);
+      A.z = fmaf(wav[w].z, f, A.z);
+      A.w = fmaf(wav[w].w, f, A.w);
+      Ls = fmaf(wlv[w], f, Ls);
     }
     store_agent_f32x4(acr, (uint32_t)(((pidx * G + h) * D + c) * 4), A);
     if (c == 0) ml_lds[h] = f32x2{M, Ls};

@@ -389,8 +389,15 @@ struct Gang {
       if (threadIdx.x < G) {
         const int h = threadIdx.x;
         const int qq = G >= 4 ? h / KEEP : h * DUP, kk = G >= 4 ? h % KEEP : 0;
-        float M = sm.red_m[0][qq][kk], S = sm.red_s[0][qq][kk];
-        for (int w = 1; w < kWaves; ++w) merge_ms(M, S, sm.red_m[w][qq][kk], sm.red_s[w][qq][kk]);
+        float rm[kWaves], rs[kWaves];  // every wave's pair first (one wait)
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          rm[w] = sm.red_m[w][qq][kk];
+          rs[w] = sm.red_s[w][qq][kk];
+        }
+        float M = rm[0], S = rs[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) merge_ms(M, S, rm[w], rs[w]);
         store_agent_f32x2(srs, st_off + (uint32_t)((c * G + h) * 8), f32x2{M, S});
       }
     }
