@@ -77,39 +77,9 @@ struct AttendSmem {
   float wacc[kWaves][G][D];
 };
 
-// A workgroup's running partial kept in shared memory across several
-// attend_items_merge calls: per head the reference maximum m (base 2), the
-// normaliser l and the unnormalised output acc[D].
-template <int D, int G>
-struct WgAcc {
-  float m[G], l[G];
-  float acc[G][D];
-};
-
-template <int D, int G>
-__device__ void wg_acc_init(WgAcc<D, G>& acc) {
-  for (int i = threadIdx.x; i < G * D; i += kThreads) (&acc.acc[0][0])[i] = 0.f;
-  if (threadIdx.x < G) {
-    acc.m[threadIdx.x] = -INFINITY;
-    acc.l[threadIdx.x] = 0.f;
-  }
-}
-
-// Store a WgAcc as partial pidx (agent-scope stores).
-template <int D, int G>
-__device__ void wg_acc_store(const WgAcc<D, G>& acc, __amdgpu_buffer_rsrc_t mlr,
-                             __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
-  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
-    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
-    store_agent_f32x4(acr, (uint32_t)(((pidx * G + h) * D + c) * 4),
-                      f32x4{acc.acc[h][c], acc.acc[h][c + 1], acc.acc[h][c + 2], acc.acc[h][c + 3]});
-    if (c == 0) store_agent_f32x2(mlr, (uint32_t)((pidx * G + h) * 8), f32x2{acc.m[h], acc.l[h]});
-  }
-}
-
-template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
-                            ItemFn item, AttendSmem<T, D, G>& sm, const Slab<T, D>* first);
+                            ItemFn item, AttendSmem<T, D, G>& sm);
 
 // Accumulate items [i0, i1) (item(it) -> Item) and store the workgroup's
 // (m, l) and acc[D] per head at partial index pidx with agent-scope stores.
@@ -118,8 +88,7 @@ template <typename T, int D, int G, bool PRE, typename ItemFn>
 __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                              ItemFn item, AttendSmem<T, D, G>& sm, __amdgpu_buffer_rsrc_t mlr,
                              __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
-  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1), false, false>(qrow, kp, vp, qscale, i0, i1, item, sm,
-                                                          nullptr);
+  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1)>(qrow, kp, vp, qscale, i0, i1, item, sm);
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
     float M = sm.wm[0][h];
@@ -144,66 +113,9 @@ __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qsca
   }
 }
 
-// Accumulate items [i0, i1) into the workgroup's running partial `acc`
-// (shared memory).  BUF: slabs in flight per workgroup (1 or 2); QL: read the
-// query slices from sm.qlds (filled by the caller, qrow unused) at every slab
-// instead of holding them in registers (frees G * D / 8 registers per lane
-// for bf16 at D = 128, room for the second slab).  Ends with a barrier.
-// PF: the first item's slab was issued by the caller (slab_issue) into
-// *first, so its loads overlapped the caller's work.
-template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF = false, typename ItemFn>
-__device__ void attend_items_merge(const T* qrow, const T* kp, const T* vp, float qscale, int i0,
-                                   int i1, ItemFn item, AttendSmem<T, D, G>& sm,
-                                   WgAcc<D, G>& acc, const Slab<T, D>* first = nullptr) {
-  if (i0 >= i1) return;  // uniform
-  attend_core<T, D, G, PRE, BUF, QL, PF>(qrow, kp, vp, qscale, i0, i1, item, sm, first);
-  float nm = -INFINITY, nl = 0.f;
-  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
-    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
-    float M = sm.wm[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][h]);
-    f32x4 A = {0.f, 0.f, 0.f, 0.f};
-    float Ls = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (sm.wm[w][h] == -INFINITY) continue;
-        const float f = exp2f(sm.wm[w][h] - M);
-        A.x = fmaf(sm.wacc[w][h][c], f, A.x);
-        A.y = fmaf(sm.wacc[w][h][c + 1], f, A.y);
-        A.z = fmaf(sm.wacc[w][h][c + 2], f, A.z);
-        A.w = fmaf(sm.wacc[w][h][c + 3], f, A.w);
-        Ls = fmaf(sm.wl[w][h], f, Ls);
-      }
-    }
-    const float pm = acc.m[h];
-    const float mx = fmaxf(pm, M);
-    const float fa = pm == -INFINITY ? 0.f : exp2f(pm - mx);
-    const float fb = M == -INFINITY ? 0.f : exp2f(M - mx);
-    acc.acc[h][c] = acc.acc[h][c] * fa + A.x * fb;
-    acc.acc[h][c + 1] = acc.acc[h][c + 1] * fa + A.y * fb;
-    acc.acc[h][c + 2] = acc.acc[h][c + 2] * fa + A.z * fb;
-    acc.acc[h][c + 3] = acc.acc[h][c + 3] * fa + A.w * fb;
-    if (c == 0) {
-      nm = mx;
-      nl = acc.l[h] * fa + Ls * fb;
-    }
-  }
-  __syncthreads();  // every thread has read the old m
-  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
-    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
-    if (c == 0) {
-      acc.m[h] = nm;
-      acc.l[h] = nl;
-    }
-  }
-  __syncthreads();
-}
-
-template <typename T, int D, int G, bool PRE, int BUF, bool QL, bool PF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
-                            ItemFn item, AttendSmem<T, D, G>& sm, const Slab<T, D>* first) {
+                            ItemFn item, AttendSmem<T, D, G>& sm) {
   using Q = Quad<T, D>;
   using V = VGeo<T, D>;
   constexpr int NLD = Q::NLD, EPL = V::EPL, LPR = V::LPR, TPL = V::TPL, NLV = V::NLV;
@@ -218,8 +130,8 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
   const bool canon = (q % DUP) == 0;
   const int tk = wave * kSub + r;
 
-  QSlice<T, D> qs[QL ? 1 : G];
-  if constexpr (!PRE && !QL) {
+  QSlice<T, D> qs[G];
+  if constexpr (!PRE) {
 #pragma unroll
     for (int h = 0; h < G; ++h) qs[h].load(qrow + h * D, q);
   }
@@ -236,14 +148,6 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
   for (int kk = 0; kk < KEEP; ++kk) mref[kk] = -INFINITY;
 
   auto issue = [&](int it, uint4 (&kx)[NLD], uint4 (&vx)[NLV], Item& itm) {
-    if (PF && it == i0) {  // issued by the caller
-#pragma unroll
-      for (int ld = 0; ld < NLD; ++ld) kx[ld] = first->k[ld];
-#pragma unroll
-      for (int u = 0; u < NLV; ++u) vx[u] = first->v[u];
-      itm = first->it;
-      return;
-    }
     itm = item(it);
     if constexpr (!PRE) {
 #pragma unroll
@@ -259,19 +163,8 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     float lg[KEEP];
     if constexpr (!PRE) {
       float v[G];
-      if constexpr (QL) {
-        // one head's slice at a time; the empty asm keeps the loads in the
-        // loop (they would otherwise be hoisted back into registers)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          asm volatile("" ::: "memory");
-          qs[0].load(&sm.qlds[h][0], q);
-          v[h] = qs[0].dot(kx);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
-      }
+      for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
       quad_reduce<2, G>(v, q);
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) lg[kk] = v[kk] * qscale;

@@ -514,17 +514,17 @@ struct Gang {
       constexpr int kSmallKpt = 8;
       uint32_t* rkeys = scratch;  // nb
       uint32_t kv[kSmallKpt];
-      Patience pt;  // each wave polls its own share
+      Patience pt;  // each wave polls its own share, reading again only what is missing
       pt.start();
+#pragma unroll
+      for (int j = 0; j < kSmallKpt; ++j) kv[j] = 0u;
       for (;;) {
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < kSmallKpt; ++j) {
           const int i = threadIdx.x + kThreads * j;
-          kv[j] = i < nb ? __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1)
-                         : 0u;
-          ok &= i >= nb || kv[j] != 0u;
-          if (i < nb) rkeys[i] = kv[j];
+          if (i < nb && kv[j] == 0u)
+            kv[j] = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
         }
         for (int i = threadIdx.x + kThreads * kSmallKpt; i < nb; i += kThreads) {
           const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
@@ -532,8 +532,15 @@ struct Gang {
           ok &= v != 0u;
         }
         const uint32_t e = ld_agent(err);
+#pragma unroll
+        for (int j = 0; j < kSmallKpt; ++j) ok &= (int)threadIdx.x + kThreads * j >= nb || kv[j] != 0u;
         if (__all(ok)) break;
         if (!pt.more(e, err, a.wait_ticks)) break;
+      }
+#pragma unroll
+      for (int j = 0; j < kSmallKpt; ++j) {
+        const int i = threadIdx.x + kThreads * j;
+        if (i < nb) rkeys[i] = kv[j];
       }
       __syncthreads();  // every wave's share is in
       auto put = [&](int i, int pos) {
