@@ -87,10 +87,11 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait of a wave.  The caller reads the sticky error word in the
-// same round as the data it polls (one round trip per round); more() returns
-// false once an error is recorded or, looked at every 8th round, when the
-// time is up (then it records one itself).
+// Bounded wait of a wave.  Every 8th round the caller reads the sticky
+// error word together with the data it polls (err_due(); one round trip per
+// round, and the one word is not read by every wave in every round); more()
+// returns false once an error is recorded or, on those rounds, when the time
+// is up (then it records one itself).
 struct Patience {
   uint64_t t0;
   uint32_t round;
@@ -98,12 +99,17 @@ struct Patience {
     t0 = (uint64_t)wall_clock64();
     round = 0;
   }
+  __device__ __forceinline__ bool err_due() const { return (round & 7u) == 7u; }
+  __device__ __forceinline__ uint32_t read_err(const uint32_t* err) const {
+    return err_due() ? ld_agent(err) : 0u;
+  }
   __device__ __forceinline__ bool more(uint32_t err_seen, uint32_t* err, uint64_t ticks) {
     if (__builtin_amdgcn_readfirstlane(err_seen) != 0u) return false;
-    if ((++round & 7u) == 0u && (uint64_t)wall_clock64() - t0 > ticks) {
+    if (err_due() && (uint64_t)wall_clock64() - t0 > ticks) {
       st_agent(err, 1u);
       return false;
     }
+    ++round;
     __builtin_amdgcn_s_sleep(1);
     return true;
   }
@@ -119,18 +125,19 @@ __device__ __forceinline__ void wave_poll_pairs(__amdgpu_buffer_rsrc_t r, uint32
   u32x2 v[NP];
   Patience pt;
   pt.start();
-  for (;;) {
+#pragma unroll
+  for (int j = 0; j < NP; ++j) v[j] = u32x2{0u, 0u};
+  for (;;) {  // reading again only the slots still missing
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int i = lane + kWave * j;
-      v[j] = u32x2{0u, 0u};
-      if (i < n) {
+      if (i < n && (v[j].x | v[j].y) == 0u)
         v[j] = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off0 + i * 8), 0, kSC1);
-        ok &= (v[j].x | v[j].y) != 0u;
-      }
     }
-    const uint32_t e = ld_agent(err);
+    const uint32_t e = pt.read_err(err);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) ok &= lane + kWave * j >= n || (v[j].x | v[j].y) != 0u;
     if (__all(ok)) break;
     if (!pt.more(e, err, ticks)) break;
   }
@@ -531,7 +538,7 @@ struct Gang {
           rkeys[i] = v;
           ok &= v != 0u;
         }
-        const uint32_t e = ld_agent(err);
+        const uint32_t e = pt.read_err(err);
 #pragma unroll
         for (int j = 0; j < kSmallKpt; ++j) ok &= (int)threadIdx.x + kThreads * j >= nb || kv[j] != 0u;
         if (__all(ok)) break;
