@@ -451,10 +451,131 @@ def check_locality(O):
     assert O.locality([1, 2, 4, 5], [1, 2, 3], None) == 0.5
 
 
+# ----------------------------------------------------------------------------
+# the multi-step driver: caches, state carried across steps, both modes
+# ----------------------------------------------------------------------------
+def _bf16_values(rng, shape):
+    """Random values exactly representable in bf16 (torch's float32 -> bf16
+    cast, a library routine independent of the oracle's rounding)."""
+    import torch
+    x = rng.standard_normal(shape).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _expected_reps_and_E(keys, logits, nb):
+    """Every block's representatives and eviction score from exact rationals."""
+    d = keys.shape[1]
+    reps = np.zeros((nb, 4, d))
+    E = np.zeros(nb)
+    for b in range(nb):
+        means = []
+        for j in range(4):
+            lo = 64 * b + 16 * j
+            for c in range(d):
+                reps[b, j, c] = float(nearest_even_by_search(fsum_exact(keys[lo:lo + 16, c]) / 16, 8))
+            means.append(fsum_exact(logits[lo:lo + 16]) / 16)
+        E[b] = float(nearest_even_by_search(max(means), 24))
+    return reps, E
+
+
+def _loop_scores(q, reps, scale):
+    """Group-softmax block scores written as loops over the stored reps."""
+    nb, _, d = reps.shape
+    G = len(q)
+    group = [0.0] * (4 * nb)
+    for h in range(G):
+        lg = [scale * sum(q[h][c] * reps[j // 4, j % 4, c] for c in range(d)) for j in range(4 * nb)]
+        mx = max(lg)
+        z = sum(math.exp(v - mx) for v in lg)
+        for j in range(4 * nb):
+            group[j] += math.exp(lg[j] - mx) / z
+    return [max(group[4 * b:4 * b + 4]) for b in range(nb)]
+
+
+def _attend_tokens(q, keys, vals, toks, scale):
+    out = np.zeros((len(q), keys.shape[1]))
+    for h in range(len(q)):
+        lg = [scale * float(np.dot(q[h], keys[t])) for t in toks]
+        mx = max(lg)
+        w = [math.exp(v - mx) for v in lg]
+        z = sum(w)
+        for i, t in enumerate(toks):
+            out[h] += (w[i] / z) * vals[t]
+    return out
+
+
+def check_row_trajectory(O):
+    """OracleRow over decode steps that fill blocks, in ascending and ordered
+    mode.  At every step: its representatives and eviction scores (grown
+    incrementally) equal exact-rational ones computed from scratch; the
+    eviction set is the global top-k_e by E; the selection is the sort-based
+    top of loop-computed scores; gamma is recomputed from the two selections
+    and the previous tail; the output is attention over the selected tokens;
+    in ordered mode the list is the sorted order and n* the brute-force prefix
+    scan."""
+    rng = np.random.default_rng(26)
+    d, G, scale = 3, 2, 0.45
+    nb_final = 9
+    T = 64 * nb_final + 40
+    keys = _bf16_values(rng, (T, d))
+    vals = rng.standard_normal((T, d))
+    logits = rng.standard_normal(T).astype(np.float32).astype(np.float64)
+    want_reps, want_E = _expected_reps_and_E(keys, logits, nb_final)
+    L0 = 64 * 4 + 50                       # blocks 4, 5, ... fill along the way
+    steps = 64 * nb_final - L0 + 20
+
+    for k, k_e in ((5, 3), (4, 4)):
+        row = O.OracleRow(keys, vals, logits, "bf16", scale, k=k, k_e=k_e)
+        prev_sel, prev_tail = None, None
+        for t in range(0, steps, 3):       # several steps skipped: fills arrive in bulk too
+            L = L0 + t + 1
+            nb = L // 64
+            q = rng.standard_normal((G, d))
+            res = row.step(L, q)
+            assert np.array_equal(row.reps(nb), want_reps[:nb]), ("reps", t)
+            assert np.array_equal(row.eviction_scores(nb), want_E[:nb]), ("E", t)
+            ev = sorted(sorted(range(nb), key=lambda i: (-want_E[i], i))[:k_e])
+            assert res["evict_set"].tolist() == ev, ("evict", t)
+            S = _loop_scores(q, want_reps[:nb], scale)
+            rest = [i for i in range(nb) if i not in ev]
+            qa = sorted(rest, key=lambda i: (-S[i], i))[:min(k - len(ev), len(rest))]
+            sel = sorted(ev + qa)
+            assert res["selected"].tolist() == sel, ("selected", t)
+            toks = [t_ for b in sel for t_ in range(64 * b, 64 * b + 64)] + list(range(64 * nb, L))
+            assert np.allclose(res["out"], _attend_tokens(q, keys, vals, toks, scale),
+                               rtol=0, atol=1e-12), ("out", t)
+            if prev_sel is not None:
+                resident = set(prev_sel) | ({prev_tail} if prev_tail is not None else set())
+                assert res["gamma"] == len(set(sel) & resident) / len(sel), ("gamma", t)
+            else:
+                assert "gamma" not in res
+            prev_sel, prev_tail = sel, (nb if L % 64 else None)
+
+    tau, cap = 0.2, 6
+    row = O.OracleRow(keys, vals, logits, "bf16", scale, k=cap, ordered=True, tau=tau)
+    fired = 0
+    for t in range(0, steps, 5):
+        L = L0 + t + 1
+        nb = L // 64
+        q = 1.5 * rng.standard_normal((G, d))
+        res = row.step(L, q)
+        assert np.array_equal(row.reps(nb), want_reps[:nb]), ("ordered reps", t)
+        S = _loop_scores(q, want_reps[:nb], scale)
+        order = sorted(range(nb), key=lambda i: (-S[i], i))[:cap]
+        assert res["selected"].tolist() == order, ("ordered list", t)
+        n = brute_stop_index(q, keys, order, L, tau, scale)
+        assert res["n_star"] == n, ("n*", t)
+        fired += n < len(order)
+        toks = [t_ for b in order[:n] for t_ in range(64 * b, 64 * b + 64)] + list(range(64 * nb, L))
+        assert np.allclose(res["out"], _attend_tokens(q, keys, vals, toks, scale),
+                           rtol=0, atol=1e-12), ("ordered out", t)
+    assert fired >= 10, fired        # the stop fires before the end of the list
+
+
 ALL_CHECKS = [
     check_round, check_rne_fraction, check_rounded_means, check_reps_layout,
     check_eviction_scores, check_scores_bruteforce, check_scores_closed_forms,
     check_forecast, check_topk_exchange, check_selection_golden, check_select_bruteforce,
     check_eviction_incremental, check_dense_reduction, check_attend_loops,
-    check_early_stop, check_locality,
+    check_early_stop, check_locality, check_row_trajectory,
 ]

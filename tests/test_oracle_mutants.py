@@ -119,10 +119,66 @@ def mut_gamma_ignores_tail(O):
     O.locality = f
 
 
+def mut_row_reps_from_previous_block(O):
+    """The incremental representatives extend from block n0 - 1 instead of n0."""
+    def reps(self, nb):
+        if self._reps.shape[0] < nb:
+            n0 = self._reps.shape[0]
+            new = O.block_reps(self.keys[max(n0 - 1, 0) * 64:], nb - n0, self.storage)
+            self._reps = np.concatenate([self._reps, new])
+        return self._reps[:nb]
+    O.OracleRow.reps = reps
+
+
+def mut_row_eviction_from_previous_block(O):
+    """The incremental eviction scores extend from block n0 - 1 instead of n0."""
+    def eviction_scores(self, nb):
+        if self._E.shape[0] < nb:
+            n0 = self._E.shape[0]
+            new = O.eviction_block_scores(self.logits[max(n0 - 1, 0) * 64:], nb - n0)
+            self._E = np.concatenate([self._E, new])
+        return self._E[:nb]
+    O.OracleRow.eviction_scores = eviction_scores
+
+
+def mut_row_prev_tail_off_by_one(O):
+    """The step records the block before the tail as the previous tail."""
+    orig = O.OracleRow.step
+
+    def step(self, L, q, f=None, attend_out=True):
+        res = orig(self, L, q, f=f, attend_out=attend_out)
+        if self.state.prev_tail_block is not None:
+            self.state.prev_tail_block -= 1
+        return res
+    O.OracleRow.step = step
+
+
+def mut_row_ordered_stop_ignored(O):
+    """The ordered branch attends the whole list (no early stop)."""
+    orig = O.early_stop_attention
+
+    def f(q, keys, values, order, L, tau, scale):
+        return orig(q, keys, values, order, L, 0.0, scale)
+    orig_step = O.OracleRow.step
+
+    def step(self, L, q, f_=None, attend_out=True, **kw):
+        if self.ordered:
+            saved = O.early_stop_attention
+            O.early_stop_attention = f
+            try:
+                return orig_step(self, L, q, attend_out=attend_out, **kw)
+            finally:
+                O.early_stop_attention = saved
+        return orig_step(self, L, q, f_, attend_out=attend_out, **kw)
+    O.OracleRow.step = step
+
+
 MUTANTS = [mut_no_softmax, mut_max_before_head_sum, mut_ties_to_higher_id, mut_tail_dropped,
            mut_stop_block_excluded, mut_sub_block_shift, mut_eviction_forgets_old,
            mut_attention_unscaled, mut_round_truncates, mut_parts_overlap, mut_mean_by_15,
-           mut_gamma_ignores_tail]
+           mut_gamma_ignores_tail, mut_row_reps_from_previous_block,
+           mut_row_eviction_from_previous_block, mut_row_prev_tail_off_by_one,
+           mut_row_ordered_stop_ignored]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
