@@ -67,7 +67,13 @@ def parse():
                     help="the MIB of the --copy-calibration run read by --traffic-from")
     ap.add_argument("--path", default="fused", choices=("fused", "split"),
                     help="fused: one nsa_decode_step launch; split: nsa_select_blocks + "
-                         "nsa_sparse_decode")
+                         "nsa_sparse_decode (the only path of the ordered early-stop mode)")
+    ap.add_argument("--dense", action="store_true",
+                    help="early-stop workload only: the dense reference, nsa_sparse_decode over "
+                         "every full block with no scoring")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps one by one instead of replaying them as one "
+                         "captured HIP graph")
     return ap.parse_args()
 
 
@@ -138,12 +144,17 @@ def gpu_leg(args, cfg):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    dense = args.dense
+    fused = args.path == "fused" and not cfg.ordered and not dense
+    L0 = cfg.seq_len(0)
     kp, vp = to_dev(batch.k_pool), to_dev(batch.v_pool)
     table = torch.from_numpy(batch.table).to(dev)
     logits = torch.from_numpy(batch.logits).to(dev)
+    del batch
     pool_bytes = 2 * kp.numel() * kp.element_size()
-    R = args.instances or max(2, min(16, math.ceil((1 << 30) / max(1, select_bytes(cfg, cfg.seq_len(0))
-                                                                    + decode_bytes(cfg, cfg.seq_len(0), cfg.k)))))
+    work = (decode_bytes(cfg, L0, cfg.nb0) if dense
+            else select_bytes(cfg, L0) + decode_bytes(cfg, L0, cfg.k))
+    R = args.instances or max(2, min(16, math.ceil((1 << 30) / max(1, work))))
     free = torch.cuda.mem_get_info()[0]
     R = max(1, min(R, int(0.6 * free // max(1, pool_bytes))))
     layers = []
@@ -158,9 +169,10 @@ def gpu_leg(args, cfg):
         lay.v_pool.copy_(vp)
         lay.block_table.copy_(table)
         lay.evict_logits.copy_(logits)
-        first = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
-        num = torch.full((cfg.batch,), cfg.nb0, dtype=torch.int32, device=dev)
-        lay.update_reps(first, num, cfg.nb0)
+        if not dense:
+            first = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
+            num = torch.full((cfg.batch,), cfg.nb0, dtype=torch.int32, device=dev)
+            lay.update_reps(first, num, cfg.nb0)
         layers.append(lay)
     del kp, vp
     torch.cuda.synchronize()
@@ -176,29 +188,46 @@ def gpu_leg(args, cfg):
     fill_first = [torch.full((cfg.batch,), cfg.seq_len(t) // 64 - 1, dtype=torch.int32, device=dev)
                   for t in range(steps)]
     ones = torch.ones(cfg.batch, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-    fused = args.path == "fused" and not cfg.ordered
+    if dense:
+        nbd = L0 // 64
+        sel_all = torch.arange(nbd, dtype=torch.int32, device=dev).repeat(
+            cfg.batch, cfg.num_kv_heads, 1).contiguous()
+        nsel_all = torch.full((cfg.batch, cfg.num_kv_heads), nbd, dtype=torch.int32, device=dev)
 
+    # every launch goes to the current stream (the capture stream while a
+    # graph is being captured)
     def step(i, ev=None):
         lay = layers[i % R]
         t = i % steps
         lay.seq_lens = lens[t]
-        if fills[t]:
-            lay.update_reps(fill_first[t], ones, 1, stream)
+        if fills[t] and not dense:
+            lay.update_reps(fill_first[t], ones, 1)
         if ev is not None:
-            ev[0].record(stream)
-        if fused:
-            lay.step(sel_q[t], qs[t], cfg.seq_len(t), stream)
+            ev[0].record()
+        if dense:
+            lay.decode(qs[t], selected=sel_all, num_selected=nsel_all, max_selected=nbd,
+                       early_stop=False)
             if ev is not None:
-                ev[1].record(stream)
-                ev[2].record(stream)
+                ev[1].record()
+                ev[2].record()
             return
-        lay.select(sel_q[t], cfg.seq_len(t), stream)
+        if fused:
+            lay.step(sel_q[t], qs[t], cfg.seq_len(t))
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
+        lay.select(sel_q[t], cfg.seq_len(t))
         if ev is not None:
-            ev[1].record(stream)
-        lay.decode(qs[t], stream)
+            ev[1].record()
+        lay.decode(qs[t])
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record()
+
+    def check_status():
+        if fused:
+            for lay in layers:
+                lay.check_step()     # raises when a wait of a fused step expired
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -208,37 +237,113 @@ def gpu_leg(args, cfg):
         torch.mul(src, 1.0, out=dst)  # reads and writes n * 4 bytes
         torch.cuda.synchronize()
         del src, dst
+    # set-up: one step per instance, so that each instance's first call (the
+    # eviction-set update over the prefilled blocks) is never timed
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    check_status()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # the K timed steps: nothing but the steps between the two events
+    base = args.warmup
+    graph = None
+    if not args.no_graph:
+        # the K timed steps captured once as a HIP graph; one untimed replay
+        # uploads it, the timed replay runs the same K steps again
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(base + i)
+        graph.replay()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record(stream)
+    start.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(base + i)
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
-    # per-kernel durations: the same steps again with events around each launch
-    # on the launch stream (an event between launches adds a small gap, so
-    # this pass is kept apart from the timed one)
+    check_status()
+    del graph
+    # per-kernel durations: the same steps again, launched one by one with
+    # events around each launch on the launch stream (an event between
+    # launches adds a small gap, so this pass is kept apart from the timed one)
     n_ev = min(args.steps, 1000)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     for i in range(n_ev):
-        step(args.warmup + args.steps + i, evs[i])
+        step(base + args.steps + i, evs[i])
     torch.cuda.synchronize()
+    check_status()
     sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ev
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_ev
 
-    n_sel = layers[0].num_selected.float().mean().item()
+    metrics = {}
     L_mid = cfg.seq_len(steps // 2)
-    sb = select_bytes(cfg, L_mid)
-    db = decode_bytes(cfg, L_mid, int(round(n_sel)))
+    if dense:
+        n_blocks = nbd
+        sb, db = 0, decode_bytes(cfg, L_mid, n_blocks)
+        metrics["blocks_attended"] = n_blocks
+    elif cfg.ordered:
+        n_star = torch.cat([lay.num_processed.flatten() for lay in layers]).float()
+        n_blocks = n_star.mean().item()
+        sb, db = select_bytes(cfg, L_mid), decode_bytes(cfg, L_mid, n_blocks)
+        metrics["n_star"] = {"mean": round(n_blocks, 2), "min": int(n_star.min().item()),
+                             "max": int(n_star.max().item()), "cap": cfg.k}
+    else:
+        n_blocks = layers[0].num_selected.float().mean().item()
+        sb, db = select_bytes(cfg, L_mid), decode_bytes(cfg, L_mid, n_blocks)
+        metrics.update(locality_metrics(layers[0], cfg, lens, sel_q, qs, fused))
     return dict(R=R, total_ms=total_ms, wall_s=wall, sel_ms=sel_ms, dec_ms=dec_ms,
-                sel_bytes=sb, dec_bytes=db, n_sel=n_sel, fused=fused)
+                sel_bytes=sb, dec_bytes=db, n_blocks=n_blocks, fused=fused, dense=dense,
+                graph=not args.no_graph, metrics=metrics)
+
+
+def locality_metrics(lay, cfg, lens, sel_q, qs, fused):
+    """Untimed: one instance through every decode step of the workload again;
+    after each step the library's residency diff gives the blocks to fetch
+    (selected now, not resident after the previous step) and to release."""
+    import torch
+    import block_sparse_kv_nsa_amd as N
+    if not hasattr(N, "nsa_residency_diff"):
+        return {}
+    dev = lay.device
+    prev_sel = lay.selected.clone()
+    prev_num = lay.num_selected.clone()
+    prev_lens = lens[-1].clone()
+    fetch = torch.empty_like(lay.selected)
+    release = torch.empty((cfg.batch, cfg.num_kv_heads, cfg.k + 1), dtype=torch.int32, device=dev)
+    n_fetch = torch.empty_like(lay.num_selected)
+    n_release = torch.empty_like(lay.num_selected)
+    gamma = torch.empty((cfg.batch, cfg.num_kv_heads), dtype=torch.float32, device=dev)
+    g_min, f_tot, r_tot, f_max = 1.0, 0, 0, 0
+    for t in range(cfg.steps):
+        lay.seq_lens = lens[t]
+        if fused:
+            lay.step(sel_q[t], qs[t], cfg.seq_len(t))
+        else:
+            lay.select(sel_q[t], cfg.seq_len(t))
+            lay.decode(qs[t])
+        lay.residency_diff(prev_sel, prev_num, prev_lens, fetch, n_fetch, release, n_release, gamma)
+        g_min = min(g_min, gamma.min().item())
+        f_tot += int(n_fetch.sum().item())
+        f_max = max(f_max, int(n_fetch.max().item()))
+        r_tot += int(n_release.sum().item())
+        prev_sel.copy_(lay.selected)
+        prev_num.copy_(lay.num_selected)
+        prev_lens = lens[t]
+    if fused:
+        lay.check_step()
+    n = cfg.steps * cfg.rows
+    return {"gamma_min": round(g_min, 4), "fetch_blocks_per_row_step": round(f_tot / n, 3),
+            "fetch_blocks_max": f_max, "release_blocks_per_row_step": round(r_tot / n, 3),
+            "gamma_bound": round(cfg.k_e / cfg.k, 4) if cfg.k_e else None}
 
 
 # ----------------------------------------------------------------------------
@@ -250,11 +355,13 @@ def cpu_leg(args, cfg):
     import workloads as W
     from oracle import nsa_oracle as O
 
+    host_cpus = os.cpu_count() or 1
+    threads = min(host_cpus, 16)
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        threads = 1
+        limiter = None
     rows = [(b, g) for b in range(cfg.batch) for g in range(cfg.num_kv_heads)]
     rng = np.random.default_rng(5)
     order = [rows[i] for i in rng.permutation(len(rows))][:args.cpu_rows]
@@ -265,29 +372,45 @@ def cpu_leg(args, cfg):
         row = O.OracleRow(W.stored_to_f64(ri.keys, cfg.dtype), W.stored_to_f64(ri.values, cfg.dtype),
                           ri.logits.astype(np.float64), cfg.dtype, 1.0 / math.sqrt(cfg.head_dim),
                           mode=cfg.mode, k=cfg.k, k_e=cfg.k_e, ordered=cfg.ordered, tau=cfg.tau)
-        row.reps(cfg.nb0)
-        if cfg.k_e:
-            row.eviction_scores(cfg.nb0)
+        if not args.dense:
+            row.reps(cfg.nb0)
+            if cfg.k_e:
+                row.eviction_scores(cfg.nb0)
         qs = [W.stored_to_f64(W.query_row(cfg, b, g, t), cfg.dtype) for t in range(cfg.steps)]
         f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode == "forecast" else None
         sample.append((row, qs, f))
-    # the workload's decode steps on the sampled rows, repeated until the
-    # budget is spent (a repeated step does the same work: no block fills)
-    spent, done, passes = 0.0, 0, 0
-    while spent < args.cpu_seconds:
+
+    def one_pass():
+        t0 = time.perf_counter()
         for row, qs, f in sample:
             for t in range(cfg.steps):
-                t0 = time.perf_counter()
-                row.step(cfg.seq_len(t), qs[t], f=f)
-                spent += time.perf_counter() - t0
-                done += 1
-        passes += 1
-    per_row_step = spent / done
+                L = cfg.seq_len(t)
+                if args.dense:
+                    O.dense_attention(qs[t], row.keys, row.values, L, row.scale)
+                else:
+                    row.step(L, qs[t], f=f)
+        return time.perf_counter() - t0
+
+    one_pass()                                   # warm-up
+    # three timed bundles of repeated passes (a repeated step does the same
+    # work: no block fills), each about a third of the budget
+    probe = one_pass()
+    per_bundle = max(1, int(args.cpu_seconds / 3 / max(probe, 1e-6)))
+    times = []
+    for _ in range(3):
+        times.append(sum(one_pass() for _ in range(per_bundle)) / per_bundle)
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_pass = sorted(times)[1]
+    per_row_step = per_pass / (len(sample) * cfg.steps)
     step_s = per_row_step * cfg.rows
-    return {"value": cfg.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} row-steps ({passes} passes over the {cfg.steps} decode steps of "
-                      f"{len(sample)} of {cfg.rows} rows; float64 NumPy, one row at a time), "
-                      f"{spent:.1f}s timed; scaled to all rows"}
+    what = "dense attention over every cached token" if args.dense else "step"
+    return {"value": cfg.batch / step_s, "unit": "tokens/s", "cores": threads,
+            "host_cpus": host_cpus, "kind": "oracle",
+            "sample": f"median of 3 timed bundles (after one warm-up pass) of {per_bundle} passes "
+                      f"over the {cfg.steps} decode steps of {len(sample)} of {cfg.rows} rows "
+                      f"({what}; float64 NumPy, one row at a time, BLAS limited to {threads} "
+                      f"threads); scaled to all rows"}
 
 
 KERNEL_SYMBOLS = {"step": "gang_kernel", "select": "score_select_kernel", "decode": "decode_kernel"}
@@ -355,11 +478,16 @@ def main():
         return 2
     import workloads as W
     cfg = W.config(WORKLOADS[args.workload])
+    if args.dense and not cfg.ordered:
+        print("--dense is the early-stop workload's dense reference", file=sys.stderr)
+        return 2
     g = gpu_leg(args, cfg)
     ms_per_step = g["total_ms"] / args.steps
     value = cfg.batch / (ms_per_step / 1e3)
     if g["fused"]:
         kernels = {"step": {"ms": g["sel_ms"], "bytes": g["sel_bytes"] + g["dec_bytes"]}}
+    elif g["dense"]:
+        kernels = {"decode": {"ms": g["dec_ms"], "bytes": g["dec_bytes"]}}
     else:
         kernels = {
             "select": {"ms": g["sel_ms"], "bytes": g["sel_bytes"]},
@@ -370,8 +498,10 @@ def main():
         k["frac"] = k["GB/s"] / HBM_PEAK_GBS
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
-    traffic = traffic_from_profiles(args.workload, dom)
+    workload = cfg.name + ("-dense" if g["dense"] else "")
+    traffic = traffic_from_profiles(workload, dom)
     step_bytes = g["sel_bytes"] + g["dec_bytes"]
+    kernel_ms = sum(v["ms"] for v in kernels.values())
     line = {
         "metric": "sparse decode tokens/s + achieved HBM GB/s (% of peak) at 32K-128K ctx, 1 GPU",
         "value": round(value, 1),
@@ -385,10 +515,13 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.context,
+        "config": {"workload": workload, "batch": cfg.batch, "context": cfg.context,
                    "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "k": cfg.k, "k_e": cfg.k_e, "mode": cfg.mode,
+                   "ordered": cfg.ordered, "tau": cfg.tau,
+                   "path": "fused" if g["fused"] else ("dense" if g["dense"] else "split"),
                    "decode_steps_cycled": cfg.steps, "layer_instances": g["R"],
+                   "timed_as": "one HIP graph of the K steps" if g["graph"] else "K launches",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dk["GB/s"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dk["frac"], 4),
@@ -397,6 +530,8 @@ def main():
                      "frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernels": {k: {"ms": round(v["ms"], 5), "bytes": v["bytes"], "GB/s": round(v["GB/s"], 1),
                         "frac": round(v["frac"], 4)} for k, v in kernels.items()},
+        "launch_gap_us": round((ms_per_step - kernel_ms) * 1e3, 2),
+        "metrics": g["metrics"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_leg(args, cfg)

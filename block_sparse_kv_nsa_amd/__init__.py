@@ -11,6 +11,7 @@ from ._abi import (  # noqa: F401
     NSA_BF16,
     NSA_ERR_HIP,
     NSA_ERR_INVALID_ARGUMENT,
+    NSA_ERR_STEP_EXPIRED,
     NSA_ERR_UNSUPPORTED,
     NSA_ERR_WORKSPACE_TOO_SMALL,
     NSA_F32,
@@ -24,9 +25,11 @@ from ._abi import (  # noqa: F401
     load,
     nsa_abi_version,
     nsa_decode_step,
+    nsa_decode_step_status,
     nsa_decode_step_workspace_bytes,
     nsa_decode_workspace_bytes,
     nsa_last_error,
+    nsa_residency_diff,
     nsa_select_blocks,
     nsa_select_workspace_bytes,
     nsa_sparse_decode,

@@ -23,6 +23,7 @@ NSA_ERR_INVALID_ARGUMENT = 1
 NSA_ERR_UNSUPPORTED = 2
 NSA_ERR_WORKSPACE_TOO_SMALL = 3
 NSA_ERR_HIP = 4
+NSA_ERR_STEP_EXPIRED = 5
 
 NSA_F32 = 0
 NSA_BF16 = 1
@@ -38,6 +39,8 @@ EXPORTS = (
     "nsa_sparse_decode",
     "nsa_decode_step_workspace_bytes",
     "nsa_decode_step",
+    "nsa_decode_step_status",
+    "nsa_residency_diff",
     "nsa_status_string",
     "nsa_last_error",
     "nsa_abi_version",
@@ -119,6 +122,10 @@ def load() -> ctypes.CDLL:
     lib.nsa_decode_step.argtypes = [P(Shape), P(SelectParams), vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                     vp, vp, vp, vp, vp, vp, sz, vp]
     lib.nsa_decode_step.restype = i32
+    lib.nsa_decode_step_status.argtypes = [vp, sz, i32, vp]
+    lib.nsa_decode_step_status.restype = i32
+    lib.nsa_residency_diff.argtypes = [P(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.nsa_residency_diff.restype = i32
     lib.nsa_status_string.argtypes = [i32]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []
@@ -232,3 +239,23 @@ def nsa_decode_step(shape: Shape, params: SelectParams, query, q, reps, evict_bl
                                 _ptr(num_selected), _ptr(out), _ptr(workspace),
                                 int(workspace_bytes), _stream(stream))
     _check(st, "nsa_decode_step")
+
+
+def nsa_decode_step_status(workspace, workspace_bytes: int, clear: bool = True,
+                           stream=None) -> None:
+    """Raises NsaError(NSA_ERR_STEP_EXPIRED) when a wait of a fused step run on
+    this workspace expired (synchronises the stream)."""
+    st = load().nsa_decode_step_status(_ptr(workspace), int(workspace_bytes), int(bool(clear)),
+                                       _stream(stream))
+    _check(st, "nsa_decode_step_status")
+
+
+def nsa_residency_diff(shape: Shape, max_selected: int, prev_selected, prev_num_selected,
+                       prev_seq_lens, selected, num_selected, fetch, num_fetch, release,
+                       num_release, gamma=None, stream=None) -> None:
+    st = load().nsa_residency_diff(ctypes.byref(shape), int(max_selected), _ptr(prev_selected),
+                                   _ptr(prev_num_selected), _ptr(prev_seq_lens), _ptr(selected),
+                                   _ptr(num_selected), _ptr(fetch), _ptr(num_fetch),
+                                   _ptr(release), _ptr(num_release), _ptr(gamma),
+                                   _stream(stream))
+    _check(st, "nsa_residency_diff")

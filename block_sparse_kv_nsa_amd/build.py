@@ -25,7 +25,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
 
-SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip", "nsa_step.hip"]
+SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip", "nsa_step.hip",
+           "nsa_residency.hip"]
 ARCH = "gfx950"
 
 

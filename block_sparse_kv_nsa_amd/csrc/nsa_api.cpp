@@ -126,6 +126,7 @@ const char* nsa_status_string(nsa_status st) {
     case NSA_ERR_UNSUPPORTED: return "NSA_ERR_UNSUPPORTED";
     case NSA_ERR_WORKSPACE_TOO_SMALL: return "NSA_ERR_WORKSPACE_TOO_SMALL";
     case NSA_ERR_HIP: return "NSA_ERR_HIP";
+    case NSA_ERR_STEP_EXPIRED: return "NSA_ERR_STEP_EXPIRED";
   }
   return "NSA_ERR_UNKNOWN";
 }
@@ -417,6 +418,67 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
     std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d gang=%d (0: by occupancy)\n", lay.rows,
                  lay.nb_max, L.gang_override);
   return launched(fn, nsa::launch_step(L, stream));
+}
+
+nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,
+                              const int32_t* prev_selected, const int32_t* prev_num_selected,
+                              const int32_t* prev_seq_lens, const int32_t* selected,
+                              const int32_t* num_selected, int32_t* fetch, int32_t* num_fetch,
+                              int32_t* release, int32_t* num_release, float* gamma,
+                              hipStream_t stream) {
+  const char* fn = "nsa_residency_diff";
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  if (max_selected < 1 || max_selected > kMaxK)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: max_selected %d outside [1, %d]", fn, max_selected,
+                kMaxK);
+  NSA_REQUIRE_PTR(prev_selected, 4);
+  NSA_REQUIRE_PTR(prev_num_selected, 4);
+  NSA_REQUIRE_PTR(prev_seq_lens, 4);
+  NSA_REQUIRE_PTR(selected, 4);
+  NSA_REQUIRE_PTR(num_selected, 4);
+  NSA_REQUIRE_PTR(fetch, 4);
+  NSA_REQUIRE_PTR(num_fetch, 4);
+  NSA_REQUIRE_PTR(release, 4);
+  NSA_REQUIRE_PTR(num_release, 4);
+  if (gamma) NSA_REQUIRE_PTR(gamma, 4);
+  nsa::ResidencyLaunch L{};
+  L.prev_selected = prev_selected;
+  L.prev_num = prev_num_selected;
+  L.prev_seq_lens = prev_seq_lens;
+  L.selected = selected;
+  L.num = num_selected;
+  L.fetch = fetch;
+  L.num_fetch = num_fetch;
+  L.release = release;
+  L.num_release = num_release;
+  L.gamma = gamma;
+  L.rows = shape->batch * shape->num_kv_heads;
+  L.Hkv = shape->num_kv_heads;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.max_selected = max_selected;
+  return launched(fn, nsa::launch_residency(L, stream));
+}
+
+nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32_t clear,
+                                  hipStream_t stream) {
+  const char* fn = "nsa_decode_step_status";
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (workspace_bytes < 256)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: workspace_bytes %zu < 256", fn, workspace_bytes);
+  uint32_t word = 0;
+  const char* base = static_cast<const char*>(workspace);
+  hipError_t e = hipMemcpyAsync(&word, base + 4 * nsa::kErr, sizeof(word), hipMemcpyDeviceToHost,
+                                stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  if (word == 0) return ok();
+  if (clear) {
+    e = hipMemsetAsync(workspace, 0, workspace_bytes, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(NSA_ERR_HIP, "%s: clearing: %s", fn, hipGetErrorString(e));
+  }
+  return fail(NSA_ERR_STEP_EXPIRED, "%s: a wait of the fused step expired (error word %u)%s", fn,
+              word, clear ? "; workspace cleared" : "");
 }
 
 }  // extern "C"

@@ -260,4 +260,22 @@ struct StepLaunch {
 };
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// residency diff between consecutive selections
+// ---------------------------------------------------------------------------
+struct ResidencyLaunch {
+  const int32_t* prev_selected;  // [rows][max_selected]
+  const int32_t* prev_num;       // [rows]
+  const int32_t* prev_seq_lens;  // [B]
+  const int32_t* selected;       // [rows][max_selected]
+  const int32_t* num;            // [rows]
+  int32_t* fetch;                // [rows][max_selected]
+  int32_t* num_fetch;            // [rows]
+  int32_t* release;              // [rows][max_selected + 1]
+  int32_t* num_release;          // [rows]
+  float* gamma;                  // [rows] or NULL
+  int rows, Hkv, max_blocks, max_selected;
+};
+hipError_t launch_residency(const ResidencyLaunch& L, hipStream_t stream);
+
 }  // namespace nsa

@@ -619,9 +619,15 @@ struct Gang {
     for (int t = n_e + m_row + threadIdx.x; t < a.k; t += kThreads) sel[t] = -1;
     if (threadIdx.x == 0) a.num_selected[row] = n_e + m_row;
 
-    if (wave == 0)
+    if (wave == 0) {
       wave_poll_pairs<NP>(mlr, st_off, C * G, err, a.wait_ticks, [&](int, f32x2) {});
+      // an expired wait anywhere in the gang (each member records its own
+      // before publishing its partial) leaves the eviction state untouched,
+      // so that the step can be run again from the same state
+      if (lane == 0) sm.s_int[0] = (int)ld_agent(err);
+    }
     __syncthreads();
+    const bool failed = sm.s_int[0] != 0;
     // every member's partial is in, so every member is done with the row's
     // statistics and keys: clear those slots (the partials' after the merge)
     if (!FORECAST)
@@ -635,7 +641,7 @@ struct Gang {
 
     // the eviction state, when it changed: every member has read the old one
     // (its partial is in)
-    if (!steady) {
+    if (!steady && !failed) {
       for (int i = threadIdx.x; i < a.k_e; i += kThreads)
         a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
       if (threadIdx.x == 0) a.evict_seen[row] = nb;

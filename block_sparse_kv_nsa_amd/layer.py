@@ -59,8 +59,19 @@ class SparseDecodeLayer:
         self.sel_ws_bytes = A.nsa_select_workspace_bytes(self.shape, self.sel_params, cap)
         self.dec_ws_bytes = A.nsa_decode_workspace_bytes(self.shape, self.dec_params)
         self.sel_ws = torch.zeros(self.sel_ws_bytes, dtype=torch.uint8, device=dev)
-        self.step_ws, self.step_ws_bytes = None, 0
         self.dec_ws = torch.zeros(self.dec_ws_bytes, dtype=torch.uint8, device=dev)
+        # the fused step's workspace (ascending mode only), zeroed once here:
+        # every completed step leaves its hand-off slots zero again
+        self.step_ws, self.step_ws_bytes = None, 0
+        if not ordered:
+            try:
+                self.step_ws_bytes = A.nsa_decode_step_workspace_bytes(self.shape, self.sel_params,
+                                                                       cap)
+            except A.NsaError as e:
+                if e.status != A.NSA_ERR_UNSUPPORTED:
+                    raise
+            else:
+                self.step_ws = torch.zeros(self.step_ws_bytes, dtype=torch.uint8, device=dev)
 
     # -- the three calls ---------------------------------------------------
     def update_reps(self, first_block: torch.Tensor, num_blocks: torch.Tensor,
@@ -94,11 +105,12 @@ class SparseDecodeLayer:
                             self.num_processed, self.out, self.dec_ws, self.dec_ws_bytes, stream)
 
     def step(self, query: torch.Tensor, q: torch.Tensor, max_seq_len: int, stream=None) -> None:
-        """Selection and decode in one launch (ascending mode)."""
+        """Selection and decode in one launch (ascending mode).  Enqueues only:
+        call check_step() where the results are consumed."""
         if self.step_ws is None:
-            self.step_ws_bytes = A.nsa_decode_step_workspace_bytes(self.shape, self.sel_params,
-                                                                   64 * self.max_blocks)
-            self.step_ws = torch.zeros(self.step_ws_bytes, dtype=torch.uint8, device=self.device)
+            raise A.NsaError(A.NSA_ERR_UNSUPPORTED,
+                             "nsa_decode_step: not available for this layer (ordered mode, or "
+                             "a context above the fused step's limit)")
         ke = self.k_e > 0
         A.nsa_decode_step(self.shape, self.sel_params, query, q, self.reps,
                           self.evict_scores if ke else None, self.k_pool, self.v_pool,
@@ -106,6 +118,22 @@ class SparseDecodeLayer:
                           self.evict_set if ke else None, self.evict_seen if ke else None,
                           self.selected, self.num_selected, self.out, self.step_ws,
                           self.step_ws_bytes, stream)
+
+    def residency_diff(self, prev_selected, prev_num_selected, prev_seq_lens, fetch, num_fetch,
+                       release, num_release, gamma=None, stream=None) -> None:
+        """Blocks to fetch and to release from the previous selection (given)
+        to the current one (this layer's selected / num_selected)."""
+        A.nsa_residency_diff(self.shape, self.k, prev_selected, prev_num_selected, prev_seq_lens,
+                             self.selected, self.num_selected, fetch, num_fetch, release,
+                             num_release, gamma, stream)
+
+    def check_step(self, stream=None) -> None:
+        """Raise NsaError(NSA_ERR_STEP_EXPIRED) if a wait of a fused step on
+        this layer expired since the last check (synchronises the stream; the
+        workspace is cleared, and the eviction state is the one before the
+        failed step, so the step can be run again)."""
+        if self.step_ws is not None:
+            A.nsa_decode_step_status(self.step_ws, self.step_ws_bytes, True, stream)
 
     def reset_state(self) -> None:
         self.evict_set.fill_(-1)

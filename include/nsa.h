@@ -55,14 +55,16 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 2
+#define NSA_ABI_VERSION 3
 
 typedef enum nsa_status {
   NSA_OK = 0,
   NSA_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, bad size or value */
   NSA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, group size, ... */
   NSA_ERR_WORKSPACE_TOO_SMALL = 3,
-  NSA_ERR_HIP = 4                 /* a kernel launch failed */
+  NSA_ERR_HIP = 4,                /* a kernel launch (or a HIP call of a status query) failed */
+  NSA_ERR_STEP_EXPIRED = 5        /* a wait inside the fused step expired (see
+                                     nsa_decode_step_status) */
 } nsa_status;
 
 typedef enum nsa_dtype { NSA_F32 = 0, NSA_BF16 = 1 } nsa_dtype;
@@ -240,10 +242,13 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  * call leaves its hand-off slots zero again (partial accumulators may keep
  * data, which is never read as a slot), so it is zeroed only once, and one
  * workspace serves calls with any max_seq_len up to the one it was sized for.
- * Every wait is bounded: 32-bit word 2 (bytes 8-11) is an error word,
- * sticky, set nonzero when a wait expired (results of such a call are
- * undefined, and the workspace must be zeroed again before the next call;
- * the two-call path gives the results without the residency assumption).
+ * Every wait is bounded (0.2 s): 32-bit word 2 (bytes 8-11) of the workspace
+ * is an error word, sticky, set nonzero when a wait expired.  The outputs of
+ * such a call (out, selected, num_selected) are undefined; the eviction state
+ * (evict_set, evict_seen) is left as the call found it, so the step can be
+ * run again (nsa_select_blocks + nsa_sparse_decode give the same results
+ * without the residency assumption).  nsa_decode_step_status reports the
+ * word to the host and clears the workspace.
  * max_seq_len is limited to 524288 tokens (NSA_ERR_UNSUPPORTED above).
  * ------------------------------------------------------------------------ */
 nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
@@ -257,6 +262,48 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
                            int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
                            void* out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Residency diff between consecutive selections (NOSA summary, "2. Sistema:
+ * NOSI": the cache is kept in block units and a step moves only what its
+ * selection changes; "Garantia de Localidad": the eviction part keeps
+ * gamma(t) >= k_e / k).
+ *
+ * For every row, A = the first prev_num_selected[row] ids of
+ * prev_selected[row] plus the previous step's partial tail block
+ * prev_seq_lens[b] / 64 when prev_seq_lens[b] % 64 != 0 (that step attended
+ * it), and S = the first num_selected[row] ids of selected[row]:
+ *   fetch[row]       S minus A, ascending; num_fetch[row] ids, the rest -1
+ *   release[row]     A minus S, ascending; num_release[row] ids, the rest -1
+ *   gamma[row]       |S and A| / |S| (1 when S is empty)
+ * Ids outside [0, max_blocks_per_seq) are ignored; a repeated id counts once.
+ *
+ *   max_selected     row stride of prev_selected, selected and fetch; 1..4096
+ *   prev_selected, selected      [B][Hkv][max_selected] int32 (any order)
+ *   prev_num_selected, num_selected   [B][Hkv] int32 (clamped to [0, max_selected])
+ *   prev_seq_lens    [B] int32, tokens cached at the previous step
+ *   fetch            [B][Hkv][max_selected] int32 out
+ *   release          [B][Hkv][max_selected + 1] int32 out
+ *   num_fetch, num_release   [B][Hkv] int32 out
+ *   gamma            [B][Hkv] float32 out, may be NULL
+ * ------------------------------------------------------------------------ */
+nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,
+                              const int32_t* prev_selected, const int32_t* prev_num_selected,
+                              const int32_t* prev_seq_lens, const int32_t* selected,
+                              const int32_t* num_selected, int32_t* fetch, int32_t* num_fetch,
+                              int32_t* release, int32_t* num_release, float* gamma,
+                              hipStream_t stream);
+
+/* Status of the fused steps run on `workspace` since it was last cleared.
+ * Waits for the work queued on `stream` (a host synchronisation: call it
+ * where a step's results are consumed, not between steps), then reads the
+ * workspace's error word.  Returns NSA_OK when every wait of those steps
+ * ended normally, NSA_ERR_STEP_EXPIRED when one expired; with clear != 0 the
+ * whole workspace is then zeroed (on `stream`, waited for), ready for the
+ * next call.  NSA_ERR_INVALID_ARGUMENT for a NULL or misaligned workspace or
+ * workspace_bytes < 256; NSA_ERR_HIP when a HIP call fails. */
+nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32_t clear,
+                                  hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* nsa_status_string(nsa_status status);

@@ -341,6 +341,24 @@ def locality(selected, prev_selected, prev_tail_block) -> float:
     return len(sel & resident) / len(sel)
 
 
+def residency_diff(selected, prev_selected, prev_tail_block):
+    """Blocks to fetch and to release between consecutive steps: (fetch, release).
+
+    NOSA summary, "2. Sistema: NOSI": with the cache kept in block units, a
+    step moves only what its selection adds to, or drops from, the blocks
+    already in place; "Garantía de Localidad" bounds how much that is.
+    Reading: the resident set after step t-1 is its selection plus its
+    partial tail block (attended then); fetch = S_t minus that set, release =
+    that set minus S_t, both ascending.  1 - |fetch|/|S_t| is gamma(t).
+    """
+    S = np.unique(np.asarray(selected, dtype=np.int64))
+    A = np.asarray(prev_selected, dtype=np.int64)
+    if prev_tail_block is not None:
+        A = np.concatenate([A, np.array([prev_tail_block], dtype=np.int64)])
+    A = np.unique(A)
+    return np.setdiff1d(S, A), np.setdiff1d(A, S)
+
+
 # =============================================================================
 # One decode step of one row, with the state that crosses steps
 # =============================================================================

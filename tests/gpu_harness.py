@@ -117,9 +117,16 @@ def run_step(layer, cfg: W.Config, step: int, seq_lens=None, fused: bool = False
 
 
 def step_error_word(layer) -> int:
-    """The fused step's sticky error word (workspace word 2)."""
+    """The fused step's sticky error word (workspace word 2), read raw."""
     torch.cuda.synchronize()
     return int(layer.step_ws[8:12].view(torch.int32).item())
+
+
+def check_step_status(layer) -> None:
+    """Every wait of the fused steps so far ended normally, as the library's
+    status query reports it (raises NsaError otherwise)."""
+    layer.check_step()
+    assert step_error_word(layer) == 0
 
 
 def step_slot_words(layer, cfg: W.Config) -> torch.Tensor:
@@ -287,20 +294,27 @@ def run_and_check(cfg: W.Config, rows=None, check_every: int = 1, batch=None, ro
     for t in range(cfg.steps):
         run_step(layer, cfg, t, fused=fused, max_seq_len=None if max_len is None else max_len(t))
         if fused:
-            assert step_error_word(layer) == 0, f"a stage wait expired at step {t}"
-        if t % check_every and t != cfg.steps - 1:
-            # still advance the oracle's eviction state from the GPU's
+            check_step_status(layer)
+        L = cfg.seq_len(t)
+        # steps where a block fills, and the step after, are always checked
+        fill_near = L % 64 == 0 or (L - 1) % 64 == 0
+        if t % check_every and t != cfg.steps - 1 and not fill_near:
+            # still advance the oracle's eviction state from the GPU's, which
+            # must be the oracle's own update (it is deterministic on E)
             res = fetch(layer)
             for r, orow in orows.items():
-                L = cfg.seq_len(t)
                 if cfg.k_e > 0 and not cfg.ordered:
-                    orow.state.evict_set = res.evict_set[r[0], r[1], :min(cfg.k_e, L // 64)].astype(np.int64)
-                    orow.state.n_seen = L // 64
+                    nb = L // 64
+                    gev = res.evict_set[r[0], r[1], :min(cfg.k_e, nb)].astype(np.int64)
+                    want = O.eviction_update(orow.state.evict_set, orow.state.n_seen, nb,
+                                             orow.eviction_scores(nb), cfg.k_e)
+                    assert gev.tolist() == want.tolist(), f"eviction set row {r} step {t}"
+                    orow.state.evict_set = gev
+                    orow.state.n_seen = nb
                 prev[r] = {"selected": [int(x) for x in res.selected[r][:res.num_selected[r]]],
                            "tail": L // 64 if L % 64 else None}
             continue
         res = fetch(layer)
-        L = cfg.seq_len(t)
         for r, orow in orows.items():
             if L % 64 == 0:
                 check_reps(layer, orow, cfg, *r, L // 64)

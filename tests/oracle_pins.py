@@ -572,10 +572,42 @@ def check_row_trajectory(O):
     assert fired >= 10, fired        # the stop fires before the end of the list
 
 
+def check_residency_diff(O):
+    """Set differences against a bitmap walk over every block id, the
+    identity gamma = 1 - |fetch|/|S| with the (separately pinned) locality,
+    and |S| - |fetch| = |A| - |release| (both are |S and A|)."""
+    rng = np.random.default_rng(27)
+    for trial in range(200):
+        nmax = int(rng.integers(1, 40))
+        S = rng.choice(nmax, int(rng.integers(0, nmax + 1)), replace=False)
+        P_ = rng.choice(nmax, int(rng.integers(0, nmax + 1)), replace=False)
+        tail = int(rng.integers(0, nmax + 3)) if rng.random() < 0.7 else None
+        fetch, release = O.residency_diff(S, P_, tail)
+        inS = [False] * (nmax + 3)
+        inA = [False] * (nmax + 3)
+        for b in S:
+            inS[int(b)] = True
+        for b in P_:
+            inA[int(b)] = True
+        if tail is not None:
+            inA[tail] = True
+        want_f = [b for b in range(nmax + 3) if inS[b] and not inA[b]]
+        want_r = [b for b in range(nmax + 3) if inA[b] and not inS[b]]
+        assert fetch.tolist() == want_f and release.tolist() == want_r, trial
+        nA = sum(inA)
+        assert len(S) - len(fetch) == nA - len(release)
+        if len(S):
+            assert math.isclose(1 - len(fetch) / len(S), O.locality(S, P_, tail), rel_tol=0,
+                                abs_tol=1e-15)
+    # hand case: resident {1, 2} + tail 3; selected {2, 3, 4} -> fetch {4}, release {1}
+    f, r = O.residency_diff([4, 2, 3], [2, 1], 3)
+    assert f.tolist() == [4] and r.tolist() == [1]
+
+
 ALL_CHECKS = [
     check_round, check_rne_fraction, check_rounded_means, check_reps_layout,
     check_eviction_scores, check_scores_bruteforce, check_scores_closed_forms,
     check_forecast, check_topk_exchange, check_selection_golden, check_select_bruteforce,
     check_eviction_incremental, check_dense_reduction, check_attend_loops,
-    check_early_stop, check_locality, check_row_trajectory,
+    check_early_stop, check_locality, check_row_trajectory, check_residency_diff,
 ]

@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
@@ -145,3 +145,26 @@ def test_product_path_has_no_fallback():
             "A._lib = None\ntry:\n    A.load()\nexcept ImportError:\n    print('raised')")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "raised" in r.stdout, r.stderr
+
+
+def test_step_status_validation():
+    """The status query checks its arguments before any HIP call."""
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_decode_step_status, None, 4096)
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_decode_step_status, FAKE + 16, 4096)
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_decode_step_status, FAKE, 128)
+    assert N.nsa_status_string(N.NSA_ERR_STEP_EXPIRED) == "NSA_ERR_STEP_EXPIRED"
+
+
+def test_residency_diff_validation():
+    s = shape()
+    args = [s, 64] + [FAKE] * 9 + [None, 0]
+    for i in range(2, 11):
+        bad = list(args)
+        bad[i] = None
+        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_residency_diff, *bad)
+    bad = list(args)
+    bad[1] = 0
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_residency_diff, *bad)
+    bad = list(args)
+    bad[11] = FAKE + 2                 # gamma misaligned
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_residency_diff, *bad)

@@ -51,6 +51,15 @@ def test_config3_long_context_sampled_rows():
     assert st["gamma_min"] >= 0.75
 
 
+def test_config3_fill_steps():
+    """Config 3 for 80 steps: block 2048 fills at step 63 (incremental reps
+    and eviction scores at nb = 2049, the eviction merge over a 2049-block
+    row, gamma at the fill step)."""
+    cfg = W.config(3, steps=80)
+    _, st = H.run_and_check(cfg, rows=H.sample_rows(cfg, 4), check_every=8)
+    assert st["gamma_min"] >= 0.75
+
+
 _C4 = {}
 
 

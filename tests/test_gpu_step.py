@@ -43,6 +43,25 @@ def test_step_config3_long_context_sampled_rows():
     assert st["gamma_min"] >= 0.75
 
 
+def test_step_config3_fill_steps():
+    """Config 3 for 80 steps on the fused step: block 2048 fills at step 63
+    (the non-steady eviction update inside the kernel at nb = 2049, with a
+    split gang, and the selection over a row longer than 2048 blocks)."""
+    cfg = W.config(3, steps=80)
+    _, st = H.run_and_check(cfg, rows=H.sample_rows(cfg, 4), check_every=8, fused=True)
+    assert st["gamma_min"] >= 0.75
+
+
+def test_step_status_query_reports_no_expiry():
+    """nsa_decode_step_status on a workspace whose steps all completed:
+    NSA_OK, and the query leaves the workspace usable."""
+    cfg = W.config(0)
+    layer, _ = H.run_and_check(cfg, fused=True)
+    layer.check_step()
+    H.run_step(layer, cfg, 0, fused=True)
+    layer.check_step()
+
+
 SMALL = [
     ("f32", 64, 1, "group_softmax"),
     ("f32", 128, 2, "group_softmax"),

@@ -173,12 +173,29 @@ def mut_row_ordered_stop_ignored(O):
     O.OracleRow.step = step
 
 
+def mut_residency_ignores_tail(O):
+    """The previous step's tail block is not counted as resident."""
+    orig = O.residency_diff
+    O.residency_diff = lambda sel, prev, tail: orig(sel, prev, None)
+
+
+def mut_residency_swapped(O):
+    """Fetch and release swapped."""
+    orig = O.residency_diff
+
+    def f(sel, prev, tail):
+        a, b = orig(sel, prev, tail)
+        return b, a
+    O.residency_diff = f
+
+
 MUTANTS = [mut_no_softmax, mut_max_before_head_sum, mut_ties_to_higher_id, mut_tail_dropped,
            mut_stop_block_excluded, mut_sub_block_shift, mut_eviction_forgets_old,
            mut_attention_unscaled, mut_round_truncates, mut_parts_overlap, mut_mean_by_15,
            mut_gamma_ignores_tail, mut_row_reps_from_previous_block,
            mut_row_eviction_from_previous_block, mut_row_prev_tail_off_by_one,
-           mut_row_ordered_stop_ignored]
+           mut_row_ordered_stop_ignored, mut_residency_ignores_tail,
+           mut_residency_swapped]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
