@@ -25,6 +25,7 @@ from ._abi import (  # noqa: F401
     load,
     nsa_abi_version,
     nsa_decode_step,
+    nsa_decode_step_noalloc,
     nsa_decode_step_status,
     nsa_decode_step_workspace_bytes,
     nsa_decode_workspace_bytes,

@@ -39,6 +39,7 @@ EXPORTS = (
     "nsa_sparse_decode",
     "nsa_decode_step_workspace_bytes",
     "nsa_decode_step",
+    "nsa_decode_step_noalloc",
     "nsa_decode_step_status",
     "nsa_residency_diff",
     "nsa_status_string",
@@ -122,6 +123,9 @@ def load() -> ctypes.CDLL:
     lib.nsa_decode_step.argtypes = [P(Shape), P(SelectParams), vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                     vp, vp, vp, vp, vp, vp, sz, vp]
     lib.nsa_decode_step.restype = i32
+    lib.nsa_decode_step_noalloc.argtypes = [P(Shape), P(SelectParams), vp, vp, vp, vp, vp, vp, vp,
+                                            vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.nsa_decode_step_noalloc.restype = i32
     lib.nsa_decode_step_status.argtypes = [vp, sz, i32, vp]
     lib.nsa_decode_step_status.restype = i32
     lib.nsa_residency_diff.argtypes = [P(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -259,3 +263,16 @@ def nsa_residency_diff(shape: Shape, max_selected: int, prev_selected, prev_num_
                                    _ptr(release), _ptr(num_release), _ptr(gamma),
                                    _stream(stream))
     _check(st, "nsa_residency_diff")
+
+
+def nsa_decode_step_noalloc(shape: Shape, params: SelectParams, query, q, reps, evict_block_score,
+                            k_pool, v_pool, block_table, seq_lens, max_seq_len: int, evict_set,
+                            evict_seen, selected, num_selected, out, step_status=None,
+                            stream=None) -> None:
+    st = load().nsa_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(params), _ptr(query),
+                                        _ptr(q), _ptr(reps), _ptr(evict_block_score),
+                                        _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                        _ptr(seq_lens), int(max_seq_len), _ptr(evict_set),
+                                        _ptr(evict_seen), _ptr(selected), _ptr(num_selected),
+                                        _ptr(out), _ptr(step_status), _stream(stream))
+    _check(st, "nsa_decode_step_noalloc")

@@ -357,15 +357,16 @@ nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_sel
   return ok();
 }
 
-nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* params,
-                           const void* query, const void* q, const void* reps,
-                           const float* evict_block_score, const void* k_pool,
-                           const void* v_pool, const int32_t* block_table,
-                           const int32_t* seq_lens, int32_t max_seq_len, int32_t* evict_set,
-                           int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
-                           void* out, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  const char* fn = "nsa_decode_step";
+// The checks and the launch description shared by nsa_decode_step and
+// nsa_decode_step_noalloc (workspace == NULL: the library's own).
+static nsa_status step_launch_checked(const char* fn, const nsa_shape* shape,
+                                      const nsa_select_params* params, const void* query,
+                                      const void* q, const void* reps,
+                                      const float* evict_block_score, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      int32_t* evict_set, int32_t* evict_seen, int32_t* selected,
+                                      int32_t* num_selected, void* out, nsa::StepLaunch* L) {
   nsa::StepLayout lay;
   if (nsa_status st = step_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
   NSA_REQUIRE_PTR(query, 16);
@@ -378,46 +379,86 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
   NSA_REQUIRE_PTR(selected, 4);
   NSA_REQUIRE_PTR(num_selected, 4);
   NSA_REQUIRE_PTR(out, 16);
-  NSA_REQUIRE_PTR(workspace, 256);
   if (params->k_e > 0) {
     NSA_REQUIRE_PTR(evict_block_score, 4);
     NSA_REQUIRE_PTR(evict_set, 4);
     NSA_REQUIRE_PTR(evict_seen, 4);
   }
-  if (workspace_bytes < lay.bytes)
-    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
-                workspace_bytes, lay.bytes);
-  nsa::StepLaunch L{};
-  L.dtype = shape->dtype;
-  L.D = shape->head_dim;
-  L.G = shape->num_q_heads / shape->num_kv_heads;
-  L.mode = params->mode;
-  L.query = query;
-  L.q = q;
-  L.reps = reps;
-  L.E = evict_block_score;
-  L.k_pool = k_pool;
-  L.v_pool = v_pool;
-  L.table = block_table;
-  L.seq_lens = seq_lens;
-  L.evict_set = evict_set;
-  L.evict_seen = evict_seen;
-  L.selected = selected;
-  L.num_selected = num_selected;
-  L.out = out;
-  L.workspace = workspace;
-  L.B = shape->batch;
-  L.Hkv = shape->num_kv_heads;
-  L.max_blocks = shape->max_blocks_per_seq;
-  L.k = params->k;
-  L.k_e = params->k_e;
-  L.scale = scale_of(shape);
-  L.gang_override = env_int("NSA_STEP_GANG");
-  L.lay = lay;
+  *L = nsa::StepLaunch{};
+  L->dtype = shape->dtype;
+  L->D = shape->head_dim;
+  L->G = shape->num_q_heads / shape->num_kv_heads;
+  L->mode = params->mode;
+  L->query = query;
+  L->q = q;
+  L->reps = reps;
+  L->E = evict_block_score;
+  L->k_pool = k_pool;
+  L->v_pool = v_pool;
+  L->table = block_table;
+  L->seq_lens = seq_lens;
+  L->evict_set = evict_set;
+  L->evict_seen = evict_seen;
+  L->selected = selected;
+  L->num_selected = num_selected;
+  L->out = out;
+  L->B = shape->batch;
+  L->Hkv = shape->num_kv_heads;
+  L->max_blocks = shape->max_blocks_per_seq;
+  L->k = params->k;
+  L->k_e = params->k_e;
+  L->scale = scale_of(shape);
+  L->gang_override = env_int("NSA_STEP_GANG");
+  L->lay = lay;
   if (env_trace())
     std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d gang=%d (0: by occupancy)\n", lay.rows,
-                 lay.nb_max, L.gang_override);
+                 lay.nb_max, L->gang_override);
+  return NSA_OK;
+}
+
+nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* params,
+                           const void* query, const void* q, const void* reps,
+                           const float* evict_block_score, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t* evict_set,
+                           int32_t* evict_seen, int32_t* selected, int32_t* num_selected,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "nsa_decode_step";
+  nsa::StepLaunch L;
+  if (nsa_status st = step_launch_checked(fn, shape, params, query, q, reps, evict_block_score,
+                                          k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                                          evict_set, evict_seen, selected, num_selected, out, &L))
+    return st;
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (workspace_bytes < L.lay.bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, L.lay.bytes);
+  L.workspace = workspace;
   return launched(fn, nsa::launch_step(L, stream));
+}
+
+nsa_status nsa_decode_step_noalloc(const nsa_shape* shape, const nsa_select_params* params,
+                                   const void* query, const void* q, const void* reps,
+                                   const float* evict_block_score, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t* evict_set, int32_t* evict_seen, int32_t* selected,
+                                   int32_t* num_selected, void* out, int32_t* step_status,
+                                   hipStream_t stream) {
+  const char* fn = "nsa_decode_step_noalloc";
+  nsa::StepLaunch L;
+  if (nsa_status st = step_launch_checked(fn, shape, params, query, q, reps, evict_block_score,
+                                          k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                                          evict_set, evict_seen, selected, num_selected, out, &L))
+    return st;
+  if (step_status) NSA_REQUIRE_PTR(step_status, 4);
+  if (L.lay.bytes > nsa::kNoAllocStepBytes)
+    return fail(NSA_ERR_UNSUPPORTED,
+                "%s: this shape needs %zu bytes of step workspace, above the %zu the library "
+                "holds per device; use nsa_decode_step with a caller workspace", fn, L.lay.bytes,
+                nsa::kNoAllocStepBytes);
+  return launched(fn, nsa::launch_step_noalloc(L, step_status, stream));
 }
 
 nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,

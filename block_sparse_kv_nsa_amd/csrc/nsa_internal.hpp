@@ -260,6 +260,13 @@ struct StepLaunch {
 };
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream);
 
+// The fused step on the library's own per-device workspace (no allocation by
+// the caller or the library): layouts up to kNoAllocStepBytes.  Clears the
+// call's hand-off slots first, then runs the same kernel; `status` (NULL, or
+// one int32) is set to 0, and to 1 by a row whose waits expired.
+constexpr size_t kNoAllocStepBytes = (size_t)64 << 20;
+hipError_t launch_step_noalloc(const StepLaunch& L, int32_t* status, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // residency diff between consecutive selections
 // ---------------------------------------------------------------------------

@@ -41,6 +41,8 @@
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
 
+#include <mutex>
+
 namespace nsa {
 namespace {
 
@@ -61,6 +63,7 @@ struct GangArgs {
   int32_t* num_selected;
   void* out;
   uint32_t* err;     // sticky error word
+  int32_t* status;   // NULL, or set to 1 by a row whose waits expired
   float* stats;      // [rows][kMaxGang][G] (m, s): max logit and sum of 2^(l - m)
   uint32_t* keys;    // [rows][nb_max] block key + 1 (1: not a candidate)
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
@@ -199,7 +202,7 @@ struct Gang {
     int* eids = reinterpret_cast<int*>(dyn);                      // k_e: the eviction set
     int* qsel = eids + (a.k_e > 0 ? a.k_e : 1);                   // k: query-aware blocks
     int* tbl = qsel + a.k;                                        // min(nb_max, kTblLds)
-    uint32_t* scratch = reinterpret_cast<uint32_t*>(tbl + min(a.nb_max, kTblLds));
+    uint32_t* lds_keys = reinterpret_cast<uint32_t*>(tbl + min(a.nb_max, kTblLds));
     const int64_t tb = (int64_t)b * a.max_blocks;                 // the row's table entries
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
     const T* kp = static_cast<const T*>(a.k_pool);
@@ -271,7 +274,7 @@ struct Gang {
     if (!steady) {
       // blocks became full since the last call: update the set (once per
       // filled block, before the stream so that no loads wait behind it)
-      uint32_t* ekeys = scratch;                                       // ncand
+      uint32_t* ekeys = lds_keys;                                      // ncand
       int* ev_old = reinterpret_cast<int*>(ekeys + a.k_e + a.nb_max);  // k_e
       const int ncand = nprev + nb - seen;
       for (int i = threadIdx.x; i < nprev; i += kThreads)
@@ -519,7 +522,7 @@ struct Gang {
       // every member's keys (polled until none is missing), in registers for
       // rows of up to kSmallKpt * kThreads blocks and in shared memory
       constexpr int kSmallKpt = 8;
-      uint32_t* rkeys = scratch;  // nb
+      uint32_t* rkeys = lds_keys;  // nb
       uint32_t kv[kSmallKpt];
       Patience pt;  // each wave polls its own share, reading again only what is missing
       pt.start();
@@ -641,6 +644,7 @@ struct Gang {
 
     // the eviction state, when it changed: every member has read the old one
     // (its partial is in)
+    if (failed && a.status != nullptr && threadIdx.x == 0) a.status[0] = 1;
     if (!steady && !failed) {
       for (int i = threadIdx.x; i < a.k_e; i += kThreads)
         a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
@@ -689,7 +693,7 @@ __global__ __launch_bounds__(kThreads, (gang_wgs_per_cu<T, D, G>())) void gang_k
 }
 
 template <typename T, int D, int G, bool FORECAST>
-hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
+hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   const StepLayout& lay = L.lay;
   const void* fn = reinterpret_cast<const void*>(gang_kernel<T, D, G, FORECAST>);
   GridInfo gi;
@@ -712,6 +716,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
   a.selected = L.selected;
   a.num_selected = L.num_selected;
   a.out = L.out;
+  a.status = status;
   char* ws = static_cast<char*>(L.workspace);
   a.err = reinterpret_cast<uint32_t*>(ws) + kErr;
   a.stats = reinterpret_cast<float*>(ws + lay.off_stats);
@@ -740,25 +745,84 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream) {
 }
 
 template <typename T, int D, int G>
-hipError_t by_mode(const StepLaunch& L, hipStream_t s) {
-  return L.mode == 1 ? launch_t<T, D, G, true>(L, s) : launch_t<T, D, G, false>(L, s);
+hipError_t by_mode(const StepLaunch& L, hipStream_t s, int32_t* st) {
+  return L.mode == 1 ? launch_t<T, D, G, true>(L, s, st) : launch_t<T, D, G, false>(L, s, st);
 }
 
 template <typename T, int D>
-hipError_t by_group(const StepLaunch& L, hipStream_t s) {
+hipError_t by_group(const StepLaunch& L, hipStream_t s, int32_t* st) {
   switch (L.G) {
-    case 1: return by_mode<T, D, 1>(L, s);
-    case 2: return by_mode<T, D, 2>(L, s);
-    case 4: return by_mode<T, D, 4>(L, s);
-    default: return by_mode<T, D, 8>(L, s);
+    case 1: return by_mode<T, D, 1>(L, s, st);
+    case 2: return by_mode<T, D, 2>(L, s, st);
+    case 4: return by_mode<T, D, 4>(L, s, st);
+    default: return by_mode<T, D, 8>(L, s, st);
   }
+}
+
+hipError_t dispatch(const StepLaunch& L, hipStream_t stream, int32_t* status) {
+  if (L.dtype == 1)
+    return L.D == 128 ? by_group<bf16, 128>(L, stream, status) : by_group<bf16, 64>(L, stream, status);
+  return L.D == 128 ? by_group<float, 128>(L, stream, status) : by_group<float, 64>(L, stream, status);
+}
+
+// ---------------------------------------------------------------------------
+// The library's own step workspace, for callers that cannot allocate: one
+// array per device, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it only names the symbol); it uses
+// the device address looked up once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocStepBytes];
+
+// Zero words [0, n0) and [n1, n2) of the workspace and the caller's status
+// word: the hand-off slots and the error word of this call's layout start
+// clear whatever the previous call (any shape) left there.
+__global__ __launch_bounds__(kThreads) void clear_slots_kernel(uint32_t* ws, uint32_t n0,
+                                                               uint32_t n1, uint32_t n2,
+                                                               int32_t* status) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n0 + (n2 - n1); i += stride)
+    ws[i < n0 ? i : n1 + (i - n0)] = 0u;
+  if (status != nullptr && blockIdx.x == 0 && threadIdx.x == 0) status[0] = 0;
+}
+
+hipError_t scratch_address(void** out) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void* addr[kDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_step(const StepLaunch& L, hipStream_t stream) {
-  if (L.dtype == 1) return L.D == 128 ? by_group<bf16, 128>(L, stream) : by_group<bf16, 64>(L, stream);
-  return L.D == 128 ? by_group<float, 128>(L, stream) : by_group<float, 64>(L, stream);
+hipError_t launch_step(const StepLaunch& L, hipStream_t stream) { return dispatch(L, stream, nullptr); }
+
+hipError_t launch_step_noalloc(const StepLaunch& L, int32_t* status, hipStream_t stream) {
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  const StepLayout& lay = L.lay;
+  const uint32_t n0 = (uint32_t)(lay.off_acc / 4), n1 = (uint32_t)(lay.off_keys / 4),
+                 n2 = (uint32_t)(lay.bytes / 4);
+  const uint32_t words = n0 + (n2 - n1);
+  const int blocks = (int)((words + kThreads * 8 - 1) / (kThreads * 8));
+  clear_slots_kernel<<<blocks > 0 ? blocks : 1, kThreads, 0, stream>>>(static_cast<uint32_t*>(ws),
+                                                                       n0, n1, n2, status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  StepLaunch M = L;
+  M.workspace = ws;
+  return dispatch(M, stream, status);
 }
 
 }  // namespace nsa

@@ -119,6 +119,19 @@ class SparseDecodeLayer:
                           self.selected, self.num_selected, self.out, self.step_ws,
                           self.step_ws_bytes, stream)
 
+    def step_noalloc(self, query: torch.Tensor, q: torch.Tensor, max_seq_len: int,
+                     step_status=None, stream=None) -> None:
+        """The fused step on the library's own per-device workspace (no
+        workspace argument).  step_status: None or a one-element int32 device
+        tensor, set to 1 if a wait of the step expired."""
+        ke = self.k_e > 0
+        A.nsa_decode_step_noalloc(self.shape, self.sel_params, query, q, self.reps,
+                                  self.evict_scores if ke else None, self.k_pool, self.v_pool,
+                                  self.block_table, self.seq_lens, max_seq_len,
+                                  self.evict_set if ke else None,
+                                  self.evict_seen if ke else None, self.selected,
+                                  self.num_selected, self.out, step_status, stream)
+
     def residency_diff(self, prev_selected, prev_num_selected, prev_seq_lens, fetch, num_fetch,
                        release, num_release, gamma=None, stream=None) -> None:
         """Blocks to fetch and to release from the previous selection (given)

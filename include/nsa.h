@@ -264,6 +264,33 @@ nsa_status nsa_decode_step(const nsa_shape* shape, const nsa_select_params* para
                            hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * nsa_decode_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  Same arguments, computation, outputs and state
+ * rules as nsa_decode_step; the hand-off slots live in an array the library
+ * holds on each device until the process ends (64 MiB; shapes whose
+ * nsa_decode_step_workspace_bytes exceeds that return NSA_ERR_UNSUPPORTED,
+ * checked before any HIP call).  Nothing is allocated or freed by the call.
+ * Each call first clears the slots its shape uses (a small kernel on
+ * `stream`), then runs the step.  Every call on a device shares that
+ * device's array: calls that overlap on one device (other streams, other
+ * host threads) race and give undefined results; run them one after
+ * another.
+ *   step_status   NULL, or one int32 (device): set to 0 by the call, and to
+ *                 1 if a wait of the step expired (the outputs are then
+ *                 undefined and the eviction state is left unchanged, as
+ *                 with nsa_decode_step).
+ * ------------------------------------------------------------------------ */
+nsa_status nsa_decode_step_noalloc(const nsa_shape* shape, const nsa_select_params* params,
+                                   const void* query, const void* q, const void* reps,
+                                   const float* evict_block_score, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t* evict_set, int32_t* evict_seen, int32_t* selected,
+                                   int32_t* num_selected, void* out, int32_t* step_status,
+                                   hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * Residency diff between consecutive selections (NOSA summary, "2. Sistema:
  * NOSI": the cache is kept in block units and a step moves only what its
  * selection changes; "Garantia de Localidad": the eviction part keeps

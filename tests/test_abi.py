@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
@@ -168,3 +168,22 @@ def test_residency_diff_validation():
     bad = list(args)
     bad[11] = FAKE + 2                 # gamma misaligned
     expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_residency_diff, *bad)
+
+
+def test_step_noalloc_validation():
+    """Arguments and the per-device size limit are checked before any HIP call."""
+    s, p = shape(), N.SelectParams(0, 64, 48, 0)
+    args = [s, p] + [FAKE] * 8 + [131088] + [FAKE] * 5 + [None, 0]
+    bad = list(args)
+    bad[2] = None
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_decode_step_noalloc, *bad)
+    bad = list(args)
+    bad[16] = FAKE + 2                 # status misaligned
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_decode_step_noalloc, *bad)
+    big = list(args)                   # 512 rows x 8 heads of head_dim 128: above the limit
+    big[0] = shape(batch=256, num_q_heads=64, num_kv_heads=8)
+    msg = expect(N.NSA_ERR_UNSUPPORTED, N.nsa_decode_step_noalloc, *big)
+    assert "per device" in msg
+    ordered = list(args)
+    ordered[1] = N.SelectParams(0, 64, 0, 1)
+    expect(N.NSA_ERR_UNSUPPORTED, N.nsa_decode_step_noalloc, *ordered)
