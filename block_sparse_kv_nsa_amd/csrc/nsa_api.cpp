@@ -339,9 +339,10 @@ static nsa_status step_layout_checked(const char* fn, const nsa_shape* shape,
   const size_t lds = nsa::gang_dyn_lds(*lay, params->k, params->k_e);
   if (lds > 64 * 1024)
     return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 65536)", fn, lds);
-  if (4 * lay->nb_max > nsa::kMaxGang * nsa::kGangReps)
+  const int cap = nsa::gang_reps_cap(shape->dtype == NSA_F32 ? 4 : 2, shape->head_dim, G);
+  if (4 * lay->nb_max > nsa::kMaxGang * cap)
     return fail(NSA_ERR_UNSUPPORTED, "%s: max_seq_len %d above the fused step's %d tokens", fn,
-                max_seq_len, nsa::kMaxGang * nsa::kGangReps * 16);
+                max_seq_len, nsa::kMaxGang * cap * 16);
   if (lay->bytes >= (size_t)1 << 32)
     return fail(NSA_ERR_UNSUPPORTED, "%s: workspace above 4 GiB", fn);
   return NSA_OK;
@@ -409,6 +410,7 @@ static nsa_status step_launch_checked(const char* fn, const nsa_shape* shape,
   L->k_e = params->k_e;
   L->scale = scale_of(shape);
   L->gang_override = env_int("NSA_STEP_GANG");
+  L->att_override = env_int("NSA_STEP_ATTENDERS");
   L->lay = lay;
   if (env_trace())
     std::fprintf(stderr, "[nsa] step rows=%d nb_max=%d gang=%d (0: by occupancy)\n", lay.rows,

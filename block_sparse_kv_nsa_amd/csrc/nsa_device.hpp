@@ -700,6 +700,36 @@ __device__ __forceinline__ void merge_ms_lanes(float& m, float& s, int off) {
   merge_ms(m, s, mh, sh);
 }
 
+// The same merge as merge_ms_lanes with a short dependency chain: the
+// maximum over the lanes first, then each lane's sum rescaled to it (one
+// exp2), then the sum over the lanes.
+__device__ __forceinline__ void merge_ms_lanes_flat(float& m, float& s, int off) {
+  float M = m;
+  if (off <= 1) M = fmaxf(M, dpp_mov<kDppQuadXor1>(M));
+  if (off <= 2) M = fmaxf(M, dpp_mov<kDppQuadXor2>(M));
+  if (off <= 4) M = fmaxf(M, dpp_mov<0x124>(M));  // row_ror:4
+  if (off <= 8) M = fmaxf(M, dpp_mov<0x128>(M));  // row_ror:8
+  float lo, hi;
+  if (off <= 16) {
+    lane_pair<16>(M, lo, hi);
+    M = fmaxf(lo, hi);
+  }
+  lane_pair<32>(M, lo, hi);
+  M = fmaxf(lo, hi);
+  float t = (m == -INFINITY) ? 0.f : s * exp2f(m - M);
+  if (off <= 1) t += dpp_mov<kDppQuadXor1>(t);
+  if (off <= 2) t += dpp_mov<kDppQuadXor2>(t);
+  if (off <= 4) t += dpp_mov<0x124>(t);
+  if (off <= 8) t += dpp_mov<0x128>(t);
+  if (off <= 16) {
+    lane_pair<16>(t, lo, hi);
+    t = lo + hi;
+  }
+  lane_pair<32>(t, lo, hi);
+  s = lo + hi;
+  m = M;
+}
+
 // max over all 64 lanes, result in every lane
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_mov<0x121>(v));  // row_ror:1

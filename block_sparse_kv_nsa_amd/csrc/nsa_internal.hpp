@@ -170,8 +170,15 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 // they look for a slot.
 // ---------------------------------------------------------------------------
 enum : int { kErr = 2 };
-constexpr int kMaxGang = 64;     // most workgroups per row
-constexpr int kGangReps = 512;   // most representatives a member scores (in registers)
+constexpr int kMaxGang = 64;     // most workgroups per row (scorers and attenders)
+constexpr int kGangReps = 1024;  // most representatives a scorer holds (in registers)
+
+// Representatives a scorer holds for a (dtype, head_dim, group) variant:
+// float32 rows of 128 elements with 8 heads per KV head leave registers for
+// half as many.
+constexpr int gang_reps_cap(int dtype_bytes, int D, int G) {
+  return (dtype_bytes == 4 && D == 128 && G == 8) ? kGangReps / 2 : kGangReps;
+}
 
 struct StepLayout {
   int rows, G, D, nb_max;
@@ -208,32 +215,48 @@ inline size_t gang_dyn_lds(const StepLayout& lay, int k, int k_e) {
 }
 
 struct GangPlan {
-  int C, gangs, per_wg;
-  int split;  // gangs split across the two workgroup slots of the compute units
+  int CS, CA;      // scorers and attenders per row
+  int gangs;       // rows handled at once (the others in turn)
+  int per_wg;      // representatives per scorer
   size_t dyn_lds;
 };
 
-// Gang size C: as many members as the resident workgroups allow across the
-// rows (at most kMaxGang), and at least enough to hold the longest row's
-// representatives in registers (kGangReps per member).  Rows beyond the
-// resident gangs are taken in turn.
-inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int per_cu,
-                      int c_override, GangPlan* p) {
+// Workgroups per row, from the workgroups the device holds at once (at most
+// kMaxGang).  A row with an eviction set gives about half of them to
+// attenders (attention over the eviction set and the tail block, which no
+// query decides); scorers take the rest: at least enough to hold the
+// longest row's representatives (reps_cap each), at most one per 64 of
+// them.  Attenders beyond the row's eviction items would idle and are not
+// planned.  c_override > 0 fixes the workgroups per row before these
+// bounds, ca_override > 0 the attenders among them.  The grid is
+// gangs * (CS + CA) workgroups: the scorers first (the dispatcher places
+// them first on their compute units), then the attenders.
+inline bool gang_plan(const StepLayout& lay, int k, int k_e, int capacity, int reps_cap,
+                      int c_override, int ca_override, GangPlan* p) {
   const int nsub = 4 * lay.nb_max;
-  const int c_min = nsub > 0 ? (nsub + kGangReps - 1) / kGangReps : 1;
-  const int c_cap = capacity < kMaxGang ? capacity : kMaxGang;
-  if (c_min > c_cap) return false;
-  int C = c_override > 0 ? c_override : capacity / (lay.rows > 0 ? lay.rows : 1);
-  C = C < c_min ? c_min : (C > c_cap ? c_cap : C);
-  p->C = C;
-  p->gangs = capacity / C < lay.rows ? capacity / C : lay.rows;
+  const int rows = lay.rows > 0 ? lay.rows : 1;
+  const int cs_min = nsub > 0 ? (nsub + reps_cap - 1) / reps_cap : 1;
+  const int cs_max_useful = nsub > 64 ? (nsub + 63) / 64 : 1;
+  int per_row = c_override > 0 ? c_override : capacity / rows;
+  if (per_row > kMaxGang) per_row = kMaxGang;
+  if (per_row < 1) per_row = 1;
+  int CA = k_e > 0 ? (ca_override > 0 ? ca_override : per_row / 2) : 0;
+  if (CA > k_e + 1) CA = k_e + 1;
+  if (CA >= per_row) CA = per_row - 1;
+  int CS = per_row - CA;
+  if (CS > cs_max_useful) CS = cs_max_useful;
+  if (CS < cs_min) CS = cs_min;
+  if (CS > kMaxGang) return false;
+  if (CS + CA > kMaxGang) CA = kMaxGang - CS;
+  if (CS + CA > capacity) CA = capacity - CS;
+  if (CA < 0) return false;
+  p->CS = CS;
+  p->CA = CA;
+  p->gangs = capacity / (CS + CA) < lay.rows ? capacity / (CS + CA) : lay.rows;
   if (p->gangs < 1) return false;
-  const int per = nsub > 0 ? (nsub + C - 1) / C : 4;
+  const int per = nsub > 0 ? (nsub + CS - 1) / CS : 4;
   p->per_wg = (int)round_up((size_t)per, 4);
   p->dyn_lds = gang_dyn_lds(lay, k, k_e);
-  // Split gangs when the grid fills exactly two workgroups per compute unit
-  // and C is even: half of every gang sits in each of the two slots.
-  p->split = (C % 2 == 0 && C >= 4 && per_cu == 2 && p->gangs * C == capacity) ? 1 : 0;
   return true;
 }
 
@@ -256,6 +279,7 @@ struct StepLaunch {
   int B, Hkv, max_blocks, k, k_e;
   float scale;
   int gang_override;  // 0: from capacity
+  int att_override;   // 0: half of the row's workgroups
   StepLayout lay;
 };
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream);

@@ -68,8 +68,8 @@ struct GangArgs {
   uint32_t* keys;    // [rows][nb_max] block key + 1 (1: not a candidate)
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
-  int rows, Hkv, max_blocks, nb_max, k, k_e, C, gangs, per_wg;
-  int split;  // split gangs (see gang_kernel)
+  int rows, Hkv, max_blocks, nb_max, k, k_e;
+  int CS, CA, gangs, per_wg;  // scorers and attenders per row, rows at once, reps per scorer
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
   uint32_t stats_bytes, keys_bytes, ml_bytes, acc_bytes;
@@ -159,159 +159,200 @@ struct Gang {
   static constexpr int KEEP = GS >= 4 ? GS / 4 : 1;
   static constexpr int DUP = GS >= 4 ? 1 : 4 / GS;
   static constexpr int RPI = kThreads / 4;        // representatives per load slot (64)
-  static constexpr int U = kGangReps / RPI;       // slots per lane
-  static constexpr int CBLK = kGangReps / kSubs;  // most blocks a member scores
+  static constexpr int REPS = gang_reps_cap((int)sizeof(T), D, G);
+  static constexpr int U = REPS / RPI;             // slots per lane
+  static constexpr int CBLK = REPS / kSubs;        // most blocks a scorer scores
   // slots per batch (two batches in flight): 4 for one query slice, 2 when
   // the slices of several heads already take many registers
   static constexpr int USL = GS >= 2 ? 2 : 4;
   static constexpr int QWORDS = G * D * (int)sizeof(T) / 4;  // attention queries, 32-bit words
   static constexpr int QPT = (QWORDS + kThreads - 1) / kThreads;
   static constexpr int NP = kMaxGang * G / kWave;  // (m, s) slots per lane when polling
+  // the selector's query slices take 4 registers per head and 16-byte load;
+  // above 128 registers (float32 rows of 128 with 8 heads) they are read
+  // from shared memory, four heads at a time, for every load slot
+  static constexpr bool QLDS = GS * NLD * 4 > 128;
+  static constexpr int HBS = QLDS ? 4 : GS;
 
   struct Smem {
     AttendSmem<T, D, G> att;
     RadixSmem rad;
     SmallTopSmem small;
     TopSmem top;
-    float lgs[U][KEEP][kThreads];  // the logits, parked during attention
-    float sM[G], sInvZ[G];
+    float lgs[U][KEEP][kThreads];  // the logits, parked while the hand-offs run
+    float sM[G];  // per head: log2 of the row normaliser (max + log2 of the sum)
     float red_m[kWaves][4][KEEP], red_s[kWaves][4][KEEP];
     uint32_t ckeys[CBLK] __attribute__((aligned(16)));
+    T sq[QLDS ? GS : 1][QLDS ? D : 1] __attribute__((aligned(16)));  // selector query (QLDS)
     f32x2 ml[G];
     int s_int[8];
   };
 
-  static __device__ __attribute__((always_inline)) void row_step(const GangArgs& a, int row, int c,
-                                                                 Smem& sm, uint32_t* dyn) {
+  // What both roles know of a row before any wait.
+  struct Row {
+    int b, g, L, nb, tail, seen, nprev, n_e;
+    bool steady;
+    int64_t tb;  // the row's first block-table entry
+  };
+
+  static __device__ __forceinline__ Row row_info(const GangArgs& a, int row) {
+    Row R;
+    R.b = row / a.Hkv;
+    R.g = row % a.Hkv;
+    R.L = sload(a.seq_lens, R.b);
+    R.nb = min(R.L / kBlock, a.nb_max);
+    // the partial block (none when the row's table is full: a longer L is
+    // outside the call's contract and attends nothing past the table)
+    R.tail = R.nb < a.max_blocks ? min(R.L - R.nb * kBlock, kBlock - 1) : 0;
+    // the eviction set: in the steady state no block became full since the
+    // last call and the set is the caller's state as it stands; otherwise
+    // the k_e best of (old set U new blocks) by eviction score, ties to the
+    // lower id
+    int seen = a.k_e > 0 ? sload(a.evict_seen, row) : 0;
+    if (seen < 0 || seen > R.nb) seen = 0;  // a new sequence in this slot
+    R.seen = seen;
+    R.steady = a.k_e == 0 || seen == R.nb;
+    R.nprev = min(a.k_e, seen);
+    R.n_e = a.k_e > 0 ? min(a.k_e, R.nprev + R.nb - seen) : 0;
+    R.tb = (int64_t)R.b * a.max_blocks;
+    return R;
+  }
+
+  // Blocks became full since the last call: the updated eviction set into
+  // eids[0..n_e), ascending.  Called by all threads; ends with a barrier.
+  static __device__ __forceinline__ void eviction_update(const GangArgs& a, int row, const Row& R,
+                                                         Smem& sm, int* eids, uint32_t* lds_keys) {
+    uint32_t* ekeys = lds_keys;                                      // ncand
+    int* ev_old = reinterpret_cast<int*>(ekeys + a.k_e + a.nb_max);  // k_e
+    const int ncand = R.nprev + R.nb - R.seen;
+    for (int i = threadIdx.x; i < R.nprev; i += kThreads)
+      ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), R.nb - 1);
+    __syncthreads();
+    const float* Er = a.E + (int64_t)row * a.max_blocks;
+    for (int i = threadIdx.x; i < ncand; i += kThreads) {
+      const int id = i < R.nprev ? ev_old[i] : R.seen + i - R.nprev;
+      ekeys[i] = order_key(Er[id]);
+    }
+    __syncthreads();
+    if (R.n_e > 0)
+      wg_top_m(ekeys, ncand, R.n_e, sm.top, [&](int i, int pos) {
+        eids[pos] = i < R.nprev ? ev_old[i] : R.seen + i - R.nprev;
+      });
+    __syncthreads();
+  }
+
+  // Item `idx` of the row's query-independent list [eviction set..., tail
+  // block]: eids in shared memory, table entry by a scalar load.
+  static __device__ __forceinline__ Item e_item(const GangArgs& a, const Row& R, const int* eids,
+                                                int idx) {
+    int blk = R.nb;  // the tail block
+    if (idx < R.n_e) blk = min(max(__builtin_amdgcn_readfirstlane(eids[idx]), 0), R.nb - 1);
+    Item x;
+    x.base = ((int64_t)sload(a.table, R.tb + blk) * a.Hkv + R.g) * (int64_t)(kBlock * D);
+    x.valid = idx < R.n_e ? kBlock : R.tail;
+    x.logits = nullptr;
+    return x;
+  }
+
+  // The attention queries of the row into shared memory (no barrier).
+  static __device__ __forceinline__ void queries_to_lds(const GangArgs& a, const Row& R, Smem& sm) {
+    const uint32_t* qrow =
+        reinterpret_cast<const uint32_t*>(static_cast<const T*>(a.q) + ((int64_t)R.b * a.Hkv + R.g) * G * D);
+    uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int w = threadIdx.x + i * kThreads;
+      if (w < QWORDS) ql[w] = qrow[w];
+    }
+  }
+
+  // Attention over this workgroup's n items (item(it) -> Item), two slabs in
+  // flight, one online-softmax state per wave; the merged partial published
+  // as partial `member` of the row.
+  template <typename ItemFn>
+  static __device__ __forceinline__ void attend_publish(const GangArgs& a, int row, int member,
+                                                        int n, ItemFn item, Smem& sm) {
+    const T* kp = static_cast<const T*>(a.k_pool);
+    const T* vp = static_cast<const T*>(a.v_pool);
+    AttnState<T, D, G> att;
+    att.init();
+    Slab<T, D> sa, sb;
+    if (n > 0) slab_issue<T, D, false>(sa, item(0), kp, vp);
+    if (n > 1) slab_issue<T, D, false>(sb, item(1), kp, vp);
+    for (int it = 0; it < n; it += 2) {
+      att.consume(sa, sm.att, a.qscale_att);
+      if (it + 2 < n) slab_issue<T, D, false>(sa, item(it + 2), kp, vp);
+      if (it + 1 < n) {
+        att.consume(sb, sm.att, a.qscale_att);
+        if (it + 3 < n) slab_issue<T, D, false>(sb, item(it + 3), kp, vp);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
+    const __amdgpu_buffer_rsrc_t acr = make_rsrc(a.part_acc, a.acc_bytes);
+    att.to_lds(sm.att);
+    wg_publish_partial(sm.att, sm.ml, mlr, acr, (int64_t)row * kMaxGang + member);
+  }
+
+  // ---- scorer c of a row: representatives [c*per_wg, +per_wg), the
+  // hand-offs and the selection.  Returns the row's count of query-aware
+  // blocks (m_row), written ascending to qsel (shared memory).
+  static __device__ __attribute__((always_inline)) int select_row(const GangArgs& a, int row,
+                                                                  const Row& R, int c, Smem& sm,
+                                                                  int* eids, int* qsel, int* tbl,
+                                                                  uint32_t* lds_keys) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int q = lane & 3, r = lane >> 2;
-    const int b = row / a.Hkv, g = row % a.Hkv;
-    const int C = a.C;
-    const int L = sload(a.seq_lens, b);
-    const int nb = min(L / kBlock, a.nb_max);
-    // the partial block (none when the row's table is full: a longer L is
-    // outside the call's contract and attends nothing past the table)
-    const int tail = nb < a.max_blocks ? min(L - nb * kBlock, kBlock - 1) : 0;
+    const int nb = R.nb, n_e = R.n_e;
     const int nsub = nb * kSubs;
     const int j0 = min(c * a.per_wg, nsub);
     const int j1 = min(j0 + a.per_wg, nsub);
     const int blk0 = j0 / kSubs, nblk = (j1 - j0) / kSubs;
+    const int nsl = (j1 - j0 + RPI - 1) / RPI;  // load slots in use
     const int h0 = GS >= 4 ? q * KEEP : q / DUP;
     const bool canon = (q % DUP) == 0;
-    int* eids = reinterpret_cast<int*>(dyn);                      // k_e: the eviction set
-    int* qsel = eids + (a.k_e > 0 ? a.k_e : 1);                   // k: query-aware blocks
-    int* tbl = qsel + a.k;                                        // min(nb_max, kTblLds)
-    uint32_t* lds_keys = reinterpret_cast<uint32_t*>(tbl + min(a.nb_max, kTblLds));
-    const int64_t tb = (int64_t)b * a.max_blocks;                 // the row's table entries
-    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
-    const T* kp = static_cast<const T*>(a.k_pool);
-    const T* vp = static_cast<const T*>(a.v_pool);
     uint32_t* err = a.err;
+    const bool tbl_lds = nb <= kTblLds;
+    const int m_row = max(0, min(a.k - n_e, nb - n_e));
 
     // the row's block table (full blocks) for the query-aware slabs, parked
     // in shared memory below when it fits (bounded loads: no branches)
-    const bool tbl_lds = nb <= kTblLds;
     uint32_t tv[kTblLds / kThreads];
     {
-      const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.table + tb, (uint32_t)(tbl_lds ? nb * 4 : 0));
+      const __amdgpu_buffer_rsrc_t trs =
+          make_rsrc(a.table + R.tb, (uint32_t)(tbl_lds ? nb * 4 : 0));
 #pragma unroll
       for (int j = 0; j < kTblLds / kThreads; ++j)
         tv[j] = __builtin_amdgcn_raw_buffer_load_b32(trs, (int)((threadIdx.x + kThreads * j) * 4), 0, 0);
     }
-    // the attention queries, parked in shared memory below
-    uint32_t qw[QPT];
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int w = threadIdx.x + i * kThreads;
-      qw[i] = w < QWORDS ? reinterpret_cast<const uint32_t*>(qrow)[w] : 0u;
-    }
-
-    // ---- the eviction set: in the steady state no block became full since
-    // the last call and the set is the caller's state as it stands; otherwise
-    // the k_e best of (old set U new blocks) by eviction score, ties to the
-    // lower id, computed below into eids
-    int seen = a.k_e > 0 ? sload(a.evict_seen, row) : 0;
-    if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
-    const bool steady = a.k_e == 0 || seen == nb;
-    const int nprev = min(a.k_e, seen);
-    const int n_e = a.k_e > 0 ? min(a.k_e, nprev + nb - seen) : 0;
-    // this member's items of [eviction set..., tail block]: cr, cr + CE, ...
-    // for the CE attending members, counted from the last of them so that
-    // member 0, which also merges the row, never has more than the others.
-    // With a split gang (a.split) only the first half attends them: those
-    // members start first on their compute units and finish streaming
-    // earlier (a compute unit serves its two workgroups' loads in order), so
-    // the eviction-set work fills their wait for the second half.
-    const int n_eitems = n_e + (tail > 0);
-    const int CE = a.split ? C / 2 : C;
-    const int cr = CE - 1 - c;
-    const int e_mine = cr >= 0 && cr < n_eitems ? (n_eitems - cr + CE - 1) / CE : 0;
-    // items consumed before the statistics hand-off (the rest, at least one
-    // pair, after this member's keys are out); even, so that the slabs keep
-    // alternating
-    const int e_first = e_mine > 2 ? max(2, (e_mine - 2) & ~1) : e_mine;
-    auto e_item = [&](int it) {  // item it of this member's share (scalar loads)
-      const int idx = cr + it * CE;
-      int blk = nb;  // the tail block
-      if (idx < n_e) {
-        const int v = steady ? sload(a.evict_set, (int64_t)row * a.k_e + idx) : eids[idx];
-        blk = min(max(v, 0), nb - 1);
-      }
-      Item x;
-      x.base = ((int64_t)sload(a.table, tb + blk) * a.Hkv + g) * (int64_t)(kBlock * D);
-      x.valid = idx < n_e ? kBlock : tail;
-      x.logits = nullptr;
-      return x;
-    };
-    auto e_issue = [&](Slab<T, D>& s, int it) { slab_issue<T, D, false>(s, e_item(it), kp, vp); };
-    // the caller's eviction set, to shared memory below (steady state; a
-    // bounded buffer load, so that no branch waits for it here)
+    // the caller's eviction set (steady state; a bounded buffer load, so that
+    // no branch waits for it here)
     const int ev_pre = (int)__builtin_amdgcn_raw_buffer_load_b32(
-        make_rsrc(a.evict_set + (int64_t)row * a.k_e, (uint32_t)(steady ? n_e * 4 : 0)),
+        make_rsrc(a.evict_set + (int64_t)row * a.k_e, (uint32_t)(R.steady ? n_e * 4 : 0)),
         (int)threadIdx.x * 4, 0, 0);
 
-    if (!steady) {
-      // blocks became full since the last call: update the set (once per
-      // filled block, before the stream so that no loads wait behind it)
-      uint32_t* ekeys = lds_keys;                                      // ncand
-      int* ev_old = reinterpret_cast<int*>(ekeys + a.k_e + a.nb_max);  // k_e
-      const int ncand = nprev + nb - seen;
-      for (int i = threadIdx.x; i < nprev; i += kThreads)
-        ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
-      __syncthreads();
-      const float* Er = a.E + (int64_t)row * a.max_blocks;
-      for (int i = threadIdx.x; i < ncand; i += kThreads) {
-        const int id = i < nprev ? ev_old[i] : seen + i - nprev;
-        ekeys[i] = order_key(Er[id]);
-      }
-      __syncthreads();
-      if (n_e > 0)
-        wg_top_m(ekeys, ncand, n_e, sm.top, [&](int i, int pos) {
-          eids[pos] = i < nprev ? ev_old[i] : seen + i - nprev;
-        });
-      __syncthreads();
-    }
-
-    // ---- 1. logits of this member's representatives, in registers
-    float lg[U][KEEP];
+    // ---- 1. logits of this scorer's representatives (to shared memory) and
+    // their running softmax statistics (group softmax), per lane
+    float m_run[KEEP], s_run[KEEP];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int kk = 0; kk < KEEP; ++kk) lg[u][kk] = -INFINITY;
+    for (int kk = 0; kk < KEEP; ++kk) {
+      m_run[kk] = -INFINITY;
+      s_run[kk] = 0.f;
     }
-    Slab<T, D> sa, sb;
-    Item e0{}, e1{};
     {
-      QSlice<T, D> qs[GS];
       const T* qb = static_cast<const T*>(a.query) +
-                    (FORECAST ? (int64_t)row * D : ((int64_t)b * a.Hkv + g) * G * D);
+                    (FORECAST ? (int64_t)row * D : ((int64_t)R.b * a.Hkv + R.g) * G * D);
+      QSlice<T, D> qs[QLDS ? 1 : GS];
+      if constexpr (QLDS) {
+        for (int i = threadIdx.x; i < GS * D; i += kThreads) sm.sq[i / D][i % D] = qb[i];
+        __syncthreads();
+      } else {
 #pragma unroll
-      for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
+        for (int h = 0; h < GS; ++h) qs[h].load(qb + h * D, q);
+      }
       const T* rb = static_cast<const T*>(a.reps) + (int64_t)row * a.max_blocks * kSubs * D;
       // two batches of USL slots in flight: the next batch is requested
-      // before the current one is consumed, so the requests of the two
-      // workgroups sharing a compute unit interleave finely
+      // before the current one is consumed
       auto issue = [&](uint4 (&x)[USL][NLD], int u0) {
 #pragma unroll
         for (int uu = 0; uu < USL; ++uu) {
@@ -327,23 +368,41 @@ struct Gang {
         for (int uu = 0; uu < USL; ++uu) {
           const int j = j0 + (u0 + uu) * RPI + wave * 16 + r;
           float v[GS];
+          if constexpr (QLDS) {
 #pragma unroll
-          for (int h = 0; h < GS; ++h) v[h] = qs[h].dot(x[uu]);
+            for (int hb = 0; hb < GS; hb += HBS) {
+              asm volatile("" ::: "memory");
+              QSlice<T, D> qh[HBS];
+#pragma unroll
+              for (int h = 0; h < HBS; ++h) qh[h].load(&sm.sq[hb + h][0], q);
+#pragma unroll
+              for (int h = 0; h < HBS; ++h) v[hb + h] = qh[h].dot(x[uu]);
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < GS; ++h) v[h] = qs[h].dot(x[uu]);
+          }
           quad_reduce<2, GS>(v, q);
 #pragma unroll
-          for (int kk = 0; kk < KEEP; ++kk)
-            lg[u0 + uu][kk] = j < j1 ? v[kk] * a.qscale_sel : -INFINITY;
+          for (int kk = 0; kk < KEEP; ++kk) {
+            const float l = j < j1 ? v[kk] * a.qscale_sel : -INFINITY;
+            sm.lgs[u0 + uu][kk][threadIdx.x] = l;
+            if constexpr (!FORECAST) {
+              const float mn = fmaxf(m_run[kk], l);
+              if (mn != -INFINITY) {
+                s_run[kk] = s_run[kk] * exp2f(m_run[kk] - mn) + exp2f(l - mn);
+                m_run[kk] = mn;
+              }
+            }
+          }
         }
       };
       uint4 xa[USL][NLD], xb[USL][NLD];
       issue(xa, 0);
       {
-        // the first two eviction-set items' addresses (their scalar loads
-        // overlap the stream), the set itself and the attention queries to
-        // shared memory
-        if (e_mine > 0) e0 = e_item(0);
-        if (e_mine > 1) e1 = e_item(1);
-        if (steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
+        // the eviction set and the table row to shared memory while the
+        // first loads are in flight
+        if (R.steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
         if (tbl_lds) {
 #pragma unroll
           for (int j = 0; j < kTblLds / kThreads; ++j) {
@@ -351,52 +410,32 @@ struct Gang {
             if (i < nb) tbl[i] = (int)tv[j];
           }
         }
-        uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
-#pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-          const int w = threadIdx.x + i * kThreads;
-          if (w < QWORDS) ql[w] = qw[i];
-        }
       }
-      static_assert(U % (2 * USL) == 0, "slots per lane");
-#pragma unroll
-      for (int u0 = 0; u0 < U; u0 += 2 * USL) {
+      static_assert(U % (2 * USL) == 0 && U % 4 == 0, "slots per lane");
+#pragma unroll 1
+      for (int u0 = 0; u0 < nsl; u0 += 2 * USL) {
         issue(xb, u0 + USL);
         consume(xa, u0);
-        if (u0 + 2 * USL < U) issue(xa, u0 + 2 * USL);
+        if (u0 + 2 * USL < nsl) issue(xa, u0 + 2 * USL);
         consume(xb, u0 + USL);
       }
     }
-    // the first two eviction-set slabs: in flight while the statistics are
-    // formed and published
-    if (e_mine > 0) slab_issue<T, D, false>(sa, e0, kp, vp);
-    if (e_mine > 1) slab_issue<T, D, false>(sb, e1, kp, vp);
 
-    // ---- 2. softmax statistics of this member's logits (group softmax)
+    // ---- 2. softmax statistics of this scorer's logits (group softmax)
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
     const uint32_t st_off = (uint32_t)(((int64_t)row * kMaxGang) * G * 8);
     if constexpr (!FORECAST) {
-      float m[KEEP], s[KEEP];
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) {
-        m[kk] = -INFINITY;
-        s[kk] = 0.f;
-        if (canon) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) m[kk] = fmaxf(m[kk], lg[u][kk]);
-          if (m[kk] != -INFINITY) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) s[kk] += exp2f(lg[u][kk] - m[kk]);
-          }
-        }
-        merge_ms_lanes(m[kk], s[kk], 4);  // the lanes of this slot's head(s)
+        float m = canon ? m_run[kk] : -INFINITY, s = canon ? s_run[kk] : 0.f;
+        merge_ms_lanes_flat(m, s, 4);  // the lanes of this slot's head(s)
         if (r == 0) {
-          sm.red_m[wave][q][kk] = m[kk];
-          sm.red_s[wave][q][kk] = s[kk];
+          sm.red_m[wave][q][kk] = m;
+          sm.red_s[wave][q][kk] = s;
         }
       }
       __syncthreads();
-      if (threadIdx.x < G) {
+      if (m_row > 0 && threadIdx.x < G) {
         const int h = threadIdx.x;
         const int qq = G >= 4 ? h / KEEP : h * DUP, kk = G >= 4 ? h % KEEP : 0;
         float rm[kWaves], rs[kWaves];  // every wave's pair first (one wait)
@@ -405,198 +444,168 @@ struct Gang {
           rm[w] = sm.red_m[w][qq][kk];
           rs[w] = sm.red_s[w][qq][kk];
         }
-        float M = rm[0], S = rs[0];
+        float M = rm[0], S = 0.f;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) merge_ms(M, S, rm[w], rs[w]);
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, rm[w]);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) S += rm[w] == -INFINITY ? 0.f : rs[w] * exp2f(rm[w] - M);
         store_agent_f32x2(srs, st_off + (uint32_t)((c * G + h) * 8), f32x2{M, S});
       }
     }
-    // the logits wait in shared memory while this member attends
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int kk = 0; kk < KEEP; ++kk) sm.lgs[u][kk][threadIdx.x] = lg[u][kk];
-    }
-    __syncthreads();  // the queries and the eviction set are in shared memory
-
-    // ---- this member's first eviction-set items (two slabs in flight)
-    AttnState<T, D, G> att;
-    att.init();
-    for (int it = 0; it < e_first; it += 2) {
-      att.consume(sa, sm.att, a.qscale_att);
-      if (it + 2 < e_mine) e_issue(sa, it + 2);
-      if (it + 1 < e_first) {
-        att.consume(sb, sm.att, a.qscale_att);
-        if (it + 3 < e_mine) e_issue(sb, it + 3);
-      }
+    if (m_row == 0) {
+      __syncthreads();  // the table row and the eviction set are in shared memory
+      return 0;
     }
 
-    // ---- exclusion flags of this member's blocks (the eviction set is never
+    // ---- exclusion flags of this scorer's blocks (the eviction set is never
     // a query-aware candidate), set while the statistics come in
-    const int m_row = max(0, min(a.k - n_e, nb - n_e));
-    if (m_row > 0) {
-      for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
-      __syncthreads();
-      for (int i = threadIdx.x; i < n_e; i += kThreads) {
-        const int id = eids[i];
-        if (id >= blk0 && id < blk0 + nblk) sm.ckeys[id - blk0] = 0u;
-      }
+    for (int i = threadIdx.x; i < CBLK; i += kThreads) sm.ckeys[i] = 1u;  // 1 = not excluded
+    __syncthreads();  // also: the logits, the table row and the eviction set
+    for (int i = threadIdx.x; i < n_e; i += kThreads) {
+      const int id = eids[i];
+      if (id >= blk0 && id < blk0 + nblk) sm.ckeys[id - blk0] = 0u;
     }
 
-    // ---- 3. row normaliser from every member's statistics
+    // ---- 3. row normaliser from every scorer's statistics
     if constexpr (!FORECAST) {
-      if (m_row > 0 && wave == 0) {
-        // lane: members lane / G, + 64 / G, ...; head lane % G
+      if (wave == 0) {
         float M = -INFINITY, S = 0.f;
-        wave_poll_pairs<NP>(srs, st_off, C * G, err, a.wait_ticks,
+        wave_poll_pairs<NP>(srs, st_off, a.CS * G, err, a.wait_ticks,
                             [&](int, f32x2 st) { merge_ms(M, S, st.x, st.y); });
         merge_ms_lanes(M, S, G);
-        if (lane < G) {
-          sm.sM[lane] = M;
-          sm.sInvZ[lane] = S > 0.f ? 1.f / S : 0.f;
-        }
+        if (lane < G) sm.sM[lane] = S > 0.f ? M + log2f(S) : INFINITY;
       }
     }
 
-    // ---- scores of this member's blocks, published as keys (+1)
+    // ---- scores of this scorer's blocks, published as keys (+1)
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.keys, a.keys_bytes);
     const uint32_t key_off = (uint32_t)((int64_t)row * a.nb_max * 4);
-    if (m_row > 0) {
-      __syncthreads();  // the normaliser and the exclusion flags
-      // every shared-memory read first (one wait for all of them), then the
-      // arithmetic without branches; the 16 lanes of a block read its
-      // exclusion flag together
-      float lv[U][KEEP];
-      uint32_t ex[U];
+    __syncthreads();  // the normaliser and the exclusion flags
+    {
+      // per head: 2^(l - M) / Z = 2^(l - (M + log2 Z))
+      float mh[KEEP];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int kk = 0; kk < KEEP; ++kk) mh[kk] = FORECAST ? 0.f : sm.sM[h0 + kk];
+      // four slots per round: every shared-memory read of the round first,
+      // then the four slots' arithmetic side by side without branches (the
+      // steps of one slot depend on each other); the 16 lanes of a block read
+      // and write its exclusion flag / key together
+#pragma unroll 1
+      for (int u0 = 0; u0 < nsl; u0 += 4) {
+        float lv[4][KEEP];
+        uint32_t ex[4];
 #pragma unroll
-        for (int kk = 0; kk < KEEP; ++kk) lv[u][kk] = sm.lgs[u][kk][threadIdx.x];
-        ex[u] = sm.ckeys[u * 16 + wave * 4 + (lane >> 4)];
-      }
-      float mh[KEEP], iz[KEEP];
+        for (int uu = 0; uu < 4; ++uu) {
 #pragma unroll
-      for (int kk = 0; kk < KEEP; ++kk) {
-        mh[kk] = FORECAST ? 0.f : sm.sM[h0 + kk];
-        iz[kk] = FORECAST ? 0.f : sm.sInvZ[h0 + kk];
-      }
+          for (int kk = 0; kk < KEEP; ++kk) lv[uu][kk] = sm.lgs[u0 + uu][kk][threadIdx.x];
+          ex[uu] = sm.ckeys[(u0 + uu) * 16 + wave * 4 + (lane >> 4)];
+        }
+        float v[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float v = 0.f;
-        if constexpr (FORECAST) {
-          v = lv[u][0];
-        } else {
+        for (int uu = 0; uu < 4; ++uu) {
+          if constexpr (FORECAST) {
+            v[uu] = lv[uu][0];
+          } else {
+            v[uu] = 0.f;
 #pragma unroll
-          for (int kk = 0; kk < KEEP; ++kk) {
-            const float l = lv[u][kk];
-            const float e = exp2f(l - mh[kk]) * iz[kk];
-            v += (canon && l != -INFINITY) ? e : 0.f;
+            for (int kk = 0; kk < KEEP; ++kk) {
+              const float l = lv[uu][kk];
+              // native 2^x: probabilities below 2^-126 of a head's
+              // total only flush to zero
+              const float e = fast_exp2(l - mh[kk]);
+              v[uu] += (canon && l != -INFINITY) ? e : 0.f;
+            }
           }
-          v += quad_partner<2>(v);
-          v += quad_partner<1>(v);
         }
-        v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
-        v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
-        const int j = j0 + u * RPI + wave * 16 + (lane >> 2);
-        const uint32_t key = (j < j1 && ex[u] != 0u) ? order_key(v) : 0u;
-        if ((lane & 15) == 0) sm.ckeys[u * 16 + wave * 4 + (lane >> 4)] = key;
+        if constexpr (!FORECAST) {
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) v[uu] += quad_partner<2>(v[uu]);
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) v[uu] += quad_partner<1>(v[uu]);
+        }
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) v[uu] = fmaxf(v[uu], dpp_mov<0x124>(v[uu]));  // row_ror:4
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) v[uu] = fmaxf(v[uu], dpp_mov<0x128>(v[uu]));  // row_ror:8
+        uint32_t key[4];
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const int j = j0 + (u0 + uu) * RPI + wave * 16 + (lane >> 2);
+          const bool valid = (u0 + uu < nsl) & (j < j1) & (ex[uu] != 0u);
+          key[uu] = valid ? order_key(v[uu]) : 0u;
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) sm.ckeys[(u0 + uu) * 16 + wave * 4 + (lane >> 4)] = key[uu];
+        }
       }
-      __syncthreads();
-      if ((int)threadIdx.x < nblk)
-        __builtin_amdgcn_raw_buffer_store_b32(sm.ckeys[threadIdx.x] + 1u, krs,
-                                              (int)(key_off + (blk0 + threadIdx.x) * 4), 0, kSC1);
     }
+    __syncthreads();
+    if ((int)threadIdx.x < nblk)
+      __builtin_amdgcn_raw_buffer_store_b32(sm.ckeys[threadIdx.x] + 1u, krs,
+                                            (int)(key_off + (blk0 + threadIdx.x) * 4), 0, kSC1);
 
-    // ---- the rest of this member's eviction-set share
-    for (int it = e_first; it < e_mine; it += 2) {
-      att.consume(sa, sm.att, a.qscale_att);
-      if (it + 2 < e_mine) e_issue(sa, it + 2);
-      if (it + 1 < e_mine) {
-        att.consume(sb, sm.att, a.qscale_att);
-        if (it + 3 < e_mine) e_issue(sb, it + 3);
-      }
-    }
-
-    // ---- 4. the row's query-aware set from every member's keys, ascending
-    if (m_row > 0) {
-      // every member's keys (polled until none is missing), in registers for
-      // rows of up to kSmallKpt * kThreads blocks and in shared memory
-      constexpr int kSmallKpt = 8;
-      uint32_t* rkeys = lds_keys;  // nb
-      uint32_t kv[kSmallKpt];
-      Patience pt;  // each wave polls its own share, reading again only what is missing
-      pt.start();
+    // ---- 4. the row's query-aware set from every scorer's keys, ascending:
+    // every key polled until none is missing (in registers for rows of up to
+    // kSmallKpt * kThreads blocks, in shared memory beyond)
+    constexpr int kSmallKpt = 8;
+    uint32_t* rkeys = lds_keys;  // nb
+    uint32_t kv[kSmallKpt];
+    Patience pt;  // each wave polls its own share, reading again only what is missing
+    pt.start();
 #pragma unroll
-      for (int j = 0; j < kSmallKpt; ++j) kv[j] = 0u;
-      for (;;) {
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < kSmallKpt; ++j) {
-          const int i = threadIdx.x + kThreads * j;
-          if (i < nb && kv[j] == 0u)
-            kv[j] = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
-        }
-        for (int i = threadIdx.x + kThreads * kSmallKpt; i < nb; i += kThreads) {
-          const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
-          rkeys[i] = v;
-          ok &= v != 0u;
-        }
-        const uint32_t e = pt.read_err(err);
-#pragma unroll
-        for (int j = 0; j < kSmallKpt; ++j) ok &= (int)threadIdx.x + kThreads * j >= nb || kv[j] != 0u;
-        if (__all(ok)) break;
-        if (!pt.more(e, err, a.wait_ticks)) break;
-      }
+    for (int j = 0; j < kSmallKpt; ++j) kv[j] = 0u;
+    for (;;) {
+      bool ok = true;
 #pragma unroll
       for (int j = 0; j < kSmallKpt; ++j) {
         const int i = threadIdx.x + kThreads * j;
-        if (i < nb) rkeys[i] = kv[j];
+        if (i < nb && kv[j] == 0u)
+          kv[j] = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
       }
-      __syncthreads();  // every wave's share is in
-      auto put = [&](int i, int pos) {
-        if (pos < m_row) qsel[pos] = i;
-      };
-      bool done = false;
-      if (nb <= kSmallKpt * kThreads) done = wg_top_small<kSmallKpt>(kv, m_row, sm.small, put);
-      if (!done) {
-        uint32_t P;
-        int shift, take_eq;
-        wg_radix_top(rkeys, nb, m_row, sm.rad, &P, &shift, &take_eq);
-        wg_radix_emit(rkeys, nb, P, shift, take_eq, sm.rad, put);
+      for (int i = threadIdx.x + kThreads * kSmallKpt; i < nb; i += kThreads) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(krs, (int)(key_off + i * 4), 0, kSC1);
+        rkeys[i] = v;
+        ok &= v != 0u;
       }
-      __syncthreads();
+      const uint32_t e = pt.read_err(err);
+#pragma unroll
+      for (int j = 0; j < kSmallKpt; ++j) ok &= (int)threadIdx.x + kThreads * j >= nb || kv[j] != 0u;
+      if (__all(ok)) break;
+      if (!pt.more(e, err, a.wait_ticks)) break;
     }
-
-    // ---- attention over this member's share of the query-aware set:
-    // positions c, c + C, ... of the ascending list
-    const int q_mine = m_row > c ? (m_row - c + C - 1) / C : 0;
-    auto q_issue = [&](Slab<T, D>& s, int it) {
-      const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * C]), 0), nb - 1);
-      Item x;
-      const int64_t phys = tbl_lds ? tbl[blk] : sload(a.table, tb + blk);
-      x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
-      x.valid = kBlock;
-      x.logits = nullptr;
-      slab_issue<T, D, false>(s, x, kp, vp);
+#pragma unroll
+    for (int j = 0; j < kSmallKpt; ++j) {
+      const int i = threadIdx.x + kThreads * j;
+      if (i < nb) rkeys[i] = kv[j];
+    }
+    __syncthreads();  // every wave's share is in
+    auto put = [&](int i, int pos) {
+      if (pos < m_row) qsel[pos] = i;
     };
-    if (q_mine > 0) q_issue(sa, 0);
-    if (q_mine > 1) q_issue(sb, 1);
-    for (int it = 0; it < q_mine; it += 2) {
-      att.consume(sa, sm.att, a.qscale_att);
-      if (it + 2 < q_mine) q_issue(sa, it + 2);
-      if (it + 1 < q_mine) {
-        att.consume(sb, sm.att, a.qscale_att);
-        if (it + 3 < q_mine) q_issue(sb, it + 3);
-      }
+    bool done = false;
+    if (nb <= kSmallKpt * kThreads) done = wg_top_small<kSmallKpt>(kv, m_row, sm.small, put);
+    if (!done) {
+      uint32_t P;
+      int shift, take_eq;
+      wg_radix_top(rkeys, nb, m_row, sm.rad, &P, &shift, &take_eq);
+      wg_radix_emit(rkeys, nb, P, shift, take_eq, sm.rad, put);
     }
+    __syncthreads();
+    return m_row;
+  }
 
-    // ---- 5. this member's partial; member 0 merges the row
-    const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
-    const __amdgpu_buffer_rsrc_t acr = make_rsrc(a.part_acc, a.acc_bytes);
-    att.to_lds(sm.att);
-    wg_publish_partial(sm.att, sm.ml, mlr, acr, (int64_t)row * kMaxGang + c);
-    if (c != 0) return;
-
+  // ---- scorer 0 of a row, after its own partial: the selected list, the
+  // merge of every member's partial into the output, the eviction state and
+  // the clearing of the row's hand-off slots.
+  static __device__ __attribute__((always_inline)) void finish_row(const GangArgs& a, int row,
+                                                                   const Row& R, int m_row,
+                                                                   Smem& sm, const int* eids,
+                                                                   const int* qsel) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nb = R.nb, n_e = R.n_e;
+    uint32_t* err = a.err;
     // the selected ids, ascending, while the other partials arrive (the
     // eviction set and the query-aware list are each ascending and disjoint:
     // each id goes after the smaller ids of the other list)
@@ -622,8 +631,15 @@ struct Gang {
     for (int t = n_e + m_row + threadIdx.x; t < a.k; t += kThreads) sel[t] = -1;
     if (threadIdx.x == 0) a.num_selected[row] = n_e + m_row;
 
+    const int members = a.CS + a.CA;
+    const uint32_t st_off = (uint32_t)(((int64_t)row * kMaxGang) * G * 8);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.stats, a.stats_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.keys, a.keys_bytes);
+    const uint32_t key_off = (uint32_t)((int64_t)row * a.nb_max * 4);
+    const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
+    const __amdgpu_buffer_rsrc_t acr = make_rsrc(a.part_acc, a.acc_bytes);
     if (wave == 0) {
-      wave_poll_pairs<NP>(mlr, st_off, C * G, err, a.wait_ticks, [&](int, f32x2) {});
+      wave_poll_pairs<NP>(mlr, st_off, members * G, err, a.wait_ticks, [&](int, f32x2) {});
       // an expired wait anywhere in the gang (each member records its own
       // before publishing its partial) leaves the eviction state untouched,
       // so that the step can be run again from the same state
@@ -634,18 +650,18 @@ struct Gang {
     // every member's partial is in, so every member is done with the row's
     // statistics and keys: clear those slots (the partials' after the merge)
     if (!FORECAST)
-      for (int i = threadIdx.x; i < C * G; i += kThreads)
+      for (int i = threadIdx.x; i < a.CS * G; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, srs, (int)(st_off + i * 8), 0, kSC1);
     if (m_row > 0)
       for (int i = threadIdx.x; i < nb; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b32(0u, krs, (int)(key_off + i * 4), 0, kSC1);
-    T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
-    combine_partials<T, D, G>((int64_t)row * kMaxGang, C, mlr, acr, out);
+    T* out = static_cast<T*>(a.out) + ((int64_t)R.b * a.Hkv + R.g) * G * D;
+    combine_partials<T, D, G>((int64_t)row * kMaxGang, members, mlr, acr, out);
 
     // the eviction state, when it changed: every member has read the old one
     // (its partial is in)
     if (failed && a.status != nullptr && threadIdx.x == 0) a.status[0] = 1;
-    if (!steady && !failed) {
+    if (!R.steady && !failed) {
       for (int i = threadIdx.x; i < a.k_e; i += kThreads)
         a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? eids[i] : -1;
       if (threadIdx.x == 0) a.evict_seen[row] = nb;
@@ -654,8 +670,62 @@ struct Gang {
     // this workgroup's merge (a subset of its waves) is done with the
     // partials: clear their (m, l) slots
     __syncthreads();
-    for (int i = threadIdx.x; i < C * G; i += kThreads)
+    for (int i = threadIdx.x; i < members * G; i += kThreads)
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, mlr, (int)(st_off + i * 8), 0, kSC1);
+  }
+
+  // ---- one row for member c of its role.  Attenders take positions c,
+  // c + CA, ... of [eviction set..., tail block] and wait for nobody;
+  // scorers select (select_row), then take positions c, c + CS, ... of the
+  // query-aware list (and of the eviction list when the row has no
+  // attenders), and scorer 0 finishes the row.
+  static __device__ __attribute__((always_inline)) void row_step(const GangArgs& a, int row,
+                                                                 bool scorer, int c, Smem& sm,
+                                                                 uint32_t* dyn) {
+    const Row R = row_info(a, row);
+    int* eids = reinterpret_cast<int*>(dyn);             // k_e: the eviction set
+    int* qsel = eids + (a.k_e > 0 ? a.k_e : 1);          // k: query-aware blocks
+    int* tbl = qsel + a.k;                               // min(nb_max, kTblLds)
+    uint32_t* lds_keys = reinterpret_cast<uint32_t*>(tbl + min(a.nb_max, kTblLds));
+    queries_to_lds(a, R, sm);
+    if (!R.steady) eviction_update(a, row, R, sm, eids, lds_keys);
+    int m_row = 0, stride = a.CA;
+    if (scorer) {
+      m_row = select_row(a, row, R, c, sm, eids, qsel, tbl, lds_keys);
+      stride = a.CS;
+    } else {
+      if (R.steady) {
+        for (int i = threadIdx.x; i < R.n_e; i += kThreads)
+          eids[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), R.nb - 1);
+      }
+      // the attender's loads wait until its partner scorer (c mod CS) has
+      // streamed its share of the row's representatives (its softmax
+      // statistics are out): until then the representatives, which the
+      // hand-offs wait for, have the memory to themselves.  Rows without
+      // query-aware blocks, and the forecast mode, publish no statistics.
+      const int m_row_a = max(0, min(a.k - R.n_e, R.nb - R.n_e));
+      if (!FORECAST && m_row_a > 0 && threadIdx.x < kWave) {
+        const uint32_t st_off = (uint32_t)(((int64_t)row * kMaxGang + c % a.CS) * G * 8);
+        wave_poll_pairs<1>(make_rsrc(a.stats, a.stats_bytes), st_off, G, a.err, a.wait_ticks,
+                           [&](int, f32x2) {});
+      }
+      __syncthreads();  // the queries and the eviction set
+    }
+    const int q_mine = m_row > c ? (m_row - c + stride - 1) / stride : 0;
+    const int n_eitems = (!scorer || a.CA == 0) ? R.n_e + (R.tail > 0) : 0;
+    const int e_mine = c < n_eitems ? (n_eitems - c + stride - 1) / stride : 0;
+    const bool tbl_lds = R.nb <= kTblLds;
+    attend_publish(a, row, scorer ? c : a.CS + c, q_mine + e_mine, [&](int it) {
+      if (it >= q_mine) return e_item(a, R, eids, c + (it - q_mine) * stride);
+      const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * stride]), 0), R.nb - 1);
+      Item x;
+      const int64_t phys = tbl_lds ? tbl[blk] : sload(a.table, R.tb + blk);
+      x.base = (phys * a.Hkv + R.g) * (int64_t)(kBlock * D);
+      x.valid = kBlock;
+      x.logits = nullptr;
+      return x;
+    }, sm);
+    if (scorer && c == 0) finish_row(a, row, R, m_row, sm, eids, qsel);
   }
 };
 
@@ -667,27 +737,22 @@ constexpr int gang_wgs_per_cu() {
   return (G >= 8 || (sizeof(T) == 4 && D == 128)) ? 1 : 2;
 }
 
+// The grid: gangs * CS scorers first (the dispatcher places them first on
+// their compute units, and a compute unit serves the loads of the workgroup
+// placed first ahead of the other's), then gangs * CA attenders.
 template <typename T, int D, int G, bool FORECAST>
 __global__ __launch_bounds__(kThreads, (gang_wgs_per_cu<T, D, G>())) void gang_kernel(
     const GangArgs a) {
   using S = Gang<T, D, G, FORECAST>;
   __shared__ typename S::Smem sm;
   extern __shared__ uint32_t dyn[];
-  // split gangs: the first half of the grid (which the dispatcher places
-  // first on every compute unit) holds members 0 .. C/2 - 1 of every gang,
-  // the second half members C/2 .. C - 1
-  int gang, c;
-  if (a.split) {
-    const int hc = a.C / 2, half = a.gangs * hc;
-    const int b = (int)blockIdx.x < half ? (int)blockIdx.x : (int)blockIdx.x - half;
-    gang = b / hc;
-    c = b % hc + ((int)blockIdx.x < half ? 0 : hc);
-  } else {
-    gang = blockIdx.x / a.C;
-    c = blockIdx.x % a.C;
-  }
+  const int ns = a.gangs * a.CS;
+  const bool scorer = (int)blockIdx.x < ns;
+  const int b = scorer ? (int)blockIdx.x : (int)blockIdx.x - ns;
+  const int per = scorer ? a.CS : a.CA;
+  const int gang = b / per, c = b % per;
   for (int row = gang; row < a.rows; row += a.gangs) {
-    S::row_step(a, row, c, sm, dyn);
+    S::row_step(a, row, scorer, c, sm, dyn);
     __syncthreads();
   }
 }
@@ -700,7 +765,8 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   hipError_t e = grid_info(fn, kThreads, gang_dyn_lds(lay, L.k, L.k_e), &gi);
   if (e != hipSuccess) return e;
   GangPlan plan;
-  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, gi.per_cu, L.gang_override, &plan))
+  if (!gang_plan(lay, L.k, L.k_e, gi.per_cu * gi.cus, gang_reps_cap((int)sizeof(T), D, G),
+                 L.gang_override, L.att_override, &plan))
     return hipErrorLaunchOutOfResources;
   GangArgs a{};
   a.query = L.query;
@@ -729,10 +795,10 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   a.nb_max = lay.nb_max;
   a.k = L.k;
   a.k_e = L.k_e;
-  a.C = plan.C;
+  a.CS = plan.CS;
+  a.CA = plan.CA;
   a.gangs = plan.gangs;
   a.per_wg = plan.per_wg;
-  a.split = plan.split;
   a.qscale_sel = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;
   a.qscale_att = L.scale * 1.4426950408889634f;
   a.wait_ticks = (uint64_t)(gi.wall_khz > 0 ? gi.wall_khz : 1) * kWaitMs;
@@ -740,7 +806,8 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   a.ml_bytes = (uint32_t)(lay.off_acc - lay.off_ml);
   a.acc_bytes = (uint32_t)(lay.off_keys - lay.off_acc);
   a.keys_bytes = (uint32_t)(lay.bytes - lay.off_keys);
-  gang_kernel<T, D, G, FORECAST><<<plan.gangs * plan.C, kThreads, plan.dyn_lds, stream>>>(a);
+  gang_kernel<T, D, G, FORECAST><<<plan.gangs * (plan.CS + plan.CA), kThreads, plan.dyn_lds,
+                                   stream>>>(a);
   return hipGetLastError();
 }
 

@@ -249,7 +249,6 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
  * run again (nsa_select_blocks + nsa_sparse_decode give the same results
  * without the residency assumption).  nsa_decode_step_status reports the
  * word to the host and clears the workspace.
- * max_seq_len is limited to 524288 tokens (NSA_ERR_UNSUPPORTED above).
  * ------------------------------------------------------------------------ */
 nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_select_params* params,
                                            int32_t max_seq_len, size_t* bytes);
