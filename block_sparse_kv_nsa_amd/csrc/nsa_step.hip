@@ -173,6 +173,7 @@ struct Gang {
   // from shared memory, four heads at a time, for every load slot
   static constexpr bool QLDS = GS * NLD * 4 > 128;
   static constexpr int HBS = QLDS ? 4 : GS;
+  static constexpr int kAttItems = 64;  // an attender's items whose blocks are looked up early
 
   struct Smem {
     AttendSmem<T, D, G> att;
@@ -186,6 +187,7 @@ struct Gang {
     T sq[QLDS ? GS : 1][QLDS ? D : 1] __attribute__((aligned(16)));  // selector query (QLDS)
     f32x2 ml[G];
     int s_int[8];
+    int ephys[kAttItems];  // an attender's first items: physical blocks
   };
 
   // What both roles know of a row before any wait.
@@ -266,9 +268,11 @@ struct Gang {
     }
   }
 
-  // Attention over this workgroup's n items (item(it) -> Item), two slabs in
+  // Attention over this workgroup's n items (item(it) -> Item), NS slabs in
   // flight, one online-softmax state per wave; the merged partial published
   // as partial `member` of the row.
+  static constexpr int SLAB_REGS = (Q::NLD + VGeo<T, D>::NLV) * 4;
+  static constexpr int NS = 2;
   template <typename ItemFn>
   static __device__ __forceinline__ void attend_publish(const GangArgs& a, int row, int member,
                                                         int n, ItemFn item, Smem& sm) {
@@ -276,15 +280,17 @@ struct Gang {
     const T* vp = static_cast<const T*>(a.v_pool);
     AttnState<T, D, G> att;
     att.init();
-    Slab<T, D> sa, sb;
-    if (n > 0) slab_issue<T, D, false>(sa, item(0), kp, vp);
-    if (n > 1) slab_issue<T, D, false>(sb, item(1), kp, vp);
-    for (int it = 0; it < n; it += 2) {
-      att.consume(sa, sm.att, a.qscale_att);
-      if (it + 2 < n) slab_issue<T, D, false>(sa, item(it + 2), kp, vp);
-      if (it + 1 < n) {
-        att.consume(sb, sm.att, a.qscale_att);
-        if (it + 3 < n) slab_issue<T, D, false>(sb, item(it + 3), kp, vp);
+    Slab<T, D> sl[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (i < n) slab_issue<T, D, false>(sl[i], item(i), kp, vp);
+    for (int it = 0; it < n; it += NS) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (it + i < n) {  // uniform
+          att.consume(sl[i], sm.att, a.qscale_att);
+          if (it + i + NS < n) slab_issue<T, D, false>(sl[i], item(it + i + NS), kp, vp);
+        }
       }
     }
     const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.part_ml, a.ml_bytes);
@@ -697,6 +703,17 @@ struct Gang {
       if (R.steady) {
         for (int i = threadIdx.x; i < R.n_e; i += kThreads)
           eids[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), R.nb - 1);
+        __syncthreads();
+      }
+      // the physical blocks of this attender's first items (positions c,
+      // c + CA, ... of [eviction set..., tail block])
+      const int n_items = R.n_e + (R.tail > 0);
+      for (int t = threadIdx.x; t < kAttItems; t += kThreads) {
+        const int idx = c + t * a.CA;
+        if (idx < n_items) {
+          const int blk = idx < R.n_e ? eids[idx] : R.nb;
+          sm.ephys[t] = a.table[R.tb + blk];
+        }
       }
       // the attender's loads wait until its partner scorer (c mod CS) has
       // streamed its share of the row's representatives (its softmax
@@ -709,14 +726,27 @@ struct Gang {
         wave_poll_pairs<1>(make_rsrc(a.stats, a.stats_bytes), st_off, G, a.err, a.wait_ticks,
                            [&](int, f32x2) {});
       }
-      __syncthreads();  // the queries and the eviction set
+      __syncthreads();  // the queries, the eviction set and the item blocks
     }
     const int q_mine = m_row > c ? (m_row - c + stride - 1) / stride : 0;
     const int n_eitems = (!scorer || a.CA == 0) ? R.n_e + (R.tail > 0) : 0;
     const int e_mine = c < n_eitems ? (n_eitems - c + stride - 1) / stride : 0;
     const bool tbl_lds = R.nb <= kTblLds;
     attend_publish(a, row, scorer ? c : a.CS + c, q_mine + e_mine, [&](int it) {
-      if (it >= q_mine) return e_item(a, R, eids, c + (it - q_mine) * stride);
+      if (it >= q_mine) {
+        const int ie = it - q_mine;
+        if (!scorer && ie < kAttItems) {
+          // looked up before the attender's loads were released
+          const int idx = c + ie * stride;
+          Item x;
+          x.base = ((int64_t)__builtin_amdgcn_readfirstlane(sm.ephys[ie]) * a.Hkv + R.g) *
+                   (int64_t)(kBlock * D);
+          x.valid = idx < R.n_e ? kBlock : R.tail;
+          x.logits = nullptr;
+          return x;
+        }
+        return e_item(a, R, eids, c + ie * stride);
+      }
       const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * stride]), 0), R.nb - 1);
       Item x;
       const int64_t phys = tbl_lds ? tbl[blk] : sload(a.table, R.tb + blk);
