@@ -14,11 +14,13 @@
 // slabs while it computes the current one (attend_items); the last workgroup
 // of each row (atomic ticket) merges the partials and writes the output.
 //
-// Early stop (S2O summary, "Regola di Arresto Anticipato"): pass 1
-// (es_mass_kernel) computes every listed block's logits and per-head
-// (max, sum) and the row's last workgroup finds the stop position n*;
-// pass 2 is the decode kernel reading those logits instead of keys and
-// attending only the first n* listed blocks and the tail.
+// Early stop (S2O summary, "Regola di Arresto Anticipato"; "Implementazione
+// del Kernel": a first dense pass seeds the state, then the blocks in order
+// of estimated importance): one workgroup per row attends the tail block,
+// then walks the ordered list one block at a time and decides after each
+// block whether every head's mass in it fell below tau times the mass
+// accumulated so far; it stops there.  Keys and values are read only up to
+// the stopping block and the two slabs in flight behind it.
 #include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
@@ -39,8 +41,6 @@ struct DecodeArgs {
   uint32_t* counters;
   float* part_ml;        // [rows][splits][G][2]
   float* part_acc;       // [rows][splits][G][D]
-  float* es_logits;      // [rows][items_max][G][64]
-  float* es_ml;          // [rows][items_max][G][2]
   int Hkv, max_blocks, max_selected, items_max, bpw;
   float qscale, tau;
 };
@@ -60,17 +60,16 @@ __device__ __forceinline__ Item item_at(const DecodeArgs& a, int row, int b, int
 }
 
 // ---------------------------------------------------------------------------
-// split-K decode (ES = early-stop pass 2: logits come from pass 1)
+// split-K decode
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, bool ES>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
   const int L = a.seq_lens[b];
   const int nb = L / kBlock;
   const int tail = L - nb * kBlock;
-  const int nlisted = min(a.num_selected[row], a.max_selected);
-  const int nsel = ES ? min(nlisted, a.num_processed[row]) : nlisted;
+  const int nsel = min(a.num_selected[row], a.max_selected);
   const int n_items = nsel + (tail > 0);
   const int i0 = split * a.bpw;
   const int i1 = min(i0 + a.bpw, n_items);
@@ -86,16 +85,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
   auto item = [&](int it) {
     int64_t idx;
-    Item x = item_at(a, row, b, g, it, nsel, nb, tail, D, &idx);
-    if constexpr (ES) {
-      // pass 1 stored the tail after the whole list
-      const int pos = it >= nsel ? nlisted : it;
-      x.logits = a.es_logits + ((int64_t)row * a.items_max + pos) * G * kBlock;
-    }
-    return x;
+    return item_at(a, row, b, g, it, nsel, nb, tail, D, &idx);
   };
-  attend_items<T, D, G, ES>(qrow, static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
-                            a.qscale, i0, i1, item, sm, mlr, acr, (int64_t)row * splits + split);
+  attend_items<T, D, G, false>(qrow, static_cast<const T*>(a.k_pool),
+                               static_cast<const T*>(a.v_pool), a.qscale, i0, i1, item, sm, mlr,
+                               acr, (int64_t)row * splits + split);
 
   if (!last_arrival(a.counters + row, splits, &s_flag)) return;
   T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
@@ -103,173 +97,146 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// early stop, pass 1: logits and per-block mass of every listed block; the
-// row's last workgroup finds the stop position
+// early stop: one workgroup walks a row's ordered list
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_inclusive_scan_f(float v, float* sm /*kWaves*/, float* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  float x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float t = __shfl_up(x, off, kWave);
-    if (lane >= off) x += t;
-  }
-  if (lane == kWave - 1) sm[wave] = x;
-  __syncthreads();
-  float before = 0.f, tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    before += (w < wave) ? sm[w] : 0.f;
-    tot += sm[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x;
-}
+// Each wave keeps an online-softmax state over its 16 of every slab's 64
+// token rows (AttnState: reference m_w per head) and the wave's accumulated
+// mass Lw in the same frame.  After a listed block every wave puts (m_w, Lw,
+// its mass of the block) per head in shared memory; with F = max m_w the
+// row's accumulated mass is A = sum Lw 2^(m_w - F) and the block's mass
+// M = sum mass_w 2^(m_w - F) (the frame cancels in M / A).
+template <typename T, int D, int G>
+struct WalkSmem {
+  AttendSmem<T, D, G> att;
+  float x[2][kWaves][G][3];  // by block parity: (m_w, Lw, block mass) per wave and head
+};
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void es_mass_kernel(DecodeArgs a) {
-  using Q = Quad<T, D>;
-  constexpr int NLD = Q::NLD;
-  constexpr int KEEP = G >= 4 ? G / 4 : 1;
-  constexpr int DUP = G >= 4 ? 1 : 4 / G;
-
+__global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
+  const int row = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int q = lane & 3, r = lane >> 2;
-  const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
   const int L = a.seq_lens[b];
   const int nb = L / kBlock;
   const int tail = L - nb * kBlock;
   const int nsel = min(a.num_selected[row], a.max_selected);
-  const int n_items = nsel + (tail > 0);
-  const int i0 = split * a.bpw;
-  const int i1 = min(i0 + a.bpw, n_items);
-  const int h0 = G >= 4 ? q * KEEP : q / DUP;
-  const bool canon = (q % DUP) == 0;
-  const int tk = wave * kSub + r;
+  const int n_items = (tail > 0) + nsel;  // the tail block first, then the list
+  __shared__ WalkSmem<T, D, G> sm;
 
-  __shared__ float red[kWaves][G];
-  __shared__ float scan_sm[kWaves];
-  __shared__ float sc[G], sT[G], carry[G];
-  __shared__ int s_flag, s_stop;
-
-  QSlice<T, D> qs[G];
+  // the attention queries to shared memory (AttnState reads them there)
   {
-    const T* qb = static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qs[h].load(qb + h * D, q);
+    constexpr int QWORDS = G * D * (int)sizeof(T) / 4;
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(
+        static_cast<const T*>(a.q) + ((int64_t)b * a.Hkv + g) * G * D);
+    uint32_t* ql = reinterpret_cast<uint32_t*>(&sm.att.qlds[0][0]);
+    for (int w = threadIdx.x; w < QWORDS; w += kThreads) ql[w] = qrow[w];
   }
-  const T* kp = static_cast<const T*>(a.k_pool);
-  const uint32_t ml_bytes = (uint32_t)((int64_t)gridDim.y * a.items_max * G * 8);
-  const __amdgpu_buffer_rsrc_t mlr = make_rsrc(a.es_ml, ml_bytes);
-
-  for (int it = i0; it < i1; ++it) {
-    int64_t pos;
-    const Item itm = item_at(a, row, b, g, it, nsel, nb, tail, D, &pos);
-    uint4 kx[NLD];
-#pragma unroll
-    for (int ld = 0; ld < NLD; ++ld)
-      kx[ld] = load16_stream(kp + itm.base + (int64_t)tk * D + Q::elem(ld, q));
-    float v[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) v[h] = qs[h].dot(kx);
-    quad_reduce<2, G>(v, q);
-    float lg[KEEP];
-    float* lp = a.es_logits + ((int64_t)row * a.items_max + pos) * G * kBlock;
-#pragma unroll
-    for (int kk = 0; kk < KEEP; ++kk) {
-      lg[kk] = tk < itm.valid ? v[kk] * a.qscale : -INFINITY;
-      if (canon) lp[(h0 + kk) * kBlock + tk] = lg[kk];
-    }
-    // per-head block max, then sum of 2^(s - max)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = -INFINITY;
-#pragma unroll
-      for (int kk = 0; kk < KEEP; ++kk)
-        if (h0 + kk == h && canon) x = fmaxf(x, lg[kk]);
-      x = wave_max(x);
-      if (lane == 0) red[wave][h] = x;
-    }
-    __syncthreads();
-    float bm[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      bm[h] = red[0][h];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) bm[h] = fmaxf(bm[h], red[w][h]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ps = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KEEP; ++kk)
-        if (h0 + kk == h && canon && bm[h] != -INFINITY) ps += exp2f(lg[kk] - bm[h]);
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) ps += __shfl_xor(ps, off, kWave);
-      if (lane == 0) red[wave][h] = ps;
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const int h = threadIdx.x;
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) tot += red[w][h];
-      store_agent_f32x2(mlr, (uint32_t)((((int64_t)row * a.items_max + pos) * G + h) * 8),
-                        f32x2{bm[h], tot});
-    }
-    __syncthreads();
-  }
-
-  if (!last_arrival(a.counters + row, gridDim.x, &s_flag)) return;
-
-  // stop position: c_h = row max logit; T_h = tail mass; A_h(n) = T_h + sum
-  // of the first n block masses; n* = first n with M_h(n) < tau*A_h(n) for
-  // every head, else nsel
-  auto ml_at = [&](int item, int h) {
-    return load_agent_f32x2(mlr, (uint32_t)((((int64_t)row * a.items_max + item) * G + h) * 8));
-  };
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float c = -INFINITY;
-    for (int i = 0; i < n_items; ++i) c = fmaxf(c, ml_at(i, h).x);
-    sc[h] = c;
-    float tmass = 0.f;
-    if (tail > 0) {
-      const f32x2 v = ml_at(nsel, h);
-      tmass = v.x == -INFINITY ? 0.f : v.y * exp2f(v.x - c);
-    }
-    sT[h] = tmass;
-    carry[h] = 0.f;
-  }
-  if (threadIdx.x == 0) s_stop = nsel;
   __syncthreads();
-  for (int base = 0; base < nsel; base += kThreads) {
-    const int n = base + threadIdx.x + 1;  // 1-based list position
-    bool cond = n <= nsel;
+
+  const T* kp = static_cast<const T*>(a.k_pool);
+  const T* vp = static_cast<const T*>(a.v_pool);
+  auto item = [&](int it) {  // position it of [tail block, listed blocks...]
+    int64_t idx;
+    const int li = tail > 0 ? it - 1 : it;
+    return item_at(a, row, b, g, li < 0 ? nsel : li, nsel, nb, tail, D, &idx);
+  };
+  AttnState<T, D, G> att;
+  att.init();
+  float Lw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) Lw[h] = 0.f;
+  // one block: attend it, then (a listed block) decide; true: stop after it
+  auto step = [&](const Slab<T, D>& s, int it) -> bool {
+    float mb[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) mb[h] = att.m[h];
+    att.consume(s, sm.att, a.qscale);
+    // the wave's mass of this block per head (its 16 token rows, frame m_w)
+    float mass[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mass = 0.f;
-      if (n <= nsel) {
-        const f32x2 v = ml_at(n - 1, h);
-        mass = v.x == -INFINITY ? 0.f : v.y * exp2f(v.x - sc[h]);
-      }
-      float tot;
-      const float incl = block_inclusive_scan_f(mass, scan_sm, &tot);
-      const float A = sT[h] + carry[h] + incl;
-      cond = cond && (mass < a.tau * A);
-      __syncthreads();
-      if (threadIdx.x == 0) carry[h] += tot;
+      float v = lane < kSub ? sm.att.p_lds[wave][lane][h] : 0.f;
+      v += dpp_mov<0x121>(v);  // row_ror:1
+      v += dpp_mov<0x122>(v);  // row_ror:2
+      v += dpp_mov<0x124>(v);  // row_ror:4
+      v += dpp_mov<0x128>(v);  // row_ror:8
+      mass[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+      Lw[h] = (mb[h] == -INFINITY ? 0.f : Lw[h] * exp2f(mb[h] - att.m[h])) + mass[h];
     }
-    if (cond) atomicMin(&s_stop, n);
+    if (tail > 0 && it == 0) return false;  // the tail block seeds the accumulated mass
+    const int par = it & 1;
+    if (lane < G) {
+      float mh = 0.f, lh = 0.f, sh = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        mh = hh == lane ? att.m[hh] : mh;
+        lh = hh == lane ? Lw[hh] : lh;
+        sh = hh == lane ? mass[hh] : sh;
+      }
+      sm.x[par][wave][lane][0] = mh;
+      sm.x[par][wave][lane][1] = lh;
+      sm.x[par][wave][lane][2] = sh;
+    }
     __syncthreads();
-    if (s_stop < nsel) break;  // uniform: read after the barrier
+    bool stop = true;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float F = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) F = fmaxf(F, sm.x[par][w][h][0]);
+      float A = 0.f, M = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.x[par][w][h][0];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - F);
+        A = fmaf(sm.x[par][w][h][1], f, A);
+        M = fmaf(sm.x[par][w][h][2], f, M);
+      }
+      stop = stop && (M < a.tau * A);
+    }
+    return stop;
+  };
+  Slab<T, D> sa, sb;
+  if (n_items > 0) slab_issue<T, D, false>(sa, item(0), kp, vp);
+  if (n_items > 1) slab_issue<T, D, false>(sb, item(1), kp, vp);
+  int processed = nsel;  // listed blocks attended
+  for (int it = 0; it < n_items; it += 2) {
+    if (step(sa, it)) {
+      processed = tail > 0 ? it : it + 1;
+      break;
+    }
+    if (it + 2 < n_items) slab_issue<T, D, false>(sa, item(it + 2), kp, vp);
+    if (it + 1 < n_items) {
+      if (step(sb, it + 1)) {
+        processed = tail > 0 ? it + 1 : it + 2;
+        break;
+      }
+      if (it + 3 < n_items) slab_issue<T, D, false>(sb, item(it + 3), kp, vp);
+    }
   }
-  if (threadIdx.x == 0) a.num_processed[row] = s_stop;
+  att.to_lds(sm.att);
+  // the waves' states merged and normalised into the output
+  T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hkv + g) * G * D;
+  for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
+    const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.att.wm[w][h]);
+    float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.att.wm[w][h];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] = fmaf(sm.att.wacc[w][h][c + e], f, num[e]);
+      den = fmaf(sm.att.wl[w][h], f, den);
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[h * D + c + e] = from_f32<T>(num[e] * inv);
+  }
+  if (threadIdx.x == 0) a.num_processed[row] = processed;
 }
 
 template <typename T, int D, int G>
@@ -289,33 +256,27 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   a.counters = reinterpret_cast<uint32_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + lay.off_ml);
   a.part_acc = reinterpret_cast<float*>(ws + lay.off_acc);
-  a.es_logits = reinterpret_cast<float*>(ws + lay.off_es_logits);
-  a.es_ml = reinterpret_cast<float*>(ws + lay.off_es_ml);
   a.Hkv = L.Hkv;
   a.max_blocks = L.max_blocks;
   a.max_selected = L.max_selected;
   a.items_max = lay.items_max;
   a.qscale = L.scale * 1.4426950408889634f;  // natural -> base-2 logits
   a.tau = L.tau;
+  if (L.early_stop) {
+    es_walk_kernel<T, D, G><<<lay.rows, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   int bpw = lay.bpw;
   if (bpw <= 0) {
-    const void* fn = L.early_stop ? reinterpret_cast<const void*>(decode_kernel<T, D, G, true>)
-                                  : reinterpret_cast<const void*>(decode_kernel<T, D, G, false>);
     GridInfo gi;
-    const hipError_t e = grid_info(fn, kThreads, 0, &gi);
+    const hipError_t e =
+        grid_info(reinterpret_cast<const void*>(decode_kernel<T, D, G>), kThreads, 0, &gi);
     if (e != hipSuccess) return e;
     bpw = balanced_blocks_per_split(lay.rows, lay.items_max, gi.per_cu * gi.cus);
   }
   a.bpw = bpw;
   dim3 grid((lay.items_max + bpw - 1) / bpw, lay.rows);
-  if (L.early_stop) {
-    es_mass_kernel<T, D, G><<<grid, kThreads, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    decode_kernel<T, D, G, true><<<grid, kThreads, 0, stream>>>(a);
-  } else {
-    decode_kernel<T, D, G, false><<<grid, kThreads, 0, stream>>>(a);
-  }
+  decode_kernel<T, D, G><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

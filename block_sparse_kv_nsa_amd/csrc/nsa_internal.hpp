@@ -80,12 +80,12 @@ struct SelectLaunch {
 hipError_t launch_select(const SelectLaunch& L, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// decode: [counters | split partial (m, l) | split partial acc | early-stop
-//          logits | early-stop per-item (m, s)]
+// decode: [counters | split partial (m, l) | split partial acc]  (the
+// early-stop walk uses none of it)
 // ---------------------------------------------------------------------------
 struct DecodeLayout {
   int rows, G, D, items_max, bpw, splits;
-  size_t off_ml, off_acc, off_es_logits, off_es_ml, bytes;
+  size_t off_ml, off_acc, bytes;
 };
 
 // Items (blocks) per decode workgroup: the largest of 1/2/4/8 that still
@@ -128,14 +128,10 @@ inline DecodeLayout decode_layout(int B, int Hkv, int G, int D, int max_selected
   s.items_max = max_selected + 1;  // listed blocks + the partial tail block
   s.bpw = bpw_override > 0 ? bpw_override : 0;
   s.splits = s.bpw > 0 ? (s.items_max + s.bpw - 1) / s.bpw : 0;
-  const size_t max_splits = (size_t)s.items_max;
+  const size_t max_splits = early_stop ? 0 : (size_t)s.items_max;
   s.off_ml = round_up((size_t)4 * s.rows, 256);
   s.off_acc = round_up(s.off_ml + (size_t)s.rows * max_splits * G * 8, 256);
-  s.off_es_logits = round_up(s.off_acc + (size_t)s.rows * max_splits * G * D * 4, 256);
-  size_t es_logits = early_stop ? (size_t)s.rows * s.items_max * G * 64 * 4 : 0;
-  s.off_es_ml = round_up(s.off_es_logits + es_logits, 256);
-  size_t es_ml = early_stop ? (size_t)s.rows * s.items_max * G * 8 : 0;
-  s.bytes = round_up(s.off_es_ml + es_ml, 256);
+  s.bytes = round_up(s.off_acc + (size_t)s.rows * max_splits * G * D * 4, 256);
   return s;
 }
 
