@@ -27,6 +27,8 @@ from ._abi import (  # noqa: F401
     nsa_decode_step,
     nsa_decode_step_noalloc,
     nsa_decode_step_status,
+    nsa_debug_checks,
+    nsa_debug_error,
     nsa_decode_step_workspace_bytes,
     nsa_decode_workspace_bytes,
     nsa_last_error,

@@ -42,6 +42,8 @@ EXPORTS = (
     "nsa_decode_step_noalloc",
     "nsa_decode_step_status",
     "nsa_residency_diff",
+    "nsa_debug_checks",
+    "nsa_debug_error",
     "nsa_status_string",
     "nsa_last_error",
     "nsa_abi_version",
@@ -130,6 +132,10 @@ def load() -> ctypes.CDLL:
     lib.nsa_decode_step_status.restype = i32
     lib.nsa_residency_diff.argtypes = [P(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.nsa_residency_diff.restype = i32
+    lib.nsa_debug_checks.argtypes = []
+    lib.nsa_debug_checks.restype = i32
+    lib.nsa_debug_error.argtypes = [P(ctypes.c_uint32), i32]
+    lib.nsa_debug_error.restype = i32
     lib.nsa_status_string.argtypes = [i32]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []
@@ -276,3 +282,16 @@ def nsa_decode_step_noalloc(shape: Shape, params: SelectParams, query, q, reps, 
                                         _ptr(evict_seen), _ptr(selected), _ptr(num_selected),
                                         _ptr(out), _ptr(step_status), _stream(stream))
     _check(st, "nsa_decode_step_noalloc")
+
+
+def nsa_debug_checks() -> bool:
+    return bool(load().nsa_debug_checks())
+
+
+def nsa_debug_error(clear: bool = True) -> int:
+    """The OR of the device-side contract violations recorded since the last
+    clear (0 unless the library was built with the checks)."""
+    out = ctypes.c_uint32(0)
+    st = load().nsa_debug_error(ctypes.byref(out), int(bool(clear)))
+    _check(st, "nsa_debug_error")
+    return out.value

@@ -24,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
+LIB_CHECKS = os.path.join(PKG, "libnsa_checks.so")
 
 SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip", "nsa_step.hip",
            "nsa_residency.hip"]
@@ -37,16 +38,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libnsa)")
 
 
-def common_flags(debug: bool) -> list[str]:
+def common_flags(debug: bool, checks: bool = False) -> list[str]:
     flags = ["-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
     flags += ["-O1", "-g"] if debug else ["-O3"]
+    if checks:
+        flags += ["-DNSA_DEBUG"]
     return flags
 
 
-def compile_one(src: str, debug: bool) -> str:
+def compile_one(src: str, debug: bool, checks: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc()] + common_flags(debug)
+    obj = os.path.join(BUILD, ("checks_" if checks else "") + src + ".o")
+    cmd = [hipcc()] + common_flags(debug, checks)
     if src.endswith(".hip"):
         cmd += ["-x", "hip", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -58,27 +61,69 @@ def compile_one(src: str, debug: bool) -> str:
     return obj
 
 
-def build(debug: bool = False, verbose: bool = True) -> str:
+def build(debug: bool = False, verbose: bool = True, checks: bool = False) -> str:
+    """Compile every source for gfx950 and link the library: libnsa.so, or
+    with checks=True libnsa_checks.so (the device-side contract checks,
+    -DNSA_DEBUG)."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: compile_one(s, debug), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: compile_one(s, debug, checks), SOURCES))
+    lib_path = LIB_CHECKS if checks else LIB
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
            "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def build_asan(verbose: bool = True) -> str:
+    """A copy of the library whose host code (the C-ABI layer, nsa_api.cpp)
+    is built with AddressSanitizer by the host compiler, linked with the
+    release kernels' objects from _build/ (run build() first).  For CPU
+    tests of the argument checks; load it with libasan preloaded."""
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    api_obj = os.path.join(out_dir, "nsa_api_asan.o")
+    lib = os.path.join(out_dir, "libnsa_asan.so")
+    gxx = shutil.which("g++") or "g++"
+    cmd = [gxx, "-std=c++17", "-fPIC", "-g", "-O1", "-fno-omit-frame-pointer",
+           "-fsanitize=address", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+           "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "nsa_api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"asan compile failed: {' '.join(cmd)}\n{r.stderr}")
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"kernel objects missing (run build() first): {missing}")
+    cmd = [gxx, "-shared", "-fsanitize=address", "-o", lib, api_obj] + objs + [
+        "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"asan link failed: {' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {lib}")
+    return lib
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--checks", action="store_true",
+                    help="also build libnsa_checks.so (device-side contract checks, -DNSA_DEBUG)")
+    ap.add_argument("--asan", action="store_true",
+                    help="also build _build/asan/libnsa_asan.so (host code under AddressSanitizer)")
     args = ap.parse_args(argv)
     build(debug=args.debug)
+    if args.checks:
+        build(debug=args.debug, checks=True)
+    if args.asan:
+        build_asan()
     return 0
 
 

@@ -172,6 +172,7 @@ nsa_status nsa_update_block_reps(const nsa_shape* shape, const void* k_pool,
   L.Hkv = shape->num_kv_heads;
   L.max_blocks = shape->max_blocks_per_seq;
   L.max_num_blocks = max_num_blocks;
+  L.P = shape->num_phys_blocks;
   if (env_trace())
     std::fprintf(stderr, "[nsa] reps grid=(%d,%d) D=%d dtype=%d\n", max_num_blocks,
                  L.B * L.Hkv, L.D, L.dtype);
@@ -315,6 +316,7 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
   L.max_blocks = shape->max_blocks_per_seq;
   L.max_selected = params->max_selected;
   L.early_stop = params->early_stop;
+  L.P = shape->num_phys_blocks;
   L.scale = scale_of(shape);
   L.tau = params->tau;
   L.lay = lay;
@@ -406,6 +408,7 @@ static nsa_status step_launch_checked(const char* fn, const nsa_shape* shape,
   L->B = shape->batch;
   L->Hkv = shape->num_kv_heads;
   L->max_blocks = shape->max_blocks_per_seq;
+  L->P = shape->num_phys_blocks;
   L->k = params->k;
   L->k_e = params->k_e;
   L->scale = scale_of(shape);
@@ -522,6 +525,30 @@ nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32
   }
   return fail(NSA_ERR_STEP_EXPIRED, "%s: a wait of the fused step expired (error word %u)%s", fn,
               word, clear ? "; workspace cleared" : "");
+}
+
+int32_t nsa_debug_checks(void) {
+#ifdef NSA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+nsa_status nsa_debug_error(uint32_t* bits, int32_t clear) {
+  const char* fn = "nsa_debug_error";
+  if (bits == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: bits is NULL", fn);
+  *bits = 0;
+  if (!nsa_debug_checks()) return ok();
+  hipError_t (*const words[])(uint32_t*, bool) = {nsa::debug_word_reps, nsa::debug_word_select,
+                                                  nsa::debug_word_decode, nsa::debug_word_step};
+  for (auto word : words) {
+    uint32_t w = 0;
+    const hipError_t e = word(&w, clear != 0);
+    if (e != hipSuccess) return fail(NSA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    *bits |= w;
+  }
+  return ok();
 }
 
 }  // extern "C"

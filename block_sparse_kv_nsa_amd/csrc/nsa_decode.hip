@@ -41,7 +41,7 @@ struct DecodeArgs {
   uint32_t* counters;
   float* part_ml;        // [rows][splits][G][2]
   float* part_acc;       // [rows][splits][G][D]
-  int Hkv, max_blocks, max_selected, items_max, bpw;
+  int Hkv, max_blocks, max_selected, items_max, bpw, P;
   float qscale, tau;
 };
 
@@ -49,8 +49,10 @@ struct DecodeArgs {
 __device__ __forceinline__ Item item_at(const DecodeArgs& a, int row, int b, int g, int it,
                                         int nsel, int nb, int tail, int D, int64_t* idx_out) {
   const bool is_tail = it >= nsel;
-  const int blk = is_tail ? nb : a.selected[(int64_t)row * a.max_selected + it];
-  const int64_t phys = a.table[(int64_t)b * a.max_blocks + blk];
+  const int blk = is_tail ? nb
+                          : dbg_clamp(a.selected[(int64_t)row * a.max_selected + it], 0, nb,
+                                      kDbgSelected);
+  const int64_t phys = dbg_clamp(a.table[(int64_t)b * a.max_blocks + blk], 0, a.P, kDbgTable);
   Item x;
   x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
   x.valid = is_tail ? tail : kBlock;
@@ -66,7 +68,7 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
-  const int L = a.seq_lens[b];
+  const int L = dbg_clamp(a.seq_lens[b], 0, kBlock * a.max_blocks + 1, kDbgSeqLen);
   const int nb = L / kBlock;
   const int tail = L - nb * kBlock;
   const int nsel = min(a.num_selected[row], a.max_selected);
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int b = row / a.Hkv, g = row % a.Hkv;
-  const int L = a.seq_lens[b];
+  const int L = dbg_clamp(a.seq_lens[b], 0, kBlock * a.max_blocks + 1, kDbgSeqLen);
   const int nb = L / kBlock;
   const int tail = L - nb * kBlock;
   const int nsel = min(a.num_selected[row], a.max_selected);
@@ -258,6 +260,7 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   a.part_acc = reinterpret_cast<float*>(ws + lay.off_acc);
   a.Hkv = L.Hkv;
   a.max_blocks = L.max_blocks;
+  a.P = L.P;
   a.max_selected = L.max_selected;
   a.items_max = lay.items_max;
   a.qscale = L.scale * 1.4426950408889634f;  // natural -> base-2 logits
@@ -296,5 +299,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   if (L.dtype == 1) return L.D == 128 ? by_group<bf16, 128>(L, stream) : by_group<bf16, 64>(L, stream);
   return L.D == 128 ? by_group<float, 128>(L, stream) : by_group<float, 64>(L, stream);
 }
+
+hipError_t debug_word_decode(uint32_t* out, bool clear) { return debug_word_access(out, clear); }
 
 }  // namespace nsa

@@ -15,6 +15,58 @@ constexpr int kWave = 64;         // CDNA wavefront
 constexpr int kThreads = 256;     // every kernel runs 4 waves per workgroup
 constexpr int kWaves = kThreads / kWave;
 
+// ---------------------------------------------------------------------------
+// device-side contract checks (builds with -DNSA_DEBUG)
+// ---------------------------------------------------------------------------
+// Block-table entries, listed block ids, eviction-set ids and sequence
+// lengths are the caller's contract.  Debug builds check them where a kernel
+// reads them: a violation sets a bit in the kernel source's error word and
+// the value is clamped into range, so that no access leaves the caller's
+// buffers.  Release builds compile the checks out.
+enum : uint32_t {
+  kDbgTable = 1u,     // block-table entry outside [0, num_phys_blocks)
+  kDbgSelected = 2u,  // listed block id outside [0, the row's full blocks)
+  kDbgEvict = 4u,     // eviction-set id outside [0, the row's full blocks)
+  kDbgSeqLen = 8u,    // seq_lens above 64 * max_blocks_per_seq
+};
+#ifdef NSA_DEBUG
+namespace {
+__device__ uint32_t debug_word;  // one per kernel source
+}
+#endif
+
+__device__ __forceinline__ int dbg_clamp(int v, int lo, int hi_excl, uint32_t code) {
+#ifdef NSA_DEBUG
+  if (v < lo || v >= hi_excl) {
+    __hip_atomic_fetch_or(&debug_word, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = v < lo || hi_excl <= lo ? lo : hi_excl - 1;
+  }
+#else
+  (void)lo;
+  (void)hi_excl;
+  (void)code;
+#endif
+  return v;
+}
+
+// The error word of the calling kernel source (debug builds; 0 otherwise),
+// cleared when `clear`.
+inline hipError_t debug_word_access(uint32_t* out, bool clear) {
+#ifdef NSA_DEBUG
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(debug_word), sizeof(uint32_t));
+  if (e == hipSuccess && clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_word), &zero, sizeof(uint32_t));
+  }
+  return e;
+#else
+  (void)clear;
+  *out = 0;
+  return hipSuccess;
+#endif
+}
+
 // bf16 travels as its 16-bit pattern.
 struct bf16 {
   uint16_t bits;

@@ -27,7 +27,7 @@ struct RepsLaunch {
   const int32_t* num_blocks;
   void* reps;
   float* E;
-  int B, Hkv, max_blocks, max_num_blocks;
+  int B, Hkv, max_blocks, max_num_blocks, P;
 };
 hipError_t launch_reps(const RepsLaunch& L, hipStream_t stream);
 
@@ -147,7 +147,7 @@ struct DecodeLaunch {
   int32_t* num_processed;
   void* out;
   void* workspace;
-  int B, Hkv, max_blocks, max_selected, early_stop;
+  int B, Hkv, max_blocks, max_selected, early_stop, P;
   float scale, tau;
   DecodeLayout lay;
 };
@@ -272,7 +272,7 @@ struct StepLaunch {
   int32_t* num_selected;
   void* out;
   void* workspace;
-  int B, Hkv, max_blocks, k, k_e;
+  int B, Hkv, max_blocks, k, k_e, P;
   float scale;
   int gang_override;  // 0: from capacity
   int att_override;   // 0: half of the row's workgroups
@@ -304,5 +304,12 @@ struct ResidencyLaunch {
   int rows, Hkv, max_blocks, max_selected;
 };
 hipError_t launch_residency(const ResidencyLaunch& L, hipStream_t stream);
+
+// The error words of the device-side contract checks, one per kernel source
+// (builds with -DNSA_DEBUG; 0 otherwise); each waits for the device.
+hipError_t debug_word_reps(uint32_t* out, bool clear);
+hipError_t debug_word_select(uint32_t* out, bool clear);
+hipError_t debug_word_decode(uint32_t* out, bool clear);
+hipError_t debug_word_step(uint32_t* out, bool clear);
 
 }  // namespace nsa

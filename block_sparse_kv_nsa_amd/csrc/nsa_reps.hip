@@ -23,13 +23,13 @@ __global__ __launch_bounds__(kThreads) void reps_kernel(const T* __restrict__ k_
                                                         const int32_t* __restrict__ first_block,
                                                         const int32_t* __restrict__ num_blocks,
                                                         T* __restrict__ reps, float* __restrict__ E,
-                                                        int Hkv, int max_blocks) {
+                                                        int Hkv, int max_blocks, int P) {
   const int row = blockIdx.y;
   const int b = row / Hkv, g = row % Hkv;
   const int i = blockIdx.x;
   if (i >= num_blocks[b]) return;
-  const int blk = first_block[b] + i;
-  const int64_t phys = table[(int64_t)b * max_blocks + blk];
+  const int blk = dbg_clamp(first_block[b] + i, 0, max_blocks, kDbgSelected);
+  const int64_t phys = dbg_clamp(table[(int64_t)b * max_blocks + blk], 0, P, kDbgTable);
   const T* slab = k_pool + (phys * Hkv + g) * (int64_t)(kBlock * D);
   T* out = reps + (((int64_t)row * max_blocks + blk) * kSubs) * D;
 
@@ -66,7 +66,7 @@ hipError_t launch_t(const RepsLaunch& L, hipStream_t stream) {
   dim3 grid(L.max_num_blocks, L.B * L.Hkv);
   reps_kernel<T, D><<<grid, kThreads, 0, stream>>>(
       static_cast<const T*>(L.k_pool), L.table, L.logits, L.first_block, L.num_blocks,
-      static_cast<T*>(L.reps), L.E, L.Hkv, L.max_blocks);
+      static_cast<T*>(L.reps), L.E, L.Hkv, L.max_blocks, L.P);
   return hipGetLastError();
 }
 
@@ -76,5 +76,7 @@ hipError_t launch_reps(const RepsLaunch& L, hipStream_t stream) {
   if (L.dtype == 1) return L.D == 128 ? launch_t<bf16, 128>(L, stream) : launch_t<bf16, 64>(L, stream);
   return L.D == 128 ? launch_t<float, 128>(L, stream) : launch_t<float, 64>(L, stream);
 }
+
+hipError_t debug_word_reps(uint32_t* out, bool clear) { return debug_word_access(out, clear); }
 
 }  // namespace nsa

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
     if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
     const int nprev = min(a.k_e, seen);
     for (int i = threadIdx.x; i < nprev; i += kThreads)
-      ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), nb - 1);
+      ev_old[i] = dbg_clamp(a.evict_set[(int64_t)row * a.k_e + i], 0, nb, kDbgEvict);
     __syncthreads();
     const int ncand = nprev + nb - seen;
     const int n_e = min(a.k_e, ncand);
@@ -402,5 +402,7 @@ hipError_t launch_select(const SelectLaunch& L, hipStream_t stream) {
   if (L.dtype == 1) return L.D == 128 ? by_group<bf16, 128>(L, stream) : by_group<bf16, 64>(L, stream);
   return L.D == 128 ? by_group<float, 128>(L, stream) : by_group<float, 64>(L, stream);
 }
+
+hipError_t debug_word_select(uint32_t* out, bool clear) { return debug_word_access(out, clear); }
 
 }  // namespace nsa

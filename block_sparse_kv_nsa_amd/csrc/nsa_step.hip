@@ -68,7 +68,7 @@ struct GangArgs {
   uint32_t* keys;    // [rows][nb_max] block key + 1 (1: not a candidate)
   float* part_ml;    // [rows][kMaxGang][G] (m, l)
   float* part_acc;   // [rows][kMaxGang][G][D]
-  int rows, Hkv, max_blocks, nb_max, k, k_e;
+  int rows, Hkv, max_blocks, nb_max, k, k_e, P;
   int CS, CA, gangs, per_wg;  // scorers and attenders per row, rows at once, reps per scorer
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
@@ -201,7 +201,7 @@ struct Gang {
     Row R;
     R.b = row / a.Hkv;
     R.g = row % a.Hkv;
-    R.L = sload(a.seq_lens, R.b);
+    R.L = dbg_clamp(sload(a.seq_lens, R.b), 0, kBlock * a.max_blocks + 1, kDbgSeqLen);
     R.nb = min(R.L / kBlock, a.nb_max);
     // the partial block (none when the row's table is full: a longer L is
     // outside the call's contract and attends nothing past the table)
@@ -228,7 +228,7 @@ struct Gang {
     int* ev_old = reinterpret_cast<int*>(ekeys + a.k_e + a.nb_max);  // k_e
     const int ncand = R.nprev + R.nb - R.seen;
     for (int i = threadIdx.x; i < R.nprev; i += kThreads)
-      ev_old[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), R.nb - 1);
+      ev_old[i] = dbg_clamp(a.evict_set[(int64_t)row * a.k_e + i], 0, R.nb, kDbgEvict);
     __syncthreads();
     const float* Er = a.E + (int64_t)row * a.max_blocks;
     for (int i = threadIdx.x; i < ncand; i += kThreads) {
@@ -250,7 +250,8 @@ struct Gang {
     int blk = R.nb;  // the tail block
     if (idx < R.n_e) blk = min(max(__builtin_amdgcn_readfirstlane(eids[idx]), 0), R.nb - 1);
     Item x;
-    x.base = ((int64_t)sload(a.table, R.tb + blk) * a.Hkv + R.g) * (int64_t)(kBlock * D);
+    x.base = ((int64_t)dbg_clamp(sload(a.table, R.tb + blk), 0, a.P, kDbgTable) * a.Hkv + R.g) *
+             (int64_t)(kBlock * D);
     x.valid = idx < R.n_e ? kBlock : R.tail;
     x.logits = nullptr;
     return x;
@@ -408,12 +409,12 @@ struct Gang {
       {
         // the eviction set and the table row to shared memory while the
         // first loads are in flight
-        if (R.steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = min(max(ev_pre, 0), nb - 1);
+        if (R.steady && (int)threadIdx.x < n_e) eids[threadIdx.x] = dbg_clamp(ev_pre, 0, nb, kDbgEvict);
         if (tbl_lds) {
 #pragma unroll
           for (int j = 0; j < kTblLds / kThreads; ++j) {
             const int i = threadIdx.x + kThreads * j;
-            if (i < nb) tbl[i] = (int)tv[j];
+            if (i < nb) tbl[i] = dbg_clamp((int)tv[j], 0, a.P, kDbgTable);
           }
         }
       }
@@ -702,7 +703,7 @@ struct Gang {
     } else {
       if (R.steady) {
         for (int i = threadIdx.x; i < R.n_e; i += kThreads)
-          eids[i] = min(max(a.evict_set[(int64_t)row * a.k_e + i], 0), R.nb - 1);
+          eids[i] = dbg_clamp(a.evict_set[(int64_t)row * a.k_e + i], 0, R.nb, kDbgEvict);
         __syncthreads();
       }
       // the physical blocks of this attender's first items (positions c,
@@ -712,7 +713,7 @@ struct Gang {
         const int idx = c + t * a.CA;
         if (idx < n_items) {
           const int blk = idx < R.n_e ? eids[idx] : R.nb;
-          sm.ephys[t] = a.table[R.tb + blk];
+          sm.ephys[t] = dbg_clamp(a.table[R.tb + blk], 0, a.P, kDbgTable);
         }
       }
       // the attender's loads wait until its partner scorer (c mod CS) has
@@ -749,7 +750,8 @@ struct Gang {
       }
       const int blk = min(max(__builtin_amdgcn_readfirstlane(qsel[c + it * stride]), 0), R.nb - 1);
       Item x;
-      const int64_t phys = tbl_lds ? tbl[blk] : sload(a.table, R.tb + blk);
+      const int64_t phys =
+          tbl_lds ? tbl[blk] : dbg_clamp(sload(a.table, R.tb + blk), 0, a.P, kDbgTable);
       x.base = (phys * a.Hkv + R.g) * (int64_t)(kBlock * D);
       x.valid = kBlock;
       x.logits = nullptr;
@@ -822,6 +824,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   a.rows = lay.rows;
   a.Hkv = L.Hkv;
   a.max_blocks = L.max_blocks;
+  a.P = L.P;
   a.nb_max = lay.nb_max;
   a.k = L.k;
   a.k_e = L.k_e;
@@ -904,6 +907,8 @@ hipError_t scratch_address(void** out) {
 }  // namespace
 
 hipError_t launch_step(const StepLaunch& L, hipStream_t stream) { return dispatch(L, stream, nullptr); }
+
+hipError_t debug_word_step(uint32_t* out, bool clear) { return debug_word_access(out, clear); }
 
 hipError_t launch_step_noalloc(const StepLaunch& L, int32_t* status, hipStream_t stream) {
   void* ws = nullptr;

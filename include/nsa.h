@@ -331,6 +331,26 @@ nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,
 nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32_t clear,
                                   hipStream_t stream);
 
+/* --------------------------------------------------------------------------
+ * Device-side contract checks.  Libraries built with -DNSA_DEBUG (build.py
+ * --checks) check, where the kernels read them, the values that are the
+ * caller's contract: block-table entries in [0, num_phys_blocks) (bit 1),
+ * listed block ids below the row's full blocks (bit 2), eviction-set ids
+ * below the row's full blocks (bit 4), seq_lens at most
+ * 64 * max_blocks_per_seq (bit 8).  A violation sets its bit and the value
+ * is clamped into range, so that no access leaves the caller's buffers (the
+ * results of that call are then meaningless).  Release builds compile the
+ * checks out.
+ * ------------------------------------------------------------------------ */
+/* 1 when the library was built with the checks, 0 otherwise. */
+int32_t nsa_debug_checks(void);
+
+/* Waits for the device, then returns in *bits (host) the OR of the bits set
+ * since the last clear (0 in release builds); clears them when clear != 0.
+ * NSA_ERR_INVALID_ARGUMENT for a NULL `bits`, NSA_ERR_HIP when a HIP call
+ * fails. */
+nsa_status nsa_debug_error(uint32_t* bits, int32_t clear);
+
 /* Text for a status code (static storage). */
 const char* nsa_status_string(nsa_status status);
 

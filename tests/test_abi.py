@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
@@ -187,3 +187,13 @@ def test_step_noalloc_validation():
     ordered = list(args)
     ordered[1] = N.SelectParams(0, 64, 0, 1)
     expect(N.NSA_ERR_UNSUPPORTED, N.nsa_decode_step_noalloc, *ordered)
+
+
+def test_debug_checks_queries():
+    """Release builds report no checks and an empty error word, without any
+    device call; a NULL output is rejected."""
+    lib = N.load()
+    if N.nsa_debug_checks():
+        pytest.skip("a build with the device checks")
+    assert N.nsa_debug_error() == 0
+    assert lib.nsa_debug_error(None, 0) == N.NSA_ERR_INVALID_ARGUMENT
