@@ -22,9 +22,11 @@ from ._abi import (  # noqa: F401
     NsaError,
     SelectParams,
     Shape,
+    StepGrid,
     load,
     nsa_abi_version,
     nsa_decode_step,
+    nsa_decode_step_grid,
     nsa_decode_step_noalloc,
     nsa_decode_step_status,
     nsa_debug_checks,

@@ -41,6 +41,7 @@ EXPORTS = (
     "nsa_decode_step",
     "nsa_decode_step_noalloc",
     "nsa_decode_step_status",
+    "nsa_decode_step_grid",
     "nsa_residency_diff",
     "nsa_debug_checks",
     "nsa_debug_error",
@@ -83,6 +84,16 @@ class SelectParams(ctypes.Structure):
         ("k", ctypes.c_int32),
         ("k_e", ctypes.c_int32),
         ("ordered", ctypes.c_int32),
+    ]
+
+
+class StepGrid(ctypes.Structure):
+    _fields_ = [
+        ("workgroups", ctypes.c_int32),
+        ("scorers_per_row", ctypes.c_int32),
+        ("attenders_per_row", ctypes.c_int32),
+        ("rows_at_once", ctypes.c_int32),
+        ("reps_per_scorer", ctypes.c_int32),
     ]
 
 
@@ -132,6 +143,8 @@ def load() -> ctypes.CDLL:
     lib.nsa_decode_step_status.restype = i32
     lib.nsa_residency_diff.argtypes = [P(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.nsa_residency_diff.restype = i32
+    lib.nsa_decode_step_grid.argtypes = [P(Shape), P(SelectParams), i32, i32, P(StepGrid)]
+    lib.nsa_decode_step_grid.restype = i32
     lib.nsa_debug_checks.argtypes = []
     lib.nsa_debug_checks.restype = i32
     lib.nsa_debug_error.argtypes = [P(ctypes.c_uint32), i32]
@@ -295,3 +308,12 @@ def nsa_debug_error(clear: bool = True) -> int:
     st = load().nsa_debug_error(ctypes.byref(out), int(bool(clear)))
     _check(st, "nsa_debug_error")
     return out.value
+
+
+def nsa_decode_step_grid(shape: Shape, params: SelectParams, max_seq_len: int,
+                         capacity: int) -> StepGrid:
+    out = StepGrid()
+    st = load().nsa_decode_step_grid(ctypes.byref(shape), ctypes.byref(params), int(max_seq_len),
+                                     int(capacity), ctypes.byref(out))
+    _check(st, "nsa_decode_step_grid")
+    return out

@@ -360,6 +360,27 @@ nsa_status nsa_decode_step_workspace_bytes(const nsa_shape* shape, const nsa_sel
   return ok();
 }
 
+nsa_status nsa_decode_step_grid(const nsa_shape* shape, const nsa_select_params* params,
+                                int32_t max_seq_len, int32_t capacity, nsa_step_grid* grid) {
+  const char* fn = "nsa_decode_step_grid";
+  if (grid == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: grid is NULL", fn);
+  if (capacity < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: capacity must be >= 1", fn);
+  nsa::StepLayout lay;
+  if (nsa_status st = step_layout_checked(fn, shape, params, max_seq_len, &lay)) return st;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int cap = nsa::gang_reps_cap(shape->dtype == NSA_F32 ? 4 : 2, shape->head_dim, G);
+  nsa::GangPlan plan;
+  if (!nsa::gang_plan(lay, params->k, params->k_e, capacity, cap, env_int("NSA_STEP_GANG"),
+                      env_int("NSA_STEP_ATTENDERS"), &plan))
+    return fail(NSA_ERR_UNSUPPORTED, "%s: no gang fits %d resident workgroups", fn, capacity);
+  grid->workgroups = plan.gangs * (plan.CS + plan.CA);
+  grid->scorers_per_row = plan.CS;
+  grid->attenders_per_row = plan.CA;
+  grid->rows_at_once = plan.gangs;
+  grid->reps_per_scorer = plan.per_wg;
+  return ok();
+}
+
 // The checks and the launch description shared by nsa_decode_step and
 // nsa_decode_step_noalloc (workspace == NULL: the library's own).
 static nsa_status step_launch_checked(const char* fn, const nsa_shape* shape,

@@ -320,6 +320,28 @@ nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,
                               int32_t* release, int32_t* num_release, float* gamma,
                               hipStream_t stream);
 
+/* Launch geometry of nsa_decode_step on a device that holds `capacity`
+ * workgroups of the step kernel at once (resident workgroups per compute
+ * unit times compute units).  Each row is handled by a gang of scorers
+ * (representatives, hand-offs, selection, query-aware attention) and
+ * attenders (attention over the eviction set and the tail block, waiting on
+ * nobody but their partner scorer's statistics); the grid holds the
+ * scorers of `rows_at_once` gangs first, then their attenders, and rows
+ * beyond rows_at_once are taken in turn.  A scorer waits for the other
+ * scorers of its gang, so the scorers of the grid must be resident
+ * together: the call expects the device to itself while it runs.
+ * NSA_ERR_UNSUPPORTED when no gang fits `capacity`. */
+typedef struct nsa_step_grid {
+  int32_t workgroups;         /* grid size */
+  int32_t scorers_per_row;    /* CS */
+  int32_t attenders_per_row;  /* CA (0: the scorers take the eviction set too) */
+  int32_t rows_at_once;       /* gangs in the grid */
+  int32_t reps_per_scorer;    /* sub-block representatives a scorer streams */
+} nsa_step_grid;
+
+nsa_status nsa_decode_step_grid(const nsa_shape* shape, const nsa_select_params* params,
+                                int32_t max_seq_len, int32_t capacity, nsa_step_grid* grid);
+
 /* Status of the fused steps run on `workspace` since it was last cleared.
  * Waits for the work queued on `stream` (a host synchronisation: call it
  * where a step's results are consumed, not between steps), then reads the
