@@ -459,13 +459,22 @@ def traffic_mode(args) -> int:
         return sum(vals) / len(vals)
 
     f_cal, w_cal = pick(fetch, CALIBRATION_SYMBOL) * 1024, pick(write, CALIBRATION_SYMBOL) * 1024
-    kernel = "step" if args.path == "fused" else "select"
-    kernels = [kernel] if args.path == "fused" else ["select", "decode"]
+    import workloads as W
+    cfg = W.config(WORKLOADS[args.workload])
+    workload = cfg.name + ("-dense" if args.dense else "")
+    if args.dense:
+        kernels = ["decode"]
+    elif args.path == "fused" and not cfg.ordered:
+        kernels = ["step"]
+    else:
+        kernels = ["select", "decode"]
     for kern in kernels:
         sym = KERNEL_SYMBOLS[kern]
+        if kern == "decode" and cfg.ordered and not args.dense:
+            sym = "es_walk_kernel"
         f_k, w_k = pick(fetch, sym) * 1024, pick(write, sym) * 1024
         rec = {
-            "kernel": kern, "symbol": sym, "workload": args.workload,
+            "kernel": kern, "symbol": sym, "workload": workload,
             "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
             "calibration": {"kernel": CALIBRATION_SYMBOL, "bytes_each_way": known,
                             "fetch_bytes_raw": f_cal, "write_bytes_raw": w_cal,
@@ -474,7 +483,7 @@ def traffic_mode(args) -> int:
             "source_hash": source_hash(KERNEL_SOURCES[kern]),
             "files": list(args.traffic_from),
         }
-        path = os.path.join(ROOT, "profiles", f"{kern}_{args.workload}_traffic.json")
+        path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_traffic.json")
         with open(path, "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec))
