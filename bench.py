@@ -77,13 +77,38 @@ def parse():
     return ap.parse_args()
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments and blank lines: what the compiler
+    sees, so that a comment edit does not count as a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def source_hash(rel: str) -> str:
     h = hashlib.sha256()
     for part in (rel, "block_sparse_kv_nsa_amd/csrc/nsa_device.hpp",
                  "block_sparse_kv_nsa_amd/csrc/nsa_internal.hpp",
                  "block_sparse_kv_nsa_amd/csrc/nsa_attend.hpp"):
-        with open(os.path.join(ROOT, part), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, part), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,38 +5,38 @@
 // nsa_sparse_decode (NOSA technical summary, "Mecanismo de Doble Selección",
 // "Implementación Basada en Bloques"; SparDA technical summary, "Kompakter
 // Forecast-Indexer"); only the schedule differs.  Each row (sequence b, KV
-// head g) is handled by a gang of C workgroups that run at the same time: the
-// grid never exceeds the workgroups the device holds resident at once, so on
-// a device not shared with other streams every workgroup starts with the
-// launch.  (A cooperative launch would guarantee this but costs about 17 us
-// per launch on this part.)  Member c of the gang
+// head g) is handled by a gang of CS scorers and CA attenders that run at the
+// same time: the grid never exceeds the workgroups the device holds resident
+// at once, so on a device not shared with other streams every workgroup
+// starts with the launch.  (A cooperative launch would guarantee this but
+// costs about 17 us per launch on this part.)  Scorer c of a gang
 //   1. streams its contiguous share of the row's sub-block representatives
-//      and keeps the logits q.r in registers; the eviction set depends on the
-//      eviction scores only, never on the query, so the loads of the member's
-//      first two eviction-set (or tail) slabs go out during the stream;
-//   2. publishes its softmax statistics (group-softmax mode) and attends
-//      those two slabs while the other members finish streaming;
-//   3. forms the row normaliser from every member's statistics, scores its
-//      own blocks and publishes their keys, then attends the rest of its
-//      eviction-set share while the other members publish theirs;
-//   4. selects the row's query-aware blocks from all the keys of the row (a
-//      radix select: every member reaches the same set) and attends its share
-//      of them;
-//   5. publishes its partial; member 0 merges the C partials into the output,
-//      writes the selected list and the eviction state, and clears the row's
-//      hand-off slots.
-// One online-softmax state per wave runs through steps 2-4, so the member's
-// attention is merged across its waves once.
+//      and keeps the logits q.r in shared memory;
+//   2. publishes its softmax statistics (group-softmax mode);
+//   3. forms the row normaliser from every scorer's statistics, scores its
+//      own blocks and publishes their keys;
+//   4. selects the row's query-aware blocks from all the keys of the row
+//      (every scorer reaches the same set) and attends its share of them;
+//   5. publishes its partial.
+// Attender c attends its share of the eviction set and the tail block: the
+// eviction set depends on the eviction scores only, never on the query, so
+// it needs no hand-off.  Its loads start once its partner scorer (c mod CS)
+// has published its statistics, so that the representatives, which every
+// hand-off waits for, have the memory to themselves until then.  Scorer 0
+// merges every member's partial into the output, writes the selected list and
+// the eviction state, and clears the row's hand-off slots.
+// One online-softmax state per wave runs through all of a member's items, so
+// the member's attention is merged across its waves once.
 //
 // Hand-offs carry their own presence: a slot is all-zero bits until it is
 // written, and no written value is all-zero (statistics (m, s) have s >= 1
 // or m = -inf; keys are stored plus one; partial (m, l) as statistics), so a
 // reader polls the data itself: one store and one load per hand-off, no
-// counters and no fences.  Member 0 clears the slots once every partial is
+// counters and no fences.  Scorer 0 clears the slots once every partial is
 // in (every member has then read every slot of the row), so a completed call
 // leaves them as it found them.  Every wait is bounded in time: on expiry the
 // workgroup records a sticky error word, later waits of the launch return at
-// once, and the launch ends.
+// once, the eviction state is left as it was, and the launch ends.
 #include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
