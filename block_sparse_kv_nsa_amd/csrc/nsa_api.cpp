@@ -189,8 +189,13 @@ static nsa_status select_layout_checked(const char* fn, const nsa_shape* shape,
                 shape->max_blocks_per_seq * 64);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   *lay = nsa::select_layout(shape->batch, shape->num_kv_heads, G,
-                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len,
+                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len, params->k,
                             env_int("NSA_SELECT_CHUNK"));
+  // dynamic shared memory of the selection kernel (its static part is
+  // under 16 KiB of the 64 KiB a workgroup may hold)
+  const size_t lds = nsa::select_dyn_lds(*lay, params->k, params->ordered ? 0 : params->k_e);
+  if (lds > 48 * 1024)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: %zu bytes of shared memory needed (max 49152)", fn, lds);
   return NSA_OK;
 }
 

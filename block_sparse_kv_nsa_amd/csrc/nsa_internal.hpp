@@ -32,14 +32,14 @@ struct RepsLaunch {
 hipError_t launch_reps(const RepsLaunch& L, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// select: [counters | chunk stats | sub-block logits]
+// select: [counters | chunk stats | sub-block logits | block keys (rows of several chunks)]
 // ---------------------------------------------------------------------------
 struct SelectLayout {
   int rows, G, GS, nb_max, chunk_reps, chunks;
-  size_t off_stats, off_logits, bytes, logits_row;  // logits_row: floats per row
+  size_t off_stats, off_logits, off_cand, bytes, logits_row;  // logits_row: floats per row
 };
 
-inline SelectLayout select_layout(int B, int Hkv, int G, bool forecast, int max_seq_len,
+inline SelectLayout select_layout(int B, int Hkv, int G, bool forecast, int max_seq_len, int k,
                                   int chunk_override = 0) {
   SelectLayout s{};
   s.rows = B * Hkv;
@@ -48,9 +48,11 @@ inline SelectLayout select_layout(int B, int Hkv, int G, bool forecast, int max_
   s.nb_max = max_seq_len / 64;
   const int nsub = 4 * s.nb_max;
   // sub-block representatives per workgroup: a multiple of 512 (one load slot
-  // of 64 per wave, 8 in flight) sized for ~2 workgroups per compute unit
+  // of 64 per wave, 8 in flight), as large as leaves about one workgroup per
+  // compute unit (the first workgroup placed on a compute unit is served
+  // ahead of the second, so a second one would end its stream later)
   int chunk = 512;
-  while (chunk < 4096 && (size_t)s.rows * ((nsub + 2 * chunk - 1) / (2 * chunk)) >= 512) chunk <<= 1;
+  while (chunk < 4096 && (size_t)s.rows * ((nsub + 2 * chunk - 1) / (2 * chunk)) >= 256) chunk <<= 1;
   if (chunk_override >= 64) chunk = chunk_override;
   s.chunk_reps = chunk;
   s.chunks = nsub > 0 ? (nsub + chunk - 1) / chunk : 1;
@@ -58,8 +60,18 @@ inline SelectLayout select_layout(int B, int Hkv, int G, bool forecast, int max_
   const size_t stats = forecast ? 0 : (size_t)s.rows * s.chunks * G * 8;
   s.off_logits = round_up(s.off_stats + stats, 256);
   s.logits_row = (size_t)nsub * s.GS;
-  s.bytes = round_up(s.off_logits + (size_t)s.rows * s.logits_row * 4, 256);
+  s.off_cand = round_up(s.off_logits + (size_t)s.rows * s.logits_row * 4, 256);
+  const size_t cand = s.chunks > 1 ? (size_t)s.rows * s.nb_max * 4 : 0;
+  s.bytes = round_up(s.off_cand + cand, 256);
+  (void)k;
   return s;
+}
+
+// Dynamic shared memory of select_kernel: the row's block keys (also the
+// eviction update's candidate keys), the old and new eviction sets and the
+// selected list.
+inline size_t select_dyn_lds(const SelectLayout& lay, int k, int k_e) {
+  return ((size_t)lay.nb_max + 3 * (size_t)k_e + k) * 4;
 }
 
 struct SelectLaunch {

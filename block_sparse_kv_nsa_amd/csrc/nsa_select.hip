@@ -14,15 +14,17 @@
 // the early-stop traversal (S2O summary, "Regola di Arresto Anticipato"), the
 // best blocks in descending order.
 //
-// Layout of the work: a grid of (chunk, row) workgroups streams the row's
-// sub-block representatives with 16-byte coalesced loads (LPR lanes per
-// representative), writes one float per (sub-block, head) -- the logit in
-// base-2 units -- and a per-chunk (max, sum of 2^(l-max)) per head.  The last
-// workgroup to finish a row (atomic ticket) merges the chunk statistics into
-// the per-head softmax normaliser, forms the block scores in LDS and runs the
-// selection there with a 4-pass 8-bit radix select (ties to the lower block
-// id), so scoring and selection cost one launch and the row's scores never
-// make a second trip through HBM.
+// Layout of the work, two launches:
+//   1. score_kernel, a grid of (chunk, row) workgroups, streams the row's
+//      sub-block representatives with 16-byte coalesced loads (LPR lanes per
+//      representative), writes one float per (sub-block, head) -- the logit
+//      in base-2 units -- and a per-chunk (max, sum of 2^(l-max)) per head;
+//   2. select_kernel, on the same grid, merges the chunk statistics into the
+//      per-head softmax normaliser and forms the scores of its chunk's blocks
+//      from the logits; the row's last workgroup (atomic ticket) takes every
+//      block key of the row and selects.  A row of one chunk selects in
+//      place.
+// Selection is exact with ties to the lower block id.
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
 
@@ -41,19 +43,20 @@ struct SelectArgs {
   uint32_t* counters;
   float2* stats;
   float* logits;
+  uint32_t* cand;  // [rows][nb_max] block keys handed to the row's last workgroup
   int64_t logits_row;
   int Hkv, max_blocks, chunk_reps, k, k_e, ordered, nb_max;
   float qscale;
 };
 
 template <typename T, int D, int G, bool FORECAST>
-__global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kThreads) void score_kernel(SelectArgs a) {
   using Q = Quad<T, D>;
   constexpr int NLD = Q::NLD;             // 16-byte loads per lane per representative
   constexpr int GS = FORECAST ? 1 : G;    // logits per sub-block
   constexpr int KEEP = GS >= 4 ? GS / 4 : 1;  // logits a lane ends up holding per rep
   constexpr int DUP = GS >= 4 ? 1 : 4 / GS;   // lanes of a quad holding the same logit
-  constexpr int U = 8;                    // representatives per lane in flight
+  constexpr int U = NLD >= 8 ? 4 : 8;     // representatives per lane in flight
   constexpr int RPI = kThreads / 4;       // representatives per workgroup and load slot
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -71,7 +74,6 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
   const bool canon = (q % DUP) == 0;
 
   __shared__ float red_m[kWaves][4][KEEP], red_s[kWaves][4][KEEP];
-  __shared__ int s_flag;
 
   QSlice<T, D> qs[GS];
   {
@@ -91,18 +93,22 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
     s[kk] = 0.f;
   }
 
-  for (int jb = j0 + wave * 16 + r; jb - r - wave * 16 < j1; jb += RPI * U) {
-    uint4 x[U][NLD];
+  // two batches of UB slots in flight: the next batch is requested before
+  // the current one is consumed
+  constexpr int UB = U / 2;
+  auto issue = [&](uint4 (&x)[UB][NLD], int jb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UB; ++u) {
       const int j = jb + u * RPI;
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld)
         x[u][ld] = j < j1 ? load16_stream(rb + (int64_t)j * D + Q::elem(ld, q))
                           : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto consume = [&](const uint4 (&x)[UB][NLD], int jb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UB; ++u) {
       const int j = jb + u * RPI;
       float v[GS];
 #pragma unroll
@@ -112,13 +118,22 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
         float lg[KEEP];
 #pragma unroll
         for (int kk = 0; kk < KEEP; ++kk) lg[kk] = v[kk] * a.qscale;
+        // plain stores: they complete at this XCD's L2 (the launch's end
+        // writes them back for the next kernel), so the waits for the next
+        // batch of loads do not also wait for write-through acknowledgements
         const uint32_t off = (uint32_t)(j * GS + h0) * 4u;
-        if constexpr (KEEP == 1) store_agent_f32(lrs, off, lg[0]);
-        else if constexpr (KEEP == 2) store_agent_f32x2(lrs, off, f32x2{lg[0], lg[1]});
-        else {
+        if constexpr (KEEP == 1) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lg[0]), lrs, (int)off, 0, 0);
+        } else if constexpr (KEEP == 2) {
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(lg[0]), __float_as_uint(lg[1])},
+                                                lrs, (int)off, 0, 0);
+        } else {
 #pragma unroll
           for (int kk = 0; kk < KEEP; kk += 4)
-            store_agent_f32x4(lrs, off + kk * 4, f32x4{lg[kk], lg[kk + 1], lg[kk + 2], lg[kk + 3]});
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(lg[kk]), __float_as_uint(lg[kk + 1]),
+                      __float_as_uint(lg[kk + 2]), __float_as_uint(lg[kk + 3])},
+                lrs, (int)(off + kk * 4), 0, 0);
         }
         if constexpr (!FORECAST) {
 #pragma unroll
@@ -130,6 +145,16 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
         }
       }
     }
+  };
+  const int jfirst = j0 + wave * 16 + r;  // this lane's representative in the first slot
+  const int bstep = RPI * UB;             // representatives per batch
+  uint4 xa[UB][NLD], xb[UB][NLD];
+  issue(xa, jfirst);
+  for (int jb = jfirst; jb - (jfirst - j0) < j1; jb += 2 * bstep) {
+    issue(xb, jb + bstep);
+    consume(xa, jb);
+    if (jb + 2 * bstep - (jfirst - j0) < j1) issue(xa, jb + 2 * bstep);
+    consume(xb, jb + bstep);
   }
 
   if constexpr (!FORECAST) {
@@ -161,26 +186,67 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
     }
   }
 
-  if (!last_arrival(a.counters + row, gridDim.x, &s_flag)) return;
+}
 
-  // ---------------------------------------------------------------------
-  // the row's last workgroup: normalise, score blocks, select
-  // ---------------------------------------------------------------------
+template <int G, bool FORECAST>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
+  constexpr int GS = FORECAST ? 1 : G;
+  constexpr int kKpt = 8;  // keys per thread of the row selection in registers
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int row = blockIdx.y, chunk = blockIdx.x, chunks = gridDim.x;
+  const int b = row / a.Hkv;
+  const int nb = min(a.seq_lens[b] / kBlock, a.nb_max);
+  const int cbs = a.chunk_reps / kSubs;  // blocks per chunk
+  const int blk0 = min(chunk * cbs, nb);
+  const int nblk = min(blk0 + cbs, nb) - blk0;
+
   extern __shared__ uint32_t dyn[];
-  uint32_t* keys = dyn;                                            // nb_max + k_e
-  int* ev_old = reinterpret_cast<int*>(keys + a.nb_max + a.k_e);   // k_e
-  int* ev_new = ev_old + a.k_e;                                    // k_e
-  int* ord = ev_new + a.k_e;                                       // k (ordered mode)
-  uint8_t* flags = reinterpret_cast<uint8_t*>(ord + (a.ordered ? a.k : 0));  // nb_max
+  uint32_t* keys = dyn;                                         // nb_max + k_e
+  int* ev_old = reinterpret_cast<int*>(keys + a.nb_max + a.k_e);  // k_e
+  int* ev_new = ev_old + a.k_e;                                 // k_e
+  int* ord = ev_new + a.k_e;                                    // k
   __shared__ float sM[G], sInvZ[G];
+  __shared__ int s_ne, s_flag;
+  __shared__ TopSmem top;
+  __shared__ SmallTopSmem small;
+
+  // this chunk's logits for the thread's first kBatch blocks, requested
+  // before anything waits
+  const __amdgpu_buffer_rsrc_t lrs =
+      make_rsrc(a.logits + (int64_t)row * a.logits_row, (uint32_t)(a.logits_row * 4));
+  constexpr int kBatch = GS >= 8 ? 2 : 4;
+  auto load_batch = [&](f32x4 (&lgv)[kBatch][GS], int b0) {
+#pragma unroll
+    for (int bb = 0; bb < kBatch; ++bb) {
+      const int li = b0 + bb * kThreads;
+#pragma unroll
+      for (int i = 0; i < GS; ++i)
+        lgv[bb][i] = li < nblk
+                         ? load_agent_f32x4(lrs, (uint32_t)(((blk0 + li) * kSubs * GS + 4 * i) * 4))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  f32x4 lgv[kBatch][GS];
+  load_batch(lgv, threadIdx.x);
+
+  // the old eviction state, also requested before any wait
+  int seen = 0, nprev = 0;
+  if (a.k_e > 0 && !a.ordered) {
+    seen = a.evict_seen[row];
+    if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
+    nprev = min(a.k_e, seen);
+    for (int i = threadIdx.x; i < nprev; i += kThreads)
+      ev_old[i] = dbg_clamp(a.evict_set[(int64_t)row * a.k_e + i], 0, nb, kDbgEvict);
+  }
 
   if constexpr (!FORECAST) {
     // per-head softmax normaliser: every thread merges the chunk statistics
     // of head tid % G it is given (all loads in flight at once), then lanes of
     // the same head merge across the wave and the waves through LDS
     const __amdgpu_buffer_rsrc_t srs =
-        make_rsrc(a.stats, (uint32_t)((int64_t)gridDim.y * gridDim.x * G * 8));
-    const int nstat = (int)gridDim.x * G;
+        make_rsrc(a.stats, (uint32_t)((int64_t)gridDim.y * chunks * G * 8));
+    const int nstat = chunks * G;
     float M = -INFINITY, S = 0.f;
     for (int i = threadIdx.x; i < nstat; i += kThreads) {
       const f32x2 st = load_agent_f32x2(srs, (uint32_t)(((int64_t)row * nstat + i) * 8));
@@ -206,20 +272,14 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
       sInvZ[h] = Sh > 0.f ? 1.f / Sh : 0.f;
     }
   }
-  __syncthreads();
 
   // eviction set: the k_e best of (old set U newly full blocks) by E.  With
   // no newly full block the candidates are the old set itself: unchanged.
-  __shared__ int s_ne;
-  __shared__ TopSmem top;
+  // Every workgroup of the row forms it (it only reads the old state); the
+  // row's last workgroup stores it.
   if (threadIdx.x == 0) s_ne = 0;
+  __syncthreads();
   if (a.k_e > 0 && !a.ordered) {
-    int seen = a.evict_seen[row];
-    if (seen < 0 || seen > nb) seen = 0;  // a new sequence in this slot
-    const int nprev = min(a.k_e, seen);
-    for (int i = threadIdx.x; i < nprev; i += kThreads)
-      ev_old[i] = dbg_clamp(a.evict_set[(int64_t)row * a.k_e + i], 0, nb, kDbgEvict);
-    __syncthreads();
     const int ncand = nprev + nb - seen;
     const int n_e = min(a.k_e, ncand);
     if (seen == nb) {
@@ -237,31 +297,17 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
         });
     }
     if (threadIdx.x == 0) s_ne = n_e;
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.k_e; i += kThreads)
-      a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? ev_new[i] : -1;
-    if (threadIdx.x == 0) a.evict_seen[row] = nb;
   }
   __syncthreads();
   const int n_e = s_ne;
 
-  // block scores -> order keys in LDS; each thread takes kBatch blocks at a
-  // time with all their logit loads in flight before any arithmetic
-  constexpr int kBatch = GS >= 8 ? 4 : 8;
-  for (int b0 = threadIdx.x; b0 < nb; b0 += kThreads * kBatch) {
-    f32x4 lgv[kBatch][GS];
+  // scores of this chunk's blocks -> order keys in LDS
+  for (int b0 = threadIdx.x; b0 < nblk; b0 += kThreads * kBatch) {
+    if (b0 != (int)threadIdx.x) load_batch(lgv, b0);
 #pragma unroll
     for (int bb = 0; bb < kBatch; ++bb) {
-      const int blk = b0 + bb * kThreads;
-#pragma unroll
-      for (int i = 0; i < GS; ++i)
-        lgv[bb][i] = blk < nb ? load_agent_f32x4(lrs, (uint32_t)((blk * kSubs * GS + 4 * i) * 4))
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int bb = 0; bb < kBatch; ++bb) {
-      const int blk = b0 + bb * kThreads;
-      if (blk >= nb) break;
+      const int li = b0 + bb * kThreads;
+      if (li >= nblk) break;
       float lg[kSubs * GS];
 #pragma unroll
       for (int i = 0; i < GS; ++i) {
@@ -283,56 +329,89 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelectArgs a) {
           best = fmaxf(best, gsum);
         }
       }
-      keys[blk] = order_key(best);
-      flags[blk] = 0;
+      keys[blk0 + li] = order_key(best);
     }
   }
   __syncthreads();
+  // the eviction set is never a query-aware candidate
   for (int i = threadIdx.x; i < n_e; i += kThreads) {
-    keys[ev_new[i]] = 0u;  // excluded from the query-aware part
-    flags[ev_new[i]] = 1;
+    const int id = ev_new[i];
+    if (id >= blk0 && id < blk0 + nblk) keys[id] = 0u;
   }
   __syncthreads();
 
-  // query-aware part (or the ordered list)
+  // query-aware part (or the ordered list): the mq best of the row
   const int mq = a.ordered ? min(a.k, nb) : min(a.k - n_e, nb - n_e);
-  int32_t* out = a.selected + (int64_t)row * a.k;
-  __shared__ int s_count;
-  if (mq > 0) {
-    const bool ordered = a.ordered != 0;
-    wg_top_m(keys, nb, mq, top, [&](int i, int pos) {
-      if (ordered) ord[pos] = i;
-      else flags[i] = 1;
-    });
+  bool done = mq <= 0;
+  if (chunks > 1) {
+    // this chunk's keys to the row's last workgroup
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(a.cand + (int64_t)row * a.nb_max, (uint32_t)(a.nb_max * 4));
+    for (int li = threadIdx.x; li < nblk; li += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b32(keys[blk0 + li], krs, (blk0 + li) * 4, 0, kSC1);
+    if (!last_arrival(a.counters + row, chunks, &s_flag)) return;
+
+    // the row's last workgroup: every chunk's keys
+    if (!done && mq <= 16 && nb <= kKpt * kThreads) {
+      uint32_t kv[kKpt];  // key + 1: 1 = excluded, 0 = past the end
+#pragma unroll
+      for (int j = 0; j < kKpt; ++j) {
+        const int i = threadIdx.x + kThreads * j;
+        kv[j] = i < nb ? __builtin_amdgcn_raw_buffer_load_b32(krs, i * 4, 0, kSC1) + 1u : 0u;
+      }
+      done = wg_top_small<kKpt>(kv, mq, small, [&](int i, int pos) { ord[pos] = i; });
+    }
+    if (!done) {
+      for (int i = threadIdx.x; i < nb; i += kThreads)
+        if (i < blk0 || i >= blk0 + nblk) keys[i] = __builtin_amdgcn_raw_buffer_load_b32(krs, i * 4, 0, kSC1);
+      __syncthreads();
+    }
+  } else if (!done && mq <= 16 && nb <= kKpt * kThreads) {
+    uint32_t kv[kKpt];
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) {
+      const int i = threadIdx.x + kThreads * j;
+      kv[j] = i < nb ? keys[i] + 1u : 0u;
+    }
+    done = wg_top_small<kKpt>(kv, mq, small, [&](int i, int pos) { ord[pos] = i; });
   }
-  if (wave == 0) {
-    if (!a.ordered) {
-      // selected = flagged blocks, ascending
-      int taken = 0;
-      const uint64_t below = (1ull << lane) - 1ull;
-      for (int base = 0; base < nb; base += 8 * kWave) {
-        bool f[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = base + j * kWave + lane;
-          f[j] = i < nb && flags[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint64_t bm = __ballot(f[j]);
-          if (f[j]) out[taken + __popcll(bm & below)] = base + j * kWave + lane;
-          taken += __popcll(bm);
+  if (!done) wg_top_m(keys, nb, mq, top, [&](int i, int pos) { ord[pos] = i; });
+  __syncthreads();
+
+  // ord[0..mq): the selected ids in id order
+  int32_t* out = a.selected + (int64_t)row * a.k;
+  const int count = a.ordered ? mq : n_e + mq;
+  if (!a.ordered) {
+    // selected ids ascending: the eviction set and the query-aware list are
+    // each ascending and disjoint, so each id goes after the smaller ids of
+    // the other list
+    auto below = [](const int* v, int n, int id) {  // entries < id of ascending v[0..n)
+      int lo = 0;
+      while (n > 0) {
+        const int half = n >> 1;
+        if (v[lo + half] < id) {
+          lo += half + 1;
+          n -= half + 1;
+        } else {
+          n = half;
         }
       }
-      if (lane == 0) s_count = taken;
-    } else if (lane == 0) {
-      s_count = mq;
+      return lo;
+    };
+    for (int t = threadIdx.x; t < count; t += kThreads) {
+      const bool ev = t < n_e;
+      const int id = ev ? ev_new[t] : ord[t - n_e];
+      out[(ev ? t : t - n_e) + (ev ? below(ord, mq, id) : below(ev_new, n_e, id))] = id;
     }
-  }
-  __syncthreads();
-  const int count = s_count;
-  if (a.ordered) {
-    // rank = entries with a larger key, or an equal key and a lower id
+    if (a.k_e > 0) {
+      for (int i = threadIdx.x; i < a.k_e; i += kThreads)
+        a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? ev_new[i] : -1;
+      if (threadIdx.x == 0) a.evict_seen[row] = nb;
+    }
+  } else {
+    // descending score: rank = entries with a larger key, or an equal key
+    // and a lower id (keys[] holds the row's keys: one chunk, or the
+    // fallback above)
     for (int i = threadIdx.x; i < mq; i += kThreads) {
       const int id = ord[i];
       const uint32_t key = keys[id];
@@ -374,10 +453,12 @@ hipError_t launch_t(const SelectLaunch& L, hipStream_t stream) {
   a.ordered = L.ordered;
   a.nb_max = lay.nb_max;
   a.qscale = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;  // natural -> base-2 logits
-  const size_t smem = (size_t)(lay.nb_max + a.k_e) * 4 + (size_t)2 * a.k_e * 4 +
-                      (size_t)(a.ordered ? a.k : 0) * 4 + round_up((size_t)lay.nb_max, 4);
+  a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
   dim3 grid(lay.chunks, lay.rows);
-  score_select_kernel<T, D, G, FORECAST><<<grid, kThreads, smem, stream>>>(a);
+  score_kernel<T, D, G, FORECAST><<<grid, kThreads, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_kernel<G, FORECAST><<<grid, kThreads, select_dyn_lds(lay, a.k, a.k_e), stream>>>(a);
   return hipGetLastError();
 }
 
