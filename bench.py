@@ -71,6 +71,12 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="early-stop workload only: the dense reference, nsa_sparse_decode over "
                          "every full block with no scoring")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="forecast workloads, two-call path: the layer instances form a stack; "
+                         "layer l+1's selection runs on a second stream while layer l decodes "
+                         "(it waits for layer l-1's decode, whose output the forecast of layer "
+                         "l+1 is made from); value is this schedule's rate, the one-stream rate "
+                         "is reported beside it")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps as one captured HIP graph instead of launching "
                          "them one by one (measured slower at short runs on this stack)")
@@ -291,6 +297,9 @@ def gpu_leg(args, cfg):
                 step(base + i)
         graph.replay()
         torch.cuda.synchronize()
+    lookahead = None
+    if args.lookahead:
+        lookahead = lookahead_pass(args, layers, sel_q, qs, lens, cfg, base)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     # the device spins for a moment before the start event, so that the host
@@ -340,7 +349,54 @@ def gpu_leg(args, cfg):
         metrics.update(locality_metrics(layers[0], cfg, lens, sel_q, qs, fused))
     return dict(R=R, total_ms=total_ms, wall_s=wall, sel_ms=sel_ms, dec_ms=dec_ms,
                 sel_bytes=sb, dec_bytes=db, n_blocks=n_blocks, fused=fused, dense=dense,
-                graph=args.graph, metrics=metrics)
+                graph=args.graph, metrics=metrics, lookahead=lookahead)
+
+
+def lookahead_pass(args, layers, sel_q, qs, lens, cfg, base):
+    """The layer instances as a stack of R layers, one token through it per
+    R steps.  SparDA's forecast of layer l selects layer l+1's blocks (SparDA
+    summary, "Trainierbare Lookahead Sparse-Selektion"), so layer l+1's
+    selection can run while layer l decodes: it needs only the forecast,
+    which is made from layer l's input, the output of layer l-1's decode.
+    Step i (layer i mod R) therefore waits for its own selection; the
+    selection of step i+1 runs on a second stream after step i-1's decode.
+    Returns the timed rate of this schedule (K steps)."""
+    import torch
+    R = len(layers)
+    steps = cfg.steps
+    sel_stream = torch.cuda.Stream()  # default priority
+    main = torch.cuda.current_stream()
+    ring = 4
+    sel_done = [torch.cuda.Event() for _ in range(ring)]
+    dec_done = [torch.cuda.Event() for _ in range(ring)]
+
+    def select(i):
+        lay, t = layers[i % R], i % steps
+        lay.seq_lens = lens[t]
+        lay.select(sel_q[t], cfg.seq_len(t), stream=sel_stream.cuda_stream)
+        sel_done[i % ring].record(sel_stream)
+
+    def run(first, n):
+        select(first)
+        for i in range(first, first + n):
+            if i + 1 < first + n:
+                if i > first:
+                    sel_stream.wait_event(dec_done[(i - 1) % ring])
+                select(i + 1)
+            main.wait_event(sel_done[i % ring])
+            layers[i % R].decode(qs[i % steps], stream=main.cuda_stream)
+            dec_done[i % ring].record(main)
+
+    run(base, 2 * R)  # untimed
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1_000_000)
+    start.record(main)
+    run(base, args.steps)
+    end.record(main)
+    torch.cuda.synchronize()
+    return {"ms_per_step": start.elapsed_time(end) / args.steps,
+            "schedule": "selection of layer l+1 on a second stream during layer l's decode"}
 
 
 def locality_metrics(lay, cfg, lens, sel_q, qs, fused):
@@ -451,7 +507,9 @@ def cpu_leg(args, cfg):
                       f"threads); scaled to all rows"}
 
 
-KERNEL_SYMBOLS = {"step": "gang_kernel", "select": "score_select_kernel", "decode": "decode_kernel"}
+# the kernels of one call (their per-launch counters are summed)
+KERNEL_SYMBOLS = {"step": ("gang_kernel",), "select": ("score_kernel", "select_kernel"),
+                  "decode": ("decode_kernel",)}
 CALIBRATION_SYMBOL = "MulFunctor"
 
 
@@ -494,10 +552,12 @@ def traffic_mode(args) -> int:
     else:
         kernels = ["select", "decode"]
     for kern in kernels:
-        sym = KERNEL_SYMBOLS[kern]
+        syms = KERNEL_SYMBOLS[kern]
         if kern == "decode" and cfg.ordered and not args.dense:
-            sym = "es_walk_kernel"
-        f_k, w_k = pick(fetch, sym) * 1024, pick(write, sym) * 1024
+            syms = ("es_walk_kernel",)
+        f_k = sum(pick(fetch, sym) for sym in syms) * 1024
+        w_k = sum(pick(write, sym) for sym in syms) * 1024
+        sym = "+".join(syms)
         rec = {
             "kernel": kern, "symbol": sym, "workload": workload,
             "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
@@ -528,8 +588,16 @@ def main():
     if args.dense and not cfg.ordered:
         print("--dense is the early-stop workload's dense reference", file=sys.stderr)
         return 2
+    if args.lookahead and (cfg.mode != "forecast" or args.path != "split" or cfg.ordered):
+        print("--lookahead needs a forecast workload on the two-call path (--path split): "
+              "only a forecast is known before the layer's own query", file=sys.stderr)
+        return 2
     g = gpu_leg(args, cfg)
     ms_per_step = g["total_ms"] / args.steps
+    if g["lookahead"] is not None:
+        g["metrics"]["one_stream_ms_per_step"] = round(ms_per_step, 5)
+        g["metrics"]["lookahead"] = g["lookahead"]["schedule"]
+        ms_per_step = g["lookahead"]["ms_per_step"]
     value = cfg.batch / (ms_per_step / 1e3)
     # a step of one kernel: its duration is the timed region's (HIP events
     # around the K launches on their stream) divided by K; a step of two
@@ -572,6 +640,7 @@ def main():
                    "path": "fused" if g["fused"] else ("dense" if g["dense"] else "split"),
                    "decode_steps_cycled": cfg.steps, "layer_instances": g["R"],
                    "timed_as": "one HIP graph of the K steps" if g["graph"] else "K launches",
+                   "schedule": "lookahead, two streams" if g["lookahead"] else "one stream",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dk["GB/s"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dk["frac"], 4),

@@ -408,10 +408,35 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
         a.evict_set[(int64_t)row * a.k_e + i] = i < n_e ? ev_new[i] : -1;
       if (threadIdx.x == 0) a.evict_seen[row] = nb;
     }
+  } else if (mq <= kThreads) {
+    // descending score, ties to the lower id: a bitonic sort of the
+    // composites (key, complement of the id), one per thread (keys[] holds
+    // the row's keys: one chunk, or the fallback above)
+    const int t = threadIdx.x;
+    uint64_t v = t < mq ? ((uint64_t)keys[ord[t]] << 32) | (uint32_t)~(uint32_t)ord[t] : 0ull;
+    __shared__ uint64_t xs[kThreads];
+    for (int size = 2; size <= kThreads; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        uint64_t o;
+        if (stride >= kWave) {
+          xs[t] = v;
+          __syncthreads();
+          o = xs[t ^ stride];
+          __syncthreads();
+        } else {
+          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride, kWave);
+          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride, kWave);
+          o = ((uint64_t)hi << 32) | lo;
+        }
+        // descending runs where bit `size` of t is clear, ascending where set
+        const bool keep_max = ((t & stride) == 0) == ((t & size) == 0);
+        v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+      }
+    }
+    if (t < mq) out[t] = (int)~(uint32_t)v;
   } else {
     // descending score: rank = entries with a larger key, or an equal key
-    // and a lower id (keys[] holds the row's keys: one chunk, or the
-    // fallback above)
+    // and a lower id
     for (int i = threadIdx.x; i < mq; i += kThreads) {
       const int id = ord[i];
       const uint32_t key = keys[id];
