@@ -15,7 +15,8 @@ head g with its G query heads), written step by step from the pages:
   pre-exponential eviction scores (ED-DMA).
 * SparDA technical summary (gist.science, German), "2. Methodik /
   Kompakter Forecast-Indexer": one forecast vector per KV head (GQA group),
-  no per-query-head loop and no softmax in the selector.
+  no per-query-head loop and no softmax in the selector; "Trainingsstrategie":
+  the inference window of 32 tokens with stride 16.
 * S2O technical summary (gist.science, Italian), "2. Regola di Arresto
   Anticipato" and "3. Implementazione del Kernel": blocks walked in descending
   estimated importance, stop once the marginal attention mass of a block is
@@ -193,6 +194,25 @@ def block_scores_forecast(f: np.ndarray, reps: np.ndarray) -> np.ndarray:
     nb, nsub, d = reps.shape
     s = reps.reshape(nb * nsub, d) @ np.asarray(f, dtype=np.float64)
     return s.reshape(nb, nsub).max(axis=1)
+
+
+def block_scores_forecast_window(f: np.ndarray, reps: np.ndarray) -> np.ndarray:
+    """SparDA inference-window block scores S: [nb] -- raw f . w, maximum over
+    the windows of a block.
+
+    SparDA summary, "Trainingsstrategie": the selector's inference grid is a
+    compression window of 32 tokens with stride 16.  The window that starts
+    at a sub-block boundary covers two adjacent 16-token sub-blocks, so its
+    mean is the mean of their two means, w = (r_j + r_{j+1}) / 2.  Readings:
+    a block owns the three windows that lie inside it (starting at its tokens
+    0, 16 and 32; the window starting at token 48 reaches into the next block
+    and belongs to neither), its score is the largest f . w over them, and,
+    as in the raw forecast mode, there is no scale and no softmax.
+    """
+    nb, nsub, d = reps.shape
+    w = (reps[:, :-1, :] + reps[:, 1:, :]) / 2.0                 # [nb, nsub - 1, d]
+    s = w.reshape(nb * (nsub - 1), d) @ np.asarray(f, dtype=np.float64)
+    return s.reshape(nb, nsub - 1).max(axis=1)
 
 
 # =============================================================================
@@ -406,6 +426,8 @@ class OracleRow:
     def scores(self, nb: int, q=None, f=None) -> np.ndarray:
         if self.mode == "forecast":
             return block_scores_forecast(f, self.reps(nb))
+        if self.mode == "forecast_window":
+            return block_scores_forecast_window(f, self.reps(nb))
         return block_scores_group_softmax(q, self.reps(nb), self.scale)
 
     def step(self, L: int, q, f=None, attend_out: bool = True) -> dict:

@@ -240,6 +240,35 @@ def check_forecast(O):
         assert math.isclose(S[b], want, rel_tol=1e-12)
 
 
+def check_forecast_window(O):
+    """The (32, 16) inference window: brute force over the 32-token windows of
+    every block from the tokens themselves (unrounded sub-block means), the
+    reduction to the raw forecast mode when a block's sub-blocks agree, and a
+    window across a block boundary that must not count."""
+    rng = np.random.default_rng(19)
+    d, nb = 5, 6
+    f = rng.standard_normal(d)
+    keys = rng.standard_normal((nb * 64, d))
+    reps = np.zeros((nb, 4, d))
+    for b in range(nb):
+        for j in range(4):
+            reps[b, j] = sum(keys[64 * b + 16 * j + i] for i in range(16)) / 16.0
+    S = O.block_scores_forecast_window(f, reps)
+    for b in range(nb):
+        best = -math.inf
+        for start in (0, 16, 32):
+            mean = sum(keys[64 * b + start + i] for i in range(32)) / 32.0
+            best = max(best, sum(f[c] * mean[c] for c in range(d)))
+        assert math.isclose(S[b], best, rel_tol=1e-12, abs_tol=1e-12), (b, S[b], best)
+    same = np.repeat(rng.standard_normal((nb, 1, d)), 4, axis=1)
+    assert np.allclose(O.block_scores_forecast_window(f, same), O.block_scores_forecast(f, same),
+                       rtol=1e-14, atol=0)
+    r = np.zeros((2, 4, 1))
+    r[0, 3, 0] = r[1, 0, 0] = 1.0          # only the window across the boundary is 1
+    S = O.block_scores_forecast_window(np.array([1.0]), r)
+    assert S.tolist() == [0.5, 0.5]
+
+
 # ----------------------------------------------------------------------------
 # step 3: selection
 # ----------------------------------------------------------------------------
@@ -607,7 +636,7 @@ def check_residency_diff(O):
 ALL_CHECKS = [
     check_round, check_rne_fraction, check_rounded_means, check_reps_layout,
     check_eviction_scores, check_scores_bruteforce, check_scores_closed_forms,
-    check_forecast, check_topk_exchange, check_selection_golden, check_select_bruteforce,
+    check_forecast, check_forecast_window, check_topk_exchange, check_selection_golden, check_select_bruteforce,
     check_eviction_incremental, check_dense_reduction, check_attend_loops,
     check_early_stop, check_locality, check_row_trajectory, check_residency_diff,
 ]

@@ -189,13 +189,33 @@ def mut_residency_swapped(O):
     O.residency_diff = f
 
 
+def mut_window_across_blocks(O):
+    """A block also owns the window that reaches into the next block."""
+    def f(fv, reps):
+        nb, nsub, d = reps.shape
+        flat = reps.reshape(nb * nsub, d)
+        nxt = np.concatenate([flat[1:], flat[-1:]], axis=0)
+        s = ((flat + nxt) / 2.0) @ np.asarray(fv, dtype=np.float64)
+        return s.reshape(nb, nsub).max(axis=1)
+    O.block_scores_forecast_window = f
+
+
+def mut_window_skips_a_sub_block(O):
+    """A window pairs sub-blocks j and j + 2."""
+    def f(fv, reps):
+        w = (reps[:, :-2, :] + reps[:, 2:, :]) / 2.0
+        nb, n, d = w.shape
+        return (w.reshape(nb * n, d) @ np.asarray(fv, dtype=np.float64)).reshape(nb, n).max(axis=1)
+    O.block_scores_forecast_window = f
+
+
 MUTANTS = [mut_no_softmax, mut_max_before_head_sum, mut_ties_to_higher_id, mut_tail_dropped,
            mut_stop_block_excluded, mut_sub_block_shift, mut_eviction_forgets_old,
            mut_attention_unscaled, mut_round_truncates, mut_parts_overlap, mut_mean_by_15,
            mut_gamma_ignores_tail, mut_row_reps_from_previous_block,
            mut_row_eviction_from_previous_block, mut_row_prev_tail_off_by_one,
            mut_row_ordered_stop_ignored, mut_residency_ignores_tail,
-           mut_residency_swapped]
+           mut_residency_swapped, mut_window_across_blocks, mut_window_skips_a_sub_block]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
