@@ -125,7 +125,7 @@ def select_bytes(cfg, L: int) -> int:
     e = 2 if cfg.dtype == "bf16" else 4
     nb = L // 64
     reps = cfg.rows * nb * 4 * cfg.head_dim * e
-    qv = (cfg.batch * cfg.num_kv_heads if cfg.mode == "forecast" else cfg.batch * cfg.num_q_heads)
+    qv = (cfg.batch * cfg.num_kv_heads if cfg.mode.startswith("forecast") else cfg.batch * cfg.num_q_heads)
     qbytes = qv * cfg.head_dim * e
     out = cfg.rows * (cfg.k + 1) * 4
     state = cfg.rows * (2 * cfg.k_e + 1) * 4 if cfg.k_e else 0
@@ -214,7 +214,7 @@ def gpu_leg(args, cfg):
     steps = cfg.steps
     lens = [torch.full((cfg.batch,), cfg.seq_len(t), dtype=torch.int32, device=dev) for t in range(steps)]
     qs = [to_dev(W.queries(cfg, t)) for t in range(steps)]
-    sel_q = ([to_dev(W.forecasts(cfg))] * steps) if cfg.mode == "forecast" else qs
+    sel_q = ([to_dev(W.forecasts(cfg))] * steps) if cfg.mode.startswith("forecast") else qs
     fills = [(cfg.seq_len(t) % 64) == 0 for t in range(steps)]
     fill_first = [torch.full((cfg.batch,), cfg.seq_len(t) // 64 - 1, dtype=torch.int32, device=dev)
                   for t in range(steps)]
@@ -471,7 +471,7 @@ def cpu_leg(args, cfg):
             if cfg.k_e:
                 row.eviction_scores(cfg.nb0)
         qs = [W.stored_to_f64(W.query_row(cfg, b, g, t), cfg.dtype) for t in range(cfg.steps)]
-        f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode == "forecast" else None
+        f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode.startswith("forecast") else None
         sample.append((row, qs, f))
 
     def one_pass():
@@ -588,7 +588,7 @@ def main():
     if args.dense and not cfg.ordered:
         print("--dense is the early-stop workload's dense reference", file=sys.stderr)
         return 2
-    if args.lookahead and (cfg.mode != "forecast" or args.path != "split" or cfg.ordered):
+    if args.lookahead and (not cfg.mode.startswith("forecast") or args.path != "split" or cfg.ordered):
         print("--lookahead needs a forecast workload on the two-call path (--path split): "
               "only a forecast is known before the layer's own query", file=sys.stderr)
         return 2

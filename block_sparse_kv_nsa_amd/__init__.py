@@ -17,6 +17,7 @@ from ._abi import (  # noqa: F401
     NSA_F32,
     NSA_OK,
     NSA_SCORE_FORECAST_RAW,
+    NSA_SCORE_FORECAST_WINDOW,
     NSA_SCORE_GROUP_SOFTMAX,
     DecodeParams,
     NsaError,

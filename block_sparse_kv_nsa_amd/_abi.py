@@ -30,6 +30,7 @@ NSA_BF16 = 1
 
 NSA_SCORE_GROUP_SOFTMAX = 0
 NSA_SCORE_FORECAST_RAW = 1
+NSA_SCORE_FORECAST_WINDOW = 2
 
 EXPORTS = (
     "nsa_update_block_reps",

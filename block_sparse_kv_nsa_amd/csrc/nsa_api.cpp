@@ -75,7 +75,8 @@ float scale_of(const nsa_shape* s) {
 
 nsa_status check_select_params(const char* fn, const nsa_select_params* p) {
   if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: params is NULL", fn);
-  if (p->mode != NSA_SCORE_GROUP_SOFTMAX && p->mode != NSA_SCORE_FORECAST_RAW)
+  if (p->mode != NSA_SCORE_GROUP_SOFTMAX && p->mode != NSA_SCORE_FORECAST_RAW &&
+      p->mode != NSA_SCORE_FORECAST_WINDOW)
     return fail(NSA_ERR_INVALID_ARGUMENT, "%s: unknown score mode %d", fn, p->mode);
   if (p->k < 1 || p->k > kMaxK)
     return fail(NSA_ERR_INVALID_ARGUMENT, "%s: k %d outside [1, %d]", fn, p->k, kMaxK);
@@ -189,7 +190,7 @@ static nsa_status select_layout_checked(const char* fn, const nsa_shape* shape,
                 shape->max_blocks_per_seq * 64);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   *lay = nsa::select_layout(shape->batch, shape->num_kv_heads, G,
-                            params->mode == NSA_SCORE_FORECAST_RAW, max_seq_len, params->k,
+                            params->mode != NSA_SCORE_GROUP_SOFTMAX, max_seq_len, params->k,
                             env_int("NSA_SELECT_CHUNK"));
   // dynamic shared memory of the selection kernel (its static part is
   // under 16 KiB of the 64 KiB a workgroup may hold)

@@ -46,6 +46,7 @@ struct SelectArgs {
   uint32_t* cand;  // [rows][nb_max] block keys handed to the row's last workgroup
   int64_t logits_row;
   int Hkv, max_blocks, chunk_reps, k, k_e, ordered, nb_max;
+  int window;  // forecast on the inference window (32, 16)
   float qscale;
 };
 
@@ -318,8 +319,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
       }
       float best = -INFINITY;
       if constexpr (FORECAST) {
+        if (a.window) {
+          // the windows inside the block: sub-blocks (j, j + 1), mean of
+          // the two means, so f.w is the mean of the two logits
 #pragma unroll
-        for (int j = 0; j < kSubs; ++j) best = fmaxf(best, lg[j]);
+          for (int j = 0; j + 1 < kSubs; ++j) best = fmaxf(best, 0.5f * (lg[j] + lg[j + 1]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < kSubs; ++j) best = fmaxf(best, lg[j]);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < kSubs; ++j) {
@@ -477,6 +485,7 @@ hipError_t launch_t(const SelectLaunch& L, hipStream_t stream) {
   a.k_e = L.ordered ? 0 : L.k_e;
   a.ordered = L.ordered;
   a.nb_max = lay.nb_max;
+  a.window = L.mode == 2;
   a.qscale = FORECAST ? 1.0f : L.scale * 1.4426950408889634f;  // natural -> base-2 logits
   a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
   dim3 grid(lay.chunks, lay.rows);
@@ -489,7 +498,7 @@ hipError_t launch_t(const SelectLaunch& L, hipStream_t stream) {
 
 template <typename T, int D, int G>
 hipError_t by_mode(const SelectLaunch& L, hipStream_t s) {
-  return L.mode == 1 ? launch_t<T, D, G, true>(L, s) : launch_t<T, D, G, false>(L, s);
+  return L.mode != 0 ? launch_t<T, D, G, true>(L, s) : launch_t<T, D, G, false>(L, s);
 }
 
 template <typename T, int D>

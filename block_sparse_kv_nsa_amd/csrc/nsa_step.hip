@@ -70,6 +70,7 @@ struct GangArgs {
   float* part_acc;   // [rows][kMaxGang][G][D]
   int rows, Hkv, max_blocks, nb_max, k, k_e, P;
   int CS, CA, gangs, per_wg;  // scorers and attenders per row, rows at once, reps per scorer
+  int window;                 // forecast on the inference window (32, 16)
   float qscale_sel, qscale_att;
   uint64_t wait_ticks;
   uint32_t stats_bytes, keys_bytes, ml_bytes, acc_bytes;
@@ -529,6 +530,19 @@ struct Gang {
           for (int uu = 0; uu < 4; ++uu) v[uu] += quad_partner<2>(v[uu]);
 #pragma unroll
           for (int uu = 0; uu < 4; ++uu) v[uu] += quad_partner<1>(v[uu]);
+        } else if (a.window) {
+          // the windows inside the block: the 16 lanes of a block hold its
+          // sub-blocks j = (lane >> 2) & 3 (4 lanes each); a rotation by 4
+          // lanes pairs each sub-block with a neighbour, and the pair is a
+          // window when their indices differ by one (not the wrap 3 <-> 0);
+          // f.w is the mean of the two logits
+          const float sj = (float)((lane >> 2) & 3);
+          const float nj = dpp_mov<0x124>(sj);  // row_ror:4
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            const float nv = dpp_mov<0x124>(v[uu]);
+            v[uu] = fabsf(nj - sj) == 1.f ? 0.5f * (v[uu] + nv) : -INFINITY;
+          }
         }
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu) v[uu] = fmaxf(v[uu], dpp_mov<0x124>(v[uu]));  // row_ror:4
@@ -827,6 +841,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
   a.P = L.P;
   a.nb_max = lay.nb_max;
   a.k = L.k;
+  a.window = L.mode == 2;
   a.k_e = L.k_e;
   a.CS = plan.CS;
   a.CA = plan.CA;
@@ -846,7 +861,7 @@ hipError_t launch_t(const StepLaunch& L, hipStream_t stream, int32_t* status) {
 
 template <typename T, int D, int G>
 hipError_t by_mode(const StepLaunch& L, hipStream_t s, int32_t* st) {
-  return L.mode == 1 ? launch_t<T, D, G, true>(L, s, st) : launch_t<T, D, G, false>(L, s, st);
+  return L.mode != 0 ? launch_t<T, D, G, true>(L, s, st) : launch_t<T, D, G, false>(L, s, st);
 }
 
 template <typename T, int D>

@@ -13,7 +13,8 @@ from . import _abi as A
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _NSA_DTYPE = {"bf16": A.NSA_BF16, "f32": A.NSA_F32}
-_MODE = {"group_softmax": A.NSA_SCORE_GROUP_SOFTMAX, "forecast": A.NSA_SCORE_FORECAST_RAW}
+_MODE = {"group_softmax": A.NSA_SCORE_GROUP_SOFTMAX, "forecast": A.NSA_SCORE_FORECAST_RAW,
+         "forecast_window": A.NSA_SCORE_FORECAST_WINDOW}
 
 
 class SparseDecodeLayer:

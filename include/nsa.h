@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 3
+#define NSA_ABI_VERSION 4
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -77,7 +77,13 @@ typedef enum nsa_score_mode {
   /* SparDA forecast: one vector f per KV head; a block scores
    * max over its sub-blocks of f.r, no scale, no softmax.  `query` is
    * [B][Hkv][D]. */
-  NSA_SCORE_FORECAST_RAW = 1
+  NSA_SCORE_FORECAST_RAW = 1,
+  /* SparDA forecast on the inference window of 32 tokens with stride 16
+   * (SparDA summary, "Trainingsstrategie"): the window starting at sub-block
+   * j has the mean (r_j + r_{j+1}) / 2; a block scores the maximum of f.w
+   * over the three windows inside it, no scale, no softmax.  `query` is
+   * [B][Hkv][D]. */
+  NSA_SCORE_FORECAST_WINDOW = 2
 } nsa_score_mode;
 
 /* Tensor geometry shared by all calls. */

@@ -76,7 +76,7 @@ def upload(layer, cfg: W.Config, batch: W.Batch) -> None:
 
 
 def device_query(cfg: W.Config, step: int) -> torch.Tensor:
-    if cfg.mode == "forecast":
+    if cfg.mode.startswith("forecast"):
         return to_dev(W.forecasts(cfg), cfg.dtype)
     return to_dev(W.queries(cfg, step), cfg.dtype)
 
@@ -201,7 +201,7 @@ def check_step(cfg: W.Config, res: StepResult, orow: O.OracleRow, b: int, g: int
     nb = L // 64
     G = cfg.group
     q = W.stored_to_f64(W.query_row(cfg, b, g, step), cfg.dtype)
-    f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode == "forecast" else None
+    f = W.stored_to_f64(W.forecast_row(cfg, b, g), cfg.dtype) if cfg.mode.startswith("forecast") else None
     S = orow.scores(nb, q=q, f=f)
     n = int(res.num_selected[b, g])
     gsel = [int(x) for x in res.selected[b, g, :n]]

@@ -75,7 +75,7 @@ def test_shape_validation(kw, status):
 @pytest.mark.parametrize("params,status", [
     (N.SelectParams(0, 64, 65, 0), N.NSA_ERR_INVALID_ARGUMENT),   # k_e > k
     (N.SelectParams(0, 0, 0, 0), N.NSA_ERR_INVALID_ARGUMENT),     # k = 0
-    (N.SelectParams(2, 64, 0, 0), N.NSA_ERR_INVALID_ARGUMENT),    # mode
+    (N.SelectParams(3, 64, 0, 0), N.NSA_ERR_INVALID_ARGUMENT),    # mode
     (N.SelectParams(0, 64, 8, 1), N.NSA_ERR_INVALID_ARGUMENT),    # ordered with k_e
     (N.SelectParams(0, 5000, 0, 0), N.NSA_ERR_INVALID_ARGUMENT),  # k too large
 ])

@@ -45,6 +45,12 @@ def test_config2_sparda_sampled_rows():
     H.run_and_check(cfg, rows=H.sample_rows(cfg, 12))
 
 
+def test_config2_sparda_inference_window_sampled_rows():
+    """The sparda-8b workload scored on the (32, 16) inference window."""
+    cfg = W.config(2).replace(name="sparda-8b-window", mode="forecast_window")
+    H.run_and_check(cfg, rows=H.sample_rows(cfg, 12))
+
+
 def test_config3_long_context_sampled_rows():
     cfg = W.config(3)
     _, st = H.run_and_check(cfg, rows=H.sample_rows(cfg, 6), check_every=3)
@@ -114,6 +120,9 @@ SMALL = [
     ("bf16", 128, 4, "group_softmax", False),
     ("bf16", 128, 4, "forecast", False),
     ("f32", 64, 4, "forecast", False),
+    ("bf16", 128, 4, "forecast_window", False),
+    ("f32", 64, 2, "forecast_window", False),
+    ("bf16", 128, 4, "forecast_window", True),
     ("bf16", 128, 8, "group_softmax", True),
     ("f32", 64, 2, "group_softmax", True),
     ("bf16", 64, 1, "group_softmax", True),
@@ -125,7 +134,7 @@ def test_small_shapes(dtype, D, G, mode, ordered):
     cfg = W.Config(f"small-{dtype}-{D}-{G}-{mode}-{int(ordered)}", 10 + SMALL.index(
         (dtype, D, G, mode, ordered)), batch=3, context=64 * 41 + 37, num_q_heads=2 * G,
         num_kv_heads=2, head_dim=D, dtype=dtype, mode=mode, k=12 if not ordered else 20,
-        k_e=0 if (mode == "forecast" or ordered) else 8, steps=30, ordered=ordered,
+        k_e=0 if (mode.startswith("forecast") or ordered) else 8, steps=30, ordered=ordered,
         tau=1e-3 if ordered else 0.0)
     H.run_and_check(cfg)
 

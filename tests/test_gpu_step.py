@@ -37,6 +37,11 @@ def test_step_config2_forecast_sampled_rows():
     H.run_and_check(cfg, rows=H.sample_rows(cfg, 12), fused=True)
 
 
+def test_step_config2_inference_window_sampled_rows():
+    cfg = W.config(2).replace(name="sparda-8b-window", mode="forecast_window")
+    H.run_and_check(cfg, rows=H.sample_rows(cfg, 12), fused=True)
+
+
 def test_step_config3_long_context_sampled_rows():
     cfg = W.config(3)
     _, st = H.run_and_check(cfg, rows=H.sample_rows(cfg, 6), check_every=3, fused=True)
@@ -71,6 +76,8 @@ SMALL = [
     ("bf16", 128, 4, "forecast"),
     ("f32", 64, 4, "forecast"),
     ("bf16", 64, 1, "forecast"),
+    ("bf16", 128, 4, "forecast_window"),
+    ("f32", 64, 2, "forecast_window"),
 ]
 
 
@@ -78,7 +85,7 @@ SMALL = [
 def test_step_small_shapes(dtype, D, G, mode):
     cfg = W.Config(f"step-small-{dtype}-{D}-{G}-{mode}", 60 + SMALL.index((dtype, D, G, mode)),
                    batch=3, context=64 * 41 + 37, num_q_heads=2 * G, num_kv_heads=2,
-                   head_dim=D, dtype=dtype, mode=mode, k=12, k_e=0 if mode == "forecast" else 8,
+                   head_dim=D, dtype=dtype, mode=mode, k=12, k_e=0 if mode.startswith("forecast") else 8,
                    steps=30)
     H.run_and_check(cfg, fused=True)
 

@@ -76,7 +76,7 @@ class Config:
     num_kv_heads: int
     head_dim: int
     dtype: str            # "f32" or "bf16"
-    mode: str             # "group_softmax" (NOSA) or "forecast" (SparDA)
+    mode: str             # "group_softmax" (NOSA), "forecast" or "forecast_window" (SparDA)
     k: int                # blocks selected per row (the cap in ordered mode)
     k_e: int              # eviction budget (query-agnostic part)
     steps: int            # decode steps; step t appends token context+t
@@ -172,7 +172,7 @@ def forecast_row(cfg: Config, b: int, g: int) -> np.ndarray:
 
 
 def planted_direction(cfg: Config, b: int, g: int) -> np.ndarray:
-    if cfg.mode == "forecast":
+    if cfg.mode.startswith("forecast"):
         v = stored_to_f64(forecast_row(cfg, b, g), cfg.dtype)
     else:
         v = stored_to_f64(query_row(cfg, b, g, 0), cfg.dtype).sum(axis=0)
