@@ -288,24 +288,37 @@ def token_set(blocks, L: int) -> np.ndarray:
     return np.concatenate(parts).astype(np.int64)
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """softmax((q . k_t) * scale) over the given tokens, applied to V: [G][d].
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, bias=None) -> np.ndarray:
+    """softmax((q . k_t) * scale [+ bias_t]) over the given tokens, applied to
+    V: [G][d].
 
-    Plain two-pass softmax in float64.
+    Plain two-pass softmax in float64.  bias: one additive logit per token
+    (the eviction logit under the ED-DMA reading, see sparse_attention), or
+    None.
     """
     logits = (np.asarray(q, dtype=np.float64) @ np.asarray(K, dtype=np.float64).T) * scale
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
     logits = logits - logits.max(axis=1, keepdims=True)
     w = np.exp(logits)
     w = w / w.sum(axis=1, keepdims=True)
     return w @ np.asarray(V, dtype=np.float64)
 
 
-def sparse_attention(q, keys, values, blocks, L: int, scale: float) -> np.ndarray:
+def sparse_attention(q, keys, values, blocks, L: int, scale: float, bias=None) -> np.ndarray:
+    """Attention over the given blocks plus the partial tail block.
+
+    bias (optional): the row's per-token eviction logits e_t in logical
+    token order.  NOSA summary, "ED-DMA": the eviction head selects on
+    pre-exponential scores and its exponential is deferred to the attention
+    stage.  Reading (a variant, off by default): exp(e_t) weights token t
+    inside the attention softmax, i.e. e_t is added to its logit.
+    """
     t = token_set(blocks, L)
-    return attend(q, keys[t], values[t], scale)
+    return attend(q, keys[t], values[t], scale, None if bias is None else np.asarray(bias)[t])
 
 
-def early_stop_attention(q, keys, values, order, L: int, tau: float, scale: float):
+def early_stop_attention(q, keys, values, order, L: int, tau: float, scale: float, bias=None):
     """Ordered traversal with the monotone-gain early stop.  Returns (n_star, out).
 
     S2O summary, "2. Regola di Arresto Anticipato" and "3. Implementazione del
@@ -317,19 +330,22 @@ def early_stop_attention(q, keys, values, order, L: int, tau: float, scale: floa
     the walk stops after the first block with M_h(n) < tau * A_h(n) for
     every head of the group (the block is loaded once for all of them); that
     block is kept.  Without such a block every listed block is attended.
+    With the ED-DMA bias (see sparse_attention) a token's logit includes its
+    eviction logit, in the masses as in the output.
     """
     q = np.asarray(q, dtype=np.float64)
     nb = L // BLOCK
     tail = np.arange(nb * BLOCK, L)
     blocks = [np.arange(b * BLOCK, (b + 1) * BLOCK) for b in order]
     every = np.concatenate([tail] + blocks).astype(np.int64)
-    logits_all = (q @ keys[every].T) * scale
+    e = np.zeros(keys.shape[0]) if bias is None else np.asarray(bias, dtype=np.float64)
+    logits_all = (q @ keys[every].T) * scale + e[every][None, :]
     c = logits_all.max(axis=1, keepdims=True)
 
     def mass(tok):
         if tok.size == 0:
             return np.zeros(q.shape[0])
-        return np.exp((q @ keys[tok].T) * scale - c).sum(axis=1)
+        return np.exp((q @ keys[tok].T) * scale + e[tok][None, :] - c).sum(axis=1)
 
     A = mass(tail)
     n_star = len(order)
@@ -339,7 +355,7 @@ def early_stop_attention(q, keys, values, order, L: int, tau: float, scale: floa
         if np.all(M < tau * A):
             n_star = n
             break
-    out = sparse_attention(q, keys, values, list(order[:n_star]), L, scale)
+    out = sparse_attention(q, keys, values, list(order[:n_star]), L, scale, bias)
     return n_star, out
 
 

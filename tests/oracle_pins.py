@@ -425,6 +425,39 @@ def brute_stop_index(q, keys, order, L, tau, scale):
     return len(order)
 
 
+def check_attention_bias(O):
+    """The ED-DMA bias variant: a bias of log(m_t) weighs token t as m_t
+    copies of it (brute force by duplication), a constant bias changes
+    nothing, and a block whose tokens carry a vanishing weight stops the walk
+    right after it."""
+    rng = np.random.default_rng(23)
+    G, d, L = 2, 5, 64 * 3 + 11
+    q = rng.standard_normal((G, d))
+    keys = rng.standard_normal((L, d))
+    values = rng.standard_normal((L, d))
+    mult = rng.integers(1, 4, size=L)
+    blocks = [2, 0]
+    got = O.sparse_attention(q, keys, values, blocks, L, 0.4, bias=np.log(mult))
+    toks = [t for b in blocks for t in range(64 * b, 64 * b + 64)] + list(range(192, L))
+    rep = [t for t in toks for _ in range(mult[t])]
+    want = O.attend(q, keys[rep], values[rep], 0.4)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    plain = O.sparse_attention(q, keys, values, blocks, L, 0.4)
+    shifted = O.sparse_attention(q, keys, values, blocks, L, 0.4, bias=np.full(L, 3.7))
+    assert np.allclose(plain, shifted, rtol=0, atol=1e-12)
+    n0, out0 = O.early_stop_attention(q, keys, values, [1, 2, 0], L, 1e-9, 0.4)
+    assert n0 == 3
+    n1, out1 = O.early_stop_attention(q, keys, values, [1, 2, 0], L, 1e-9, 0.4,
+                                      bias=np.full(L, -2.5))
+    assert n1 == 3 and np.allclose(out0, out1, rtol=0, atol=1e-12)
+    e = np.zeros(L)
+    e[128:192] = -60.0                      # block 2: weight e^-60 per token
+    n2, out2 = O.early_stop_attention(q, keys, values, [1, 2, 0], L, 1e-9, 0.4, bias=e)
+    assert n2 == 2
+    assert np.allclose(out2, O.sparse_attention(q, keys, values, [1, 2], L, 0.4, bias=e),
+                       rtol=0, atol=1e-12)
+
+
 def check_early_stop(O):
     rng = np.random.default_rng(24)
     d, G = 8, 2
@@ -638,5 +671,5 @@ ALL_CHECKS = [
     check_eviction_scores, check_scores_bruteforce, check_scores_closed_forms,
     check_forecast, check_forecast_window, check_topk_exchange, check_selection_golden, check_select_bruteforce,
     check_eviction_incremental, check_dense_reduction, check_attend_loops,
-    check_early_stop, check_locality, check_row_trajectory, check_residency_diff,
+    check_attention_bias, check_early_stop, check_locality, check_row_trajectory, check_residency_diff,
 ]

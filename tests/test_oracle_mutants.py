@@ -64,10 +64,10 @@ def mut_tail_dropped(O):
 def mut_stop_block_excluded(O):
     orig = O.early_stop_attention
 
-    def f(q, keys, values, order, L, tau, scale):
-        n, _ = orig(q, keys, values, order, L, tau, scale)
+    def f(q, keys, values, order, L, tau, scale, bias=None):
+        n, _ = orig(q, keys, values, order, L, tau, scale, bias)
         n2 = n - 1 if n < len(order) else n
-        return n2, O.sparse_attention(q, keys, values, list(order[:n2]), L, scale)
+        return n2, O.sparse_attention(q, keys, values, list(order[:n2]), L, scale, bias)
     O.early_stop_attention = f
 
 
@@ -90,7 +90,7 @@ def mut_eviction_forgets_old(O):
 
 def mut_attention_unscaled(O):
     orig = O.attend
-    O.attend = lambda q, K, V, scale: orig(q, K, V, 1.0)
+    O.attend = lambda q, K, V, scale, bias=None: orig(q, K, V, 1.0, bias)
 
 
 def mut_round_truncates(O):
@@ -209,13 +209,33 @@ def mut_window_skips_a_sub_block(O):
     O.block_scores_forecast_window = f
 
 
+def mut_bias_subtracted(O):
+    """The eviction logit lowers the token's weight instead of raising it."""
+    orig = O.attend
+
+    def f(q, K, V, scale, bias=None):
+        return orig(q, K, V, scale, None if bias is None else -np.asarray(bias))
+    O.attend = f
+
+
+def mut_bias_missing_from_stop_masses(O):
+    """The early-stop masses leave the bias out (the output keeps it)."""
+    orig = O.early_stop_attention
+
+    def f(q, keys, values, order, L, tau, scale, bias=None):
+        n, _ = orig(q, keys, values, order, L, tau, scale)
+        return n, O.sparse_attention(q, keys, values, list(order[:n]), L, scale, bias)
+    O.early_stop_attention = f
+
+
 MUTANTS = [mut_no_softmax, mut_max_before_head_sum, mut_ties_to_higher_id, mut_tail_dropped,
            mut_stop_block_excluded, mut_sub_block_shift, mut_eviction_forgets_old,
            mut_attention_unscaled, mut_round_truncates, mut_parts_overlap, mut_mean_by_15,
            mut_gamma_ignores_tail, mut_row_reps_from_previous_block,
            mut_row_eviction_from_previous_block, mut_row_prev_tail_off_by_one,
            mut_row_ordered_stop_ignored, mut_residency_ignores_tail,
-           mut_residency_swapped, mut_window_across_blocks, mut_window_skips_a_sub_block]
+           mut_residency_swapped, mut_window_across_blocks, mut_window_skips_a_sub_block,
+           mut_bias_subtracted, mut_bias_missing_from_stop_masses]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
