@@ -39,6 +39,7 @@ from ._abi import (  # noqa: F401
     nsa_select_blocks,
     nsa_select_workspace_bytes,
     nsa_sparse_decode,
+    nsa_sparse_decode_biased,
     nsa_status_string,
     nsa_update_block_reps,
 )

@@ -38,6 +38,7 @@ EXPORTS = (
     "nsa_select_blocks",
     "nsa_decode_workspace_bytes",
     "nsa_sparse_decode",
+    "nsa_sparse_decode_biased",
     "nsa_decode_step_workspace_bytes",
     "nsa_decode_step",
     "nsa_decode_step_noalloc",
@@ -132,6 +133,9 @@ def load() -> ctypes.CDLL:
     lib.nsa_sparse_decode.argtypes = [P(Shape), P(DecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
     lib.nsa_sparse_decode.restype = i32
+    lib.nsa_sparse_decode_biased.argtypes = [P(Shape), P(DecodeParams), vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.nsa_sparse_decode_biased.restype = i32
     lib.nsa_decode_step_workspace_bytes.argtypes = [P(Shape), P(SelectParams), i32, P(sz)]
     lib.nsa_decode_step_workspace_bytes.restype = i32
     lib.nsa_decode_step.argtypes = [P(Shape), P(SelectParams), vp, vp, vp, vp, vp, vp, vp, vp, i32,
@@ -242,6 +246,17 @@ def nsa_sparse_decode(shape: Shape, params: DecodeParams, q, k_pool, v_pool, blo
                                   _ptr(out), _ptr(workspace), int(workspace_bytes),
                                   _stream(stream))
     _check(st, "nsa_sparse_decode")
+
+
+def nsa_sparse_decode_biased(shape: Shape, params: DecodeParams, q, k_pool, v_pool, block_table,
+                             seq_lens, selected, num_selected, attn_bias, num_processed, out,
+                             workspace, workspace_bytes: int, stream=None) -> None:
+    st = load().nsa_sparse_decode_biased(ctypes.byref(shape), ctypes.byref(params), _ptr(q),
+                                         _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                         _ptr(seq_lens), _ptr(selected), _ptr(num_selected),
+                                         _ptr(attn_bias), _ptr(num_processed), _ptr(out),
+                                         _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check(st, "nsa_sparse_decode_biased")
 
 
 def nsa_decode_step_workspace_bytes(shape: Shape, params: SelectParams, max_seq_len: int) -> int:

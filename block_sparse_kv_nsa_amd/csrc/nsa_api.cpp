@@ -281,13 +281,13 @@ nsa_status nsa_decode_workspace_bytes(const nsa_shape* shape, const nsa_decode_p
   return ok();
 }
 
-nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* params,
-                             const void* q, const void* k_pool, const void* v_pool,
-                             const int32_t* block_table, const int32_t* seq_lens,
-                             const int32_t* selected, const int32_t* num_selected,
-                             int32_t* num_processed, void* out, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "nsa_sparse_decode";
+static nsa_status sparse_decode(const char* fn, const nsa_shape* shape,
+                                const nsa_decode_params* params, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* selected, const int32_t* num_selected,
+                                const float* attn_bias, int32_t* num_processed, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   nsa::DecodeLayout lay;
   if (nsa_status st = decode_layout_checked(fn, shape, params, &lay)) return st;
   NSA_REQUIRE_PTR(q, 16);
@@ -325,11 +325,38 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
   L.P = shape->num_phys_blocks;
   L.scale = scale_of(shape);
   L.tau = params->tau;
+  L.bias = attn_bias;
   L.lay = lay;
   if (env_trace())
     std::fprintf(stderr, "[nsa] decode rows=%d items=%d bpw=%d (0: by occupancy) G=%d D=%d "
-                 "early_stop=%d\n", lay.rows, lay.items_max, lay.bpw, L.G, L.D, L.early_stop);
+                 "early_stop=%d bias=%d\n", lay.rows, lay.items_max, lay.bpw, L.G, L.D,
+                 L.early_stop, attn_bias != nullptr);
   return launched(fn, nsa::launch_decode(L, stream));
+}
+
+nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* params,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* selected, const int32_t* num_selected,
+                             int32_t* num_processed, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return sparse_decode("nsa_sparse_decode", shape, params, q, k_pool, v_pool, block_table,
+                       seq_lens, selected, num_selected, nullptr, num_processed, out, workspace,
+                       workspace_bytes, stream);
+}
+
+nsa_status nsa_sparse_decode_biased(const nsa_shape* shape, const nsa_decode_params* params,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* selected, const int32_t* num_selected,
+                                    const float* attn_bias, int32_t* num_processed, void* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  const char* fn = "nsa_sparse_decode_biased";
+  NSA_REQUIRE_PTR(attn_bias, 4);
+  return sparse_decode(fn, shape, params, q, k_pool, v_pool, block_table, seq_lens, selected,
+                       num_selected, attn_bias, num_processed, out, workspace, workspace_bytes,
+                       stream);
 }
 
 static nsa_status step_layout_checked(const char* fn, const nsa_shape* shape,

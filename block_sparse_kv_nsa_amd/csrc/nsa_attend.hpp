@@ -36,18 +36,22 @@ struct Item {
   int64_t base;          // element offset of the (block, KV head) slab
   int valid;             // token rows in use (64, or the tail length)
   const float* logits;   // precomputed logits [G][64] (early-stop pass 2), else null
+  const float* bias = nullptr;  // the slab's 64 additive logits (natural log), if any
 };
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // One 64-token slab of K and V (this lane's pieces of it) with its item.
 template <typename T, int D>
 struct Slab {
   uint4 k[Quad<T, D>::NLD];
   uint4 v[VGeo<T, D>::NLV];
+  float b;  // this lane's token bias (BIAS builds only)
   Item it;
 };
 
 // Issue the loads of item itm into s, in the layouts attend_core consumes.
-template <typename T, int D, bool PRE>
+template <typename T, int D, bool PRE, bool BIAS = false>
 __device__ __forceinline__ void slab_issue(Slab<T, D>& s, const Item& itm, const T* kp,
                                            const T* vp) {
   using Q = Quad<T, D>;
@@ -58,6 +62,7 @@ __device__ __forceinline__ void slab_issue(Slab<T, D>& s, const Item& itm, const
   const int sl = lane % V::LPR, grp = lane / V::LPR;
   const int tk = wave * kSub + r;
   s.it = itm;
+  if constexpr (BIAS) s.b = itm.bias[tk];
   if constexpr (!PRE) {
 #pragma unroll
     for (int ld = 0; ld < Q::NLD; ++ld)
@@ -77,18 +82,19 @@ struct AttendSmem {
   float wacc[kWaves][G][D];
 };
 
-template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, bool BIAS, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                             ItemFn item, AttendSmem<T, D, G>& sm);
 
 // Accumulate items [i0, i1) (item(it) -> Item) and store the workgroup's
 // (m, l) and acc[D] per head at partial index pidx with agent-scope stores.
-// With PRE the logits come from Item::logits instead of q . k.
-template <typename T, int D, int G, bool PRE, typename ItemFn>
+// With PRE the logits come from Item::logits instead of q . k; with BIAS each
+// token's logit also gets Item::bias of the token (natural-log units).
+template <typename T, int D, int G, bool PRE, bool BIAS = false, typename ItemFn>
 __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                              ItemFn item, AttendSmem<T, D, G>& sm, __amdgpu_buffer_rsrc_t mlr,
                              __amdgpu_buffer_rsrc_t acr, int64_t pidx) {
-  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1)>(qrow, kp, vp, qscale, i0, i1, item, sm);
+  attend_core<T, D, G, PRE, (G < 8 ? 2 : 1), BIAS>(qrow, kp, vp, qscale, i0, i1, item, sm);
   for (int idx4 = threadIdx.x; idx4 < G * D / 4; idx4 += kThreads) {
     const int h = (idx4 * 4) / D, c = (idx4 * 4) % D;
     float M = sm.wm[0][h];
@@ -113,7 +119,7 @@ __device__ void attend_items(const T* qrow, const T* kp, const T* vp, float qsca
   }
 }
 
-template <typename T, int D, int G, bool PRE, int BUF, typename ItemFn>
+template <typename T, int D, int G, bool PRE, int BUF, bool BIAS, typename ItemFn>
 __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscale, int i0, int i1,
                             ItemFn item, AttendSmem<T, D, G>& sm) {
   using Q = Quad<T, D>;
@@ -147,8 +153,9 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
 #pragma unroll
   for (int kk = 0; kk < KEEP; ++kk) mref[kk] = -INFINITY;
 
-  auto issue = [&](int it, uint4 (&kx)[NLD], uint4 (&vx)[NLV], Item& itm) {
+  auto issue = [&](int it, uint4 (&kx)[NLD], uint4 (&vx)[NLV], Item& itm, float& bx) {
     itm = item(it);
+    if constexpr (BIAS) bx = itm.bias[tk];
     if constexpr (!PRE) {
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld)
@@ -159,7 +166,7 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
       vx[u] = load16_stream(vp + itm.base + (int64_t)(wave * kSub + u * TPL + grp) * D + sl * EPL);
   };
 
-  auto consume = [&](const Item& itm, const uint4 (&kx)[NLD], const uint4 (&vx)[NLV]) {
+  auto consume = [&](const Item& itm, const uint4 (&kx)[NLD], const uint4 (&vx)[NLV], float bx) {
     float lg[KEEP];
     if constexpr (!PRE) {
       float v[G];
@@ -171,6 +178,10 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     } else {
 #pragma unroll
       for (int kk = 0; kk < KEEP; ++kk) lg[kk] = itm.logits[(h0 + kk) * kBlock + tk];
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kk = 0; kk < KEEP; ++kk) lg[kk] = fmaf(bx, kLog2e, lg[kk]);
     }
     bool over = false;
 #pragma unroll
@@ -234,13 +245,14 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     // next slab's loads in flight while the current one is consumed
     uint4 ka[NLD], va[NLV], kb[NLD], vb[NLV];
     Item ia, ib;
-    if (i0 < i1) issue(i0, ka, va, ia);
+    float ba = 0.f, bb = 0.f;
+    if (i0 < i1) issue(i0, ka, va, ia, ba);
     for (int it = i0; it < i1; it += 2) {
-      if (it + 1 < i1) issue(it + 1, kb, vb, ib);
-      consume(ia, ka, va);
+      if (it + 1 < i1) issue(it + 1, kb, vb, ib, bb);
+      consume(ia, ka, va, ba);
       if (it + 1 < i1) {
-        if (it + 2 < i1) issue(it + 2, ka, va, ia);
-        consume(ib, kb, vb);
+        if (it + 2 < i1) issue(it + 2, ka, va, ia, ba);
+        consume(ib, kb, vb, bb);
       }
     }
   } else {
@@ -249,8 +261,9 @@ __device__ void attend_core(const T* qrow, const T* kp, const T* vp, float qscal
     for (int it = i0; it < i1; ++it) {
       uint4 ka[NLD], va[NLV];
       Item ia;
-      issue(it, ka, va, ia);
-      consume(ia, ka, va);
+      float ba = 0.f;
+      issue(it, ka, va, ia, ba);
+      consume(ia, ka, va, ba);
     }
   }
 
@@ -308,6 +321,7 @@ struct AttnState {
   // code (they would otherwise be hoisted into registers for the whole run).
   static constexpr int HB = (int)(128 / sizeof(QSlice<T, D>)) < 1 ? 1
                             : ((int)(128 / sizeof(QSlice<T, D>)) < G ? (int)(128 / sizeof(QSlice<T, D>)) : G);
+  template <bool BIAS = false>
   __device__ __forceinline__ void consume(const Slab<T, D>& s, AttendSmem<T, D, G>& sm,
                                           float qscale) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -332,7 +346,9 @@ struct AttnState {
     bool over = false;
 #pragma unroll
     for (int kk = 0; kk < KEEP; ++kk) {
-      lg[kk] = tk < s.it.valid ? v[kk] * qscale : -INFINITY;
+      float x = v[kk] * qscale;
+      if constexpr (BIAS) x = fmaf(s.b, kLog2e, x);
+      lg[kk] = tk < s.it.valid ? x : -INFINITY;
       over |= lg[kk] > mref[kk] + kLazyMax;
     }
     if (__any(over)) {  // wave-uniform: raise the reference, rescale

@@ -39,6 +39,7 @@ struct DecodeArgs {
   int32_t* num_processed;
   void* out;
   uint32_t* counters;
+  const float* bias;     // [B][Hkv][64 * max_blocks] additive logits, or null
   float* part_ml;        // [rows][splits][G][2]
   float* part_acc;       // [rows][splits][G][D]
   int Hkv, max_blocks, max_selected, items_max, bpw, P;
@@ -57,6 +58,9 @@ __device__ __forceinline__ Item item_at(const DecodeArgs& a, int row, int b, int
   x.base = (phys * a.Hkv + g) * (int64_t)(kBlock * D);
   x.valid = is_tail ? tail : kBlock;
   x.logits = nullptr;
+  x.bias = a.bias != nullptr
+               ? a.bias + (((int64_t)b * a.Hkv + g) * a.max_blocks + blk) * (int64_t)kBlock
+               : nullptr;
   *idx_out = it;
   return x;
 }
@@ -64,7 +68,7 @@ __device__ __forceinline__ Item item_at(const DecodeArgs& a, int row, int b, int
 // ---------------------------------------------------------------------------
 // split-K decode
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool BIAS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.Hkv, g = row % a.Hkv;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     int64_t idx;
     return item_at(a, row, b, g, it, nsel, nb, tail, D, &idx);
   };
-  attend_items<T, D, G, false>(qrow, static_cast<const T*>(a.k_pool),
+  attend_items<T, D, G, false, BIAS>(qrow, static_cast<const T*>(a.k_pool),
                                static_cast<const T*>(a.v_pool), a.qscale, i0, i1, item, sm, mlr,
                                acr, (int64_t)row * splits + split);
 
@@ -113,7 +117,7 @@ struct WalkSmem {
   float x[2][kWaves][G][3];  // by block parity: (m_w, Lw, block mass) per wave and head
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool BIAS>
 __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
     float mb[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) mb[h] = att.m[h];
-    att.consume(s, sm.att, a.qscale);
+    att.template consume<BIAS>(s, sm.att, a.qscale);
     // the wave's mass of this block per head (its 16 token rows, frame m_w)
     float mass[G];
 #pragma unroll
@@ -200,21 +204,21 @@ __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
     return stop;
   };
   Slab<T, D> sa, sb;
-  if (n_items > 0) slab_issue<T, D, false>(sa, item(0), kp, vp);
-  if (n_items > 1) slab_issue<T, D, false>(sb, item(1), kp, vp);
+  if (n_items > 0) slab_issue<T, D, false, BIAS>(sa, item(0), kp, vp);
+  if (n_items > 1) slab_issue<T, D, false, BIAS>(sb, item(1), kp, vp);
   int processed = nsel;  // listed blocks attended
   for (int it = 0; it < n_items; it += 2) {
     if (step(sa, it)) {
       processed = tail > 0 ? it : it + 1;
       break;
     }
-    if (it + 2 < n_items) slab_issue<T, D, false>(sa, item(it + 2), kp, vp);
+    if (it + 2 < n_items) slab_issue<T, D, false, BIAS>(sa, item(it + 2), kp, vp);
     if (it + 1 < n_items) {
       if (step(sb, it + 1)) {
         processed = tail > 0 ? it + 1 : it + 2;
         break;
       }
-      if (it + 3 < n_items) slab_issue<T, D, false>(sb, item(it + 3), kp, vp);
+      if (it + 3 < n_items) slab_issue<T, D, false, BIAS>(sb, item(it + 3), kp, vp);
     }
   }
   att.to_lds(sm.att);
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) a.num_processed[row] = processed;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool BIAS>
 hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   const DecodeLayout& lay = L.lay;
   DecodeArgs a{};
@@ -265,31 +269,37 @@ hipError_t launch_t(const DecodeLaunch& L, hipStream_t stream) {
   a.items_max = lay.items_max;
   a.qscale = L.scale * 1.4426950408889634f;  // natural -> base-2 logits
   a.tau = L.tau;
+  a.bias = L.bias;
   if (L.early_stop) {
-    es_walk_kernel<T, D, G><<<lay.rows, kThreads, 0, stream>>>(a);
+    es_walk_kernel<T, D, G, BIAS><<<lay.rows, kThreads, 0, stream>>>(a);
     return hipGetLastError();
   }
   int bpw = lay.bpw;
   if (bpw <= 0) {
     GridInfo gi;
     const hipError_t e =
-        grid_info(reinterpret_cast<const void*>(decode_kernel<T, D, G>), kThreads, 0, &gi);
+        grid_info(reinterpret_cast<const void*>(decode_kernel<T, D, G, BIAS>), kThreads, 0, &gi);
     if (e != hipSuccess) return e;
     bpw = balanced_blocks_per_split(lay.rows, lay.items_max, gi.per_cu * gi.cus);
   }
   a.bpw = bpw;
   dim3 grid((lay.items_max + bpw - 1) / bpw, lay.rows);
-  decode_kernel<T, D, G><<<grid, kThreads, 0, stream>>>(a);
+  decode_kernel<T, D, G, BIAS><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t by_bias(const DecodeLaunch& L, hipStream_t s) {
+  return L.bias != nullptr ? launch_t<T, D, G, true>(L, s) : launch_t<T, D, G, false>(L, s);
 }
 
 template <typename T, int D>
 hipError_t by_group(const DecodeLaunch& L, hipStream_t s) {
   switch (L.G) {
-    case 1: return launch_t<T, D, 1>(L, s);
-    case 2: return launch_t<T, D, 2>(L, s);
-    case 4: return launch_t<T, D, 4>(L, s);
-    default: return launch_t<T, D, 8>(L, s);
+    case 1: return by_bias<T, D, 1>(L, s);
+    case 2: return by_bias<T, D, 2>(L, s);
+    case 4: return by_bias<T, D, 4>(L, s);
+    default: return by_bias<T, D, 8>(L, s);
   }
 }
 

@@ -159,6 +159,7 @@ struct DecodeLaunch {
   int32_t* num_processed;
   void* out;
   void* workspace;
+  const float* bias;  // per-token additive logits, or null
   int B, Hkv, max_blocks, max_selected, early_stop, P;
   float scale, tau;
   DecodeLayout lay;

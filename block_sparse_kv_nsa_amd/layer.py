@@ -90,7 +90,10 @@ class SparseDecodeLayer:
                             stream)
 
     def decode(self, q: torch.Tensor, stream=None, selected=None, num_selected=None,
-               max_selected=None, early_stop=None) -> None:
+               max_selected=None, early_stop=None, bias=None) -> None:
+        """Attention over the selected blocks and the tail.  bias: None, or
+        the per-token additive logits [B][Hkv][64 * max_blocks] float32
+        (the eviction logits, ED-DMA variant: nsa_sparse_decode_biased)."""
         params = self.dec_params
         if max_selected is not None or early_stop is not None:
             params = A.DecodeParams(max_selected or self.k,
@@ -100,10 +103,17 @@ class SparseDecodeLayer:
             if need > self.dec_ws_bytes:
                 self.dec_ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
                 self.dec_ws_bytes = need
+        sel = self.selected if selected is None else selected
+        nsel = self.num_selected if num_selected is None else num_selected
+        if bias is not None:
+            A.nsa_sparse_decode_biased(self.shape, params, q, self.k_pool, self.v_pool,
+                                       self.block_table, self.seq_lens, sel, nsel, bias,
+                                       self.num_processed, self.out, self.dec_ws,
+                                       self.dec_ws_bytes, stream)
+            return
         A.nsa_sparse_decode(self.shape, params, q, self.k_pool, self.v_pool, self.block_table,
-                            self.seq_lens, self.selected if selected is None else selected,
-                            self.num_selected if num_selected is None else num_selected,
-                            self.num_processed, self.out, self.dec_ws, self.dec_ws_bytes, stream)
+                            self.seq_lens, sel, nsel, self.num_processed, self.out, self.dec_ws,
+                            self.dec_ws_bytes, stream)
 
     def step(self, query: torch.Tensor, q: torch.Tensor, max_seq_len: int, stream=None) -> None:
         """Selection and decode in one launch (ascending mode).  Enqueues only:

@@ -9,7 +9,8 @@
  *   nsa_select_blocks       score every full block against the current query
  *                           and pick the blocks to attend
  *   nsa_sparse_decode       attention over the picked blocks plus the partial
- *                           last block
+ *                           last block (nsa_sparse_decode_biased: with the
+ *                           eviction logits inside the softmax)
  *
  * Sources for the operations (web pages on the method):
  *   - NOSA technical summary (gist.science/es/paper/2510.13602),
@@ -226,6 +227,25 @@ nsa_status nsa_sparse_decode(const nsa_shape* shape, const nsa_decode_params* pa
                              const int32_t* selected, const int32_t* num_selected,
                              int32_t* num_processed, void* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* nsa_sparse_decode with the eviction logits inside the attention softmax.
+ * NOSA summary, "ED-DMA": the eviction head selects on pre-exponential
+ * scores and defers its exponential to the attention stage.  Read as: token
+ * t of row (b, g) weighs exp(attn_bias[b][g][t]) times its plain weight,
+ *   out[b][h] = sum_t softmax_t(q_h . k_t * scale + attn_bias[b][g][t]) v_t,
+ * and the early-stop masses take the same logits.
+ *
+ *   attn_bias   [B][Hkv][64*max_blocks_per_seq] float32, natural-log units,
+ *               logical token order (the evict_logits of
+ *               nsa_update_block_reps); not NULL, 4-byte aligned
+ * Everything else as nsa_sparse_decode, whose errors it returns. */
+nsa_status nsa_sparse_decode_biased(const nsa_shape* shape, const nsa_decode_params* params,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* selected, const int32_t* num_selected,
+                                    const float* attn_bias, int32_t* num_processed, void* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * Fused step -- nsa_select_blocks followed by nsa_sparse_decode in one launch

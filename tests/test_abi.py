@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
@@ -125,6 +125,17 @@ def test_decode_validation():
     small = list(args)
     small[12] = 0
     expect(N.NSA_ERR_WORKSPACE_TOO_SMALL, N.nsa_sparse_decode, *small)
+    # the biased form: the bias after num_selected, required and 4-byte aligned
+    biased = args[:9] + [FAKE] + args[9:]
+    nobias = list(biased)
+    nobias[9] = None
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_sparse_decode_biased, *nobias)
+    odd = list(biased)
+    odd[9] = FAKE + 2
+    expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_sparse_decode_biased, *odd)
+    small = list(biased)
+    small[13] = 0
+    expect(N.NSA_ERR_WORKSPACE_TOO_SMALL, N.nsa_sparse_decode_biased, *small)
 
 
 def test_reps_validation_and_noop():
