@@ -21,6 +21,10 @@
 // block whether every head's mass in it fell below tau times the mass
 // accumulated so far; it stops there.  Keys and values are read only up to
 // the stopping block and the two slabs in flight behind it.
+//
+// ED-DMA variant (NOSA summary, "ED-DMA", read as the eviction head's
+// exponential applied inside the attention): the BIAS kernels add each
+// token's eviction logit to its attention logit, loaded with the slab.
 #include "nsa_attend.hpp"
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"

@@ -12,6 +12,10 @@
  *                           last block (nsa_sparse_decode_biased: with the
  *                           eviction logits inside the softmax)
  *
+ * nsa_decode_step does the last two in one launch (and
+ * nsa_decode_step_noalloc without a workspace); nsa_residency_diff reports
+ * the blocks to fetch and release between consecutive selections.
+ *
  * Sources for the operations (web pages on the method):
  *   - NOSA technical summary (gist.science/es/paper/2510.13602),
  *     "Metodologia / 1. Algoritmo: NOSA" (two-part selection, strict
@@ -20,7 +24,8 @@
  *     needed).
  *   - SparDA technical summary (gist.science/de/paper/2606.04511),
  *     "Kompakter Forecast-Indexer" (one forecast vector per KV head, no
- *     per-head loop, no softmax).
+ *     per-head loop, no softmax) and "Trainingsstrategie" (the inference
+ *     window of 32 tokens with stride 16).
  *   - S2O technical summary (gist.science/it/paper/2602.22575),
  *     "1. Permutazione Online" (keep the physical layout, gather through
  *     index arrays), "2. Regola di Arresto Anticipato" and
@@ -32,7 +37,9 @@
  *     are g*G .. g*G+G-1 with G = num_q_heads / num_kv_heads.
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
  *     the struct pointers (host) and `bytes` outputs (host).  The library
- *     allocates, frees and retains nothing.
+ *     allocates and frees nothing; it keeps only a small host table of each
+ *     kernel's resident workgroups per device and, for
+ *     nsa_decode_step_noalloc, one static device array per device.
  *   - Every call only enqueues kernels on `stream` (NULL = the default
  *     stream); nothing synchronises the host, so a step can be captured in a
  *     HIP graph.  Calls on distinct workspaces may run concurrently.
