@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(SelectArgs a) {
   const int b = row / a.Hkv, g = row % a.Hkv;
   // blocks past the host bound max_seq_len/64 are ignored (no out-of-range
   // workspace writes if a caller understates the bound)
-  const int nb = min(a.seq_lens[b] / kBlock, a.nb_max);
+  const int nb =
+      min(dbg_clamp(a.seq_lens[b], 0, kBlock * a.max_blocks + 1, kDbgSeqLen) / kBlock, a.nb_max);
   const int nsub = nb * kSubs;
   const int j0 = chunk * a.chunk_reps;
   const int j1 = min(j0 + a.chunk_reps, nsub);
@@ -197,7 +198,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   const int wave = threadIdx.x / kWave;
   const int row = blockIdx.y, chunk = blockIdx.x, chunks = gridDim.x;
   const int b = row / a.Hkv;
-  const int nb = min(a.seq_lens[b] / kBlock, a.nb_max);
+  const int nb =
+      min(dbg_clamp(a.seq_lens[b], 0, kBlock * a.max_blocks + 1, kDbgSeqLen) / kBlock, a.nb_max);
   const int cbs = a.chunk_reps / kSubs;  // blocks per chunk
   const int blk0 = min(chunk * cbs, nb);
   const int nblk = min(blk0 + cbs, nb) - blk0;
