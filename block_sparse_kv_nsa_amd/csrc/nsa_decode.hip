@@ -20,7 +20,7 @@
 // then walks the ordered list one block at a time and decides after each
 // block whether every head's mass in it fell below tau times the mass
 // accumulated so far; it stops there.  Keys and values are read only up to
-// the stopping block and the two slabs in flight behind it.
+// the stopping block and the slabs in flight behind it.
 //
 // ED-DMA variant (NOSA summary, "ED-DMA", read as the eviction head's
 // exponential applied inside the attention): the BIAS kernels add each
@@ -115,6 +115,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // its mass of the block) per head in shared memory; with F = max m_w the
 // row's accumulated mass is A = sum Lw 2^(m_w - F) and the block's mass
 // M = sum mass_w 2^(m_w - F) (the frame cancels in M / A).
+constexpr int kWalkSlabs = 3;
+
 template <typename T, int D, int G>
 struct WalkSmem {
   AttendSmem<T, D, G> att;
@@ -207,22 +209,26 @@ __global__ __launch_bounds__(kThreads) void es_walk_kernel(DecodeArgs a) {
     }
     return stop;
   };
-  Slab<T, D> sa, sb;
-  if (n_items > 0) slab_issue<T, D, false, BIAS>(sa, item(0), kp, vp);
-  if (n_items > 1) slab_issue<T, D, false, BIAS>(sb, item(1), kp, vp);
+  // kWalkSlabs slabs in flight: the next ones are requested before a
+  // block's decision (three measured faster than two; four need too many
+  // registers)
+  Slab<T, D> sl[kWalkSlabs];
+#pragma unroll
+  for (int i = 0; i < kWalkSlabs; ++i)
+    if (i < n_items) slab_issue<T, D, false, BIAS>(sl[i], item(i), kp, vp);
   int processed = nsel;  // listed blocks attended
-  for (int it = 0; it < n_items; it += 2) {
-    if (step(sa, it)) {
-      processed = tail > 0 ? it : it + 1;
-      break;
-    }
-    if (it + 2 < n_items) slab_issue<T, D, false, BIAS>(sa, item(it + 2), kp, vp);
-    if (it + 1 < n_items) {
-      if (step(sb, it + 1)) {
-        processed = tail > 0 ? it + 1 : it + 2;
-        break;
+  bool stopped = false;
+  for (int it = 0; it < n_items && !stopped; it += kWalkSlabs) {
+#pragma unroll
+    for (int i = 0; i < kWalkSlabs; ++i) {
+      if (!stopped && it + i < n_items) {  // uniform
+        if (step(sl[i], it + i)) {
+          processed = tail > 0 ? it + i : it + i + 1;
+          stopped = true;
+        } else if (it + i + kWalkSlabs < n_items) {
+          slab_issue<T, D, false, BIAS>(sl[i], item(it + i + kWalkSlabs), kp, vp);
+        }
       }
-      if (it + 3 < n_items) slab_issue<T, D, false, BIAS>(sb, item(it + 3), kp, vp);
     }
   }
   att.to_lds(sm.att);
