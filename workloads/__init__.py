@@ -26,3 +26,13 @@ from .synth import (  # noqa: F401
     storage_dtype,
     stored_to_f64,
 )
+from .prefill import (  # noqa: F401
+    PREFILL_CONFIGS,
+    PrefillBatch,
+    PrefillConfig,
+    build_prefill,
+    kv_row,
+    prefill_config,
+    prefill_table,
+    q_row,
+)
