@@ -21,6 +21,7 @@ from ._abi import (  # noqa: F401
     NSA_SCORE_GROUP_SOFTMAX,
     DecodeParams,
     NsaError,
+    PrefillParams,
     SelectParams,
     Shape,
     StepGrid,
@@ -36,6 +37,9 @@ from ._abi import (  # noqa: F401
     nsa_decode_workspace_bytes,
     nsa_last_error,
     nsa_residency_diff,
+    nsa_s2o_attend,
+    nsa_s2o_index,
+    nsa_s2o_workspace_bytes,
     nsa_select_blocks,
     nsa_select_workspace_bytes,
     nsa_sparse_decode,

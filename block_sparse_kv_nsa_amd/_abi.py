@@ -45,6 +45,9 @@ EXPORTS = (
     "nsa_decode_step_status",
     "nsa_decode_step_grid",
     "nsa_residency_diff",
+    "nsa_s2o_workspace_bytes",
+    "nsa_s2o_index",
+    "nsa_s2o_attend",
     "nsa_debug_checks",
     "nsa_debug_error",
     "nsa_status_string",
@@ -107,6 +110,14 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("segment", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -148,6 +159,13 @@ def load() -> ctypes.CDLL:
     lib.nsa_decode_step_status.restype = i32
     lib.nsa_residency_diff.argtypes = [P(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.nsa_residency_diff.restype = i32
+    lib.nsa_s2o_workspace_bytes.argtypes = [P(Shape), P(PrefillParams), P(sz)]
+    lib.nsa_s2o_workspace_bytes.restype = i32
+    lib.nsa_s2o_index.argtypes = [P(Shape), P(PrefillParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nsa_s2o_index.restype = i32
+    lib.nsa_s2o_attend.argtypes = [P(Shape), P(PrefillParams), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp]
+    lib.nsa_s2o_attend.restype = i32
     lib.nsa_decode_step_grid.argtypes = [P(Shape), P(SelectParams), i32, i32, P(StepGrid)]
     lib.nsa_decode_step_grid.restype = i32
     lib.nsa_debug_checks.argtypes = []
@@ -298,6 +316,30 @@ def nsa_residency_diff(shape: Shape, max_selected: int, prev_selected, prev_num_
                                    _ptr(release), _ptr(num_release), _ptr(gamma),
                                    _stream(stream))
     _check(st, "nsa_residency_diff")
+
+
+def nsa_s2o_workspace_bytes(shape: Shape, params: PrefillParams) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().nsa_s2o_workspace_bytes(ctypes.byref(shape), ctypes.byref(params),
+                                        ctypes.byref(out))
+    _check(st, "nsa_s2o_workspace_bytes")
+    return out.value
+
+
+def nsa_s2o_index(shape: Shape, params: PrefillParams, q, k_pool, block_table, seq_lens, q_perm,
+                  kv_perm, workspace, workspace_bytes: int, stream=None) -> None:
+    st = load().nsa_s2o_index(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_pool),
+                              _ptr(block_table), _ptr(seq_lens), _ptr(q_perm), _ptr(kv_perm),
+                              _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check(st, "nsa_s2o_index")
+
+
+def nsa_s2o_attend(shape: Shape, params: PrefillParams, q, k_pool, v_pool, block_table, seq_lens,
+                   q_perm, kv_perm, out, num_tiles, stream=None) -> None:
+    st = load().nsa_s2o_attend(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_pool),
+                               _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(q_perm),
+                               _ptr(kv_perm), _ptr(out), _ptr(num_tiles), _stream(stream))
+    _check(st, "nsa_s2o_attend")
 
 
 def nsa_decode_step_noalloc(shape: Shape, params: SelectParams, query, q, reps, evict_block_score,

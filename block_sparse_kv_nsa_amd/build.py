@@ -27,7 +27,7 @@ LIB = os.path.join(PKG, "libnsa.so")
 LIB_CHECKS = os.path.join(PKG, "libnsa_checks.so")
 
 SOURCES = ["nsa_api.cpp", "nsa_reps.hip", "nsa_select.hip", "nsa_decode.hip", "nsa_step.hip",
-           "nsa_residency.hip"]
+           "nsa_residency.hip", "nsa_prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -559,6 +559,122 @@ nsa_status nsa_residency_diff(const nsa_shape* shape, int32_t max_selected,
   return launched(fn, nsa::launch_residency(L, stream));
 }
 
+static nsa_status prefill_checked(const char* fn, const nsa_shape* shape,
+                                  const nsa_prefill_params* params, nsa::PrefillLayout* lay) {
+  if (nsa_status st = check_shape(fn, shape)) return st;
+  if (shape->dtype != NSA_BF16)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: S2O prefill is built for bf16 only", fn);
+  if (params == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: params is NULL", fn);
+  if (params->segment < 64 || params->segment > 4096 || params->segment % 64 != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: segment %d must be a multiple of 64 in [64, 4096]",
+                fn, params->segment);
+  if (params->max_seq_len < 64 || params->max_seq_len % 64 != 0 ||
+      params->max_seq_len > 64 * shape->max_blocks_per_seq)
+    return fail(NSA_ERR_INVALID_ARGUMENT,
+                "%s: max_seq_len %d must be a multiple of 64 in [64, 64 * max_blocks_per_seq]", fn,
+                params->max_seq_len);
+  if (!(params->tau >= 0.f) || std::isinf(params->tau))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "%s: tau must be finite and >= 0", fn);
+  *lay = nsa::prefill_layout(shape->batch, shape->num_q_heads, shape->num_kv_heads,
+                             shape->head_dim, params->segment, params->max_seq_len, 0);
+  if (lay->items >= ((size_t)1 << 31))
+    return fail(NSA_ERR_UNSUPPORTED,
+                "%s: batch * num_q_heads * segments * max_seq_len = %zu history entries "
+                "(at most 2^31 - 1)", fn, lay->items);
+  return NSA_OK;
+}
+
+nsa_status nsa_s2o_workspace_bytes(const nsa_shape* shape, const nsa_prefill_params* params,
+                                   size_t* bytes) {
+  const char* fn = "nsa_s2o_workspace_bytes";
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  nsa::PrefillLayout lay;
+  if (nsa_status st = prefill_checked(fn, shape, params, &lay)) return st;
+  size_t sort_bytes = 0;
+  if (hipError_t e = nsa::prefill_sort_bytes(lay, &sort_bytes))
+    return fail(NSA_ERR_HIP, "%s: sizing the segmented sort: %s", fn, hipGetErrorString(e));
+  lay = nsa::prefill_layout(lay.B, lay.Hq, lay.Hkv, lay.D, lay.seg, lay.max_len, sort_bytes);
+  *bytes = lay.bytes;
+  return ok();
+}
+
+nsa_status nsa_s2o_index(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
+                         const void* k_pool, const int32_t* block_table, const int32_t* seq_lens,
+                         int32_t* q_perm, int32_t* kv_perm, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "nsa_s2o_index";
+  nsa::PrefillLayout lay;
+  if (nsa_status st = prefill_checked(fn, shape, params, &lay)) return st;
+  NSA_REQUIRE_PTR(q, 16);
+  NSA_REQUIRE_PTR(k_pool, 16);
+  NSA_REQUIRE_PTR(block_table, 4);
+  NSA_REQUIRE_PTR(seq_lens, 4);
+  NSA_REQUIRE_PTR(q_perm, 4);
+  NSA_REQUIRE_PTR(kv_perm, 4);
+  NSA_REQUIRE_PTR(workspace, 256);
+  size_t sort_bytes = 0;
+  if (hipError_t e = nsa::prefill_sort_bytes(lay, &sort_bytes))
+    return fail(NSA_ERR_HIP, "%s: sizing the segmented sort: %s", fn, hipGetErrorString(e));
+  lay = nsa::prefill_layout(lay.B, lay.Hq, lay.Hkv, lay.D, lay.seg, lay.max_len, sort_bytes);
+  if (workspace_bytes < lay.bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, lay.bytes);
+  nsa::PrefillLaunch L{};
+  L.D = shape->head_dim;
+  L.G = shape->num_q_heads / shape->num_kv_heads;
+  L.q = q;
+  L.k_pool = k_pool;
+  L.table = block_table;
+  L.seq_lens = seq_lens;
+  L.q_perm = q_perm;
+  L.kv_perm = kv_perm;
+  L.workspace = workspace;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.P = shape->num_phys_blocks;
+  L.lay = lay;
+  if (env_trace())
+    std::fprintf(stderr, "[nsa] s2o index B=%d Hq=%d Hkv=%d D=%d seg=%d max_len=%d nseg=%d "
+                 "sort=%zu bytes\n", lay.B, lay.Hq, lay.Hkv, lay.D, lay.seg, lay.max_len, lay.nseg,
+                 sort_bytes);
+  return launched(fn, nsa::launch_prefill_index(L, stream));
+}
+
+nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* q_perm, const int32_t* kv_perm,
+                          void* out, int32_t* num_tiles, hipStream_t stream) {
+  const char* fn = "nsa_s2o_attend";
+  nsa::PrefillLayout lay;
+  if (nsa_status st = prefill_checked(fn, shape, params, &lay)) return st;
+  NSA_REQUIRE_PTR(q, 16);
+  NSA_REQUIRE_PTR(k_pool, 16);
+  NSA_REQUIRE_PTR(v_pool, 16);
+  NSA_REQUIRE_PTR(block_table, 4);
+  NSA_REQUIRE_PTR(seq_lens, 4);
+  NSA_REQUIRE_PTR(q_perm, 4);
+  NSA_REQUIRE_PTR(kv_perm, 4);
+  NSA_REQUIRE_PTR(out, 16);
+  NSA_REQUIRE_PTR(num_tiles, 4);
+  nsa::PrefillLaunch L{};
+  L.D = shape->head_dim;
+  L.G = shape->num_q_heads / shape->num_kv_heads;
+  L.q = q;
+  L.k_pool = k_pool;
+  L.v_pool = v_pool;
+  L.table = block_table;
+  L.seq_lens = seq_lens;
+  L.q_perm_in = q_perm;
+  L.kv_perm_in = kv_perm;
+  L.out = out;
+  L.num_tiles = num_tiles;
+  L.max_blocks = shape->max_blocks_per_seq;
+  L.P = shape->num_phys_blocks;
+  L.scale = scale_of(shape);
+  L.tau = params->tau;
+  L.lay = lay;
+  return launched(fn, nsa::launch_prefill_attend(L, stream));
+}
+
 nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32_t clear,
                                   hipStream_t stream) {
   const char* fn = "nsa_decode_step_status";
@@ -595,7 +711,8 @@ nsa_status nsa_debug_error(uint32_t* bits, int32_t clear) {
   *bits = 0;
   if (!nsa_debug_checks()) return ok();
   hipError_t (*const words[])(uint32_t*, bool) = {nsa::debug_word_reps, nsa::debug_word_select,
-                                                  nsa::debug_word_decode, nsa::debug_word_step};
+                                                  nsa::debug_word_decode, nsa::debug_word_step,
+                                                  nsa::debug_word_prefill};
   for (auto word : words) {
     uint32_t w = 0;
     const hipError_t e = word(&w, clear != 0);

@@ -325,4 +325,71 @@ hipError_t debug_word_select(uint32_t* out, bool clear);
 hipError_t debug_word_decode(uint32_t* out, bool clear);
 hipError_t debug_word_step(uint32_t* out, bool clear);
 
+// ---------------------------------------------------------------------------
+// S2O prefill.  Index step workspace:
+//   [segment key sums (float64) | guide vectors | representative queries |
+//    segment begin offsets | segment end offsets | history score keys (in) |
+//    history score keys (sorted) | the segmented sort's own storage]
+// Every list is indexed by segment (b, query head h, segment s), or by
+// (b, KV head g, segment s) for the key sums and guide vectors; the history
+// keys of segment i occupy [i * max_seq_len, i * max_seq_len + s * seg).
+// ---------------------------------------------------------------------------
+struct PrefillLayout {
+  int B, Hq, Hkv, D, seg, max_len, nseg;
+  size_t segs;   // B * Hq * nseg
+  size_t items;  // segs * max_len
+  size_t off_keysum, off_guide, off_rep, off_begin, off_end, off_kin, off_kout, off_sort,
+      sort_bytes, bytes;
+};
+
+inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int D, int seg, int max_len,
+                                    size_t sort_bytes) {
+  PrefillLayout s{};
+  s.B = B;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.D = D;
+  s.seg = seg;
+  s.max_len = max_len;
+  s.nseg = (max_len + seg - 1) / seg;
+  s.segs = (size_t)B * Hq * s.nseg;
+  s.items = s.segs * (size_t)max_len;
+  const size_t kv_rows = (size_t)B * Hkv * s.nseg;
+  s.off_keysum = 0;
+  s.off_guide = round_up(s.off_keysum + kv_rows * D * 8, 256);
+  s.off_rep = round_up(s.off_guide + kv_rows * D * 2, 256);
+  s.off_begin = round_up(s.off_rep + s.segs * D * 2, 256);
+  s.off_end = round_up(s.off_begin + s.segs * 4, 256);
+  s.off_kin = round_up(s.off_end + s.segs * 4, 256);
+  s.off_kout = round_up(s.off_kin + s.items * 4, 256);
+  s.off_sort = round_up(s.off_kout + s.items * 4, 256);
+  s.sort_bytes = sort_bytes;
+  s.bytes = round_up(s.off_sort + sort_bytes, 256);
+  return s;
+}
+
+struct PrefillLaunch {
+  int D, G;
+  const void* q;        // [B][Hq][max_len][D] bf16
+  const void* k_pool;   // [P][Hkv][64][D] bf16
+  const void* v_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  int32_t* q_perm;      // [B][Hq][nseg][seg]
+  int32_t* kv_perm;     // [B][Hq][nseg][max_len]
+  const int32_t* q_perm_in;
+  const int32_t* kv_perm_in;
+  void* out;            // [B][Hq][max_len][D] bf16
+  int32_t* num_tiles;   // [B][Hq][nseg][seg / 64]
+  void* workspace;
+  int max_blocks, P;
+  float scale, tau;
+  PrefillLayout lay;
+};
+// Bytes of the segmented sort's own storage for a layout (asks the device).
+hipError_t prefill_sort_bytes(const PrefillLayout& lay, size_t* bytes);
+hipError_t launch_prefill_index(const PrefillLaunch& L, hipStream_t stream);
+hipError_t launch_prefill_attend(const PrefillLaunch& L, hipStream_t stream);
+hipError_t debug_word_prefill(uint32_t* out, bool clear);
+
 }  // namespace nsa

@@ -1,0 +1,602 @@
+// S2O prefill attention on gfx950: segment orders by index, then a two-pass
+// attention on the matrix cores that gathers its tiles through those orders.
+//
+// S2O technical summary (gist.science, Italian):
+//  * "1. Permutazione Online tramite Caricamento Guidato da Indici": per
+//    segment, the queries are ordered by their score against one shared guide
+//    vector (the mean key of the history before the segment) and the history
+//    tokens by their score against one representative query (the mean query
+//    of the segment); tiles are then gathered by index, nothing is moved.
+//  * "2. Regola di Arresto Anticipato": history tiles are walked in that
+//    order until a tile's attention mass falls below tau times the mass
+//    accumulated so far, for every query of the query tile.
+//  * "3. Implementazione del Kernel": pass 1 attends densely and causally
+//    inside the segment and seeds (m, l, acc); pass 2 resumes over the
+//    permuted history with the early stop.
+//
+// Index step (nsa_s2o_index): s2o_sums_kernel (mean query of each segment,
+// key sums of each segment, float64), s2o_guide_kernel (prefix means of the
+// key sums: the guide vectors; sort segment offsets), s2o_qorder_kernel
+// (query scores against the guide, bitonic sort of up to 4096 entries in
+// shared memory), s2o_kvscore_kernel (every history token against every
+// later segment's representative query on the matrix cores, as sort keys),
+// then a segmented radix sort of the keys per (sequence, head, segment)
+// (rocPRIM; stable, so equal scores keep ascending token order).
+//
+// Attention (nsa_s2o_attend): s2o_attend_kernel, one workgroup per tile of
+// 64 permuted queries.  Each wave holds 16 queries as the B operand of
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16): the output puts one query per lane
+// column, so softmax statistics stay per lane and P^T feeds the V^T P^T
+// product without a transpose.  K tiles sit in shared memory row-major
+// (rows padded by 16 bytes), V tiles transposed with a 4-key-group swizzle
+// so that both the stores and the 8-byte operand reads are free of bank
+// conflicts.  The next tile's K/V are loaded into registers while the
+// current one is computed.
+#include <hip/hip_runtime.h>
+
+#include <rocprim/device/device_segmented_radix_sort.hpp>
+#include <rocprim/iterator/counting_iterator.hpp>
+#include <rocprim/iterator/transform_iterator.hpp>
+
+#include "nsa_device.hpp"
+#include "nsa_internal.hpp"
+
+namespace nsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTile = 64;       // queries per query tile, tokens per history tile
+constexpr int kMaxSegSort = 4096;
+
+struct IndexArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  int32_t* q_perm;
+  double* keysum;
+  uint16_t* guide;
+  uint16_t* rep;
+  uint32_t* begin;
+  uint32_t* end;
+  uint32_t* kin;
+  int B, Hq, Hkv, G, seg, max_len, nseg, max_blocks, P;
+};
+
+__device__ __forceinline__ int seq_len_of(const int32_t* seq_lens, int b, int max_len) {
+  return dbg_clamp(seq_lens[b], 0, max_len + 1, kDbgSeqLen);
+}
+
+// Row of token t of sequence b in KV head g of a pool.
+template <int D>
+__device__ __forceinline__ const uint16_t* token_row(const uint16_t* pool, const int32_t* table,
+                                                     int b, int g, int t, int Hkv, int max_blocks,
+                                                     int P) {
+  const int slot = dbg_clamp(table[(int64_t)b * max_blocks + (t >> 6)], 0, P, kDbgTable);
+  return pool + (((int64_t)slot * Hkv + g) * kBlock + (t & 63)) * D;
+}
+
+__device__ __forceinline__ void add_bf16x8(double (&acc)[8], const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] += (double)bf16_lo(w[e]);
+    acc[2 * e + 1] += (double)bf16_hi(w[e]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float64 sums of a segment's rows: its queries (-> representative query) or
+// its keys (-> key sums, prefix-summed into guide vectors).  grid (nseg,
+// B*Hq + B*Hkv).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void s2o_sums_kernel(IndexArgs a) {
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int RPI = kThreads / CPR;    // rows per pass
+  __shared__ double red[RPI][D];
+  const int s = blockIdx.x, y = blockIdx.y;
+  const bool is_q = y < a.B * a.Hq;
+  const int b = is_q ? y / a.Hq : (y - a.B * a.Hq) / a.Hkv;
+  const int head = is_q ? y % a.Hq : (y - a.B * a.Hq) % a.Hkv;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int t0 = s * a.seg;
+  if (t0 >= L) return;
+  const int n = min(a.seg, L - t0);
+  const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0; r < n; r += RPI) {
+    const uint16_t* row =
+        is_q ? a.q + (((int64_t)b * a.Hq + head) * a.max_len + t0 + r) * D
+             : token_row<D>(a.k_pool, a.table, b, head, t0 + r, a.Hkv, a.max_blocks, a.P);
+    add_bf16x8(acc, load16(row + c * 8));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r0][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double tot = 0;
+    for (int r = 0; r < RPI; ++r) tot += red[r][d];
+    if (is_q) {
+      a.rep[(((int64_t)b * a.Hq + head) * a.nseg + s) * D + d] = f64_to_bf16(tot / (double)n);
+    } else {
+      a.keysum[(((int64_t)b * a.Hkv + head) * a.nseg + s) * D + d] = tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Guide vectors (stored mean key of each segment's history) and the sort's
+// segment offsets.  grid (B*Hkv).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void s2o_guide_kernel(IndexArgs a) {
+  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int nseg_b = (L + a.seg - 1) / a.seg;
+  const int64_t kv_row = (int64_t)b * a.Hkv + g;
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double pre = 0;
+    for (int s = 0; s < nseg_b; ++s) {
+      const int64_t i = (kv_row * a.nseg + s) * D + d;
+      a.guide[i] = s == 0 ? (uint16_t)0 : f64_to_bf16(pre / (double)((int64_t)s * a.seg));
+      pre += a.keysum[i];
+    }
+  }
+  for (int i = threadIdx.x; i < a.G * a.nseg; i += kThreads) {
+    const int h = g * a.G + i / a.nseg, s = i % a.nseg;
+    const size_t idx = ((size_t)b * a.Hq + h) * a.nseg + s;
+    const uint32_t beg = (uint32_t)(idx * (size_t)a.max_len);
+    a.begin[idx] = beg;
+    a.end[idx] = beg + (uint32_t)((int64_t)s * a.seg < L ? s * a.seg : 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q_perm: a segment's queries by descending score against its guide vector
+// (equal scores: lower offset first).  Entries past the segment's length are
+// -1.  grid (nseg, B*Hq).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void s2o_qorder_kernel(IndexArgs a) {
+  constexpr int LPQ = D / 8;  // lanes per query
+  __shared__ uint64_t srt[kMaxSegSort];
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int t0 = s * a.seg;
+  if (t0 >= L) return;
+  const int n = min(a.seg, L - t0);
+  int P2 = 1;
+  while (P2 < n) P2 <<= 1;
+  const int sub = threadIdx.x % LPQ;
+  const uint4 gv = load16(a.guide + (((int64_t)b * a.Hkv + g) * a.nseg + s) * D + sub * 8);
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  for (int i0 = 0; i0 < P2; i0 += kThreads / LPQ) {
+    const int i = i0 + threadIdx.x / LPQ;
+    float acc = 0.f;
+    if (i < n) {
+      const uint4 qv = load16(a.q + (((int64_t)bh) * a.max_len + t0 + i) * D + sub * 8);
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf16_lo(qw[e]), bf16_lo(gw[e]), acc);
+        acc = fmaf(bf16_hi(qw[e]), bf16_hi(gw[e]), acc);
+      }
+    }
+#pragma unroll
+    for (int off = LPQ / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    if (sub == 0 && i < P2)
+      srt[i] = i < n ? ((uint64_t)order_key(acc) << 32) | (uint32_t)~(uint32_t)i : 0ull;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P2; i += kThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = srt[i], y = srt[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? x < y : x > y) {
+            srt[i] = y;
+            srt[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* out = a.q_perm + ((int64_t)bh * a.nseg + s) * a.seg;
+  for (int i = threadIdx.x; i < a.seg; i += kThreads)
+    out[i] = i < n ? (int32_t)~(uint32_t)(srt[i] & 0xFFFFFFFFull) : -1;
+}
+
+// ---------------------------------------------------------------------------
+// History score keys: token t against the representative query of every
+// (head of the group, later segment s) on the matrix cores; key layout is the
+// sort's ([segment][max_len]).  grid (ceil(max_len/64), B*Hkv); wave w takes
+// tokens t0 + 16w .. +15 as the A operand, 16 (head, segment) pairs at a time
+// as the B operand.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void s2o_kvscore_kernel(IndexArgs a) {
+  constexpr int KC = D / 32;
+  const int b = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int t0 = blockIdx.x * kTile;
+  if (t0 >= L) return;
+  const int s_min = t0 / a.seg + 1;
+  const int nseg_b = (L + a.seg - 1) / a.seg;
+  if (s_min >= nseg_b) return;  // no later segment: the tile is no one's history
+  const int ns = nseg_b - s_min, pairs = a.G * ns;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int col = lane % 16, grp = lane / 16;
+  // every token of this tile lies in the history of every segment >= s_min
+  const uint16_t* kr =
+      token_row<D>(a.k_pool, a.table, b, g, t0 + 16 * w + col, a.Hkv, a.max_blocks, a.P);
+  bf16x8 kf[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    const uint4 v = load16(kr + 32 * c + 8 * grp);
+    kf[c] = __builtin_bit_cast(bf16x8, v);
+  }
+  const int tok = t0 + 16 * w + 4 * grp;  // this lane's output rows: tok .. tok+3
+  for (int p0 = 0; p0 < pairs; p0 += 16) {
+    const int p = p0 + col;
+    const bool ok = p < pairs;
+    const int h = g * a.G + (ok ? p / ns : 0), s = s_min + (ok ? p % ns : 0);
+    const size_t seg_idx = ((size_t)b * a.Hq + h) * a.nseg + s;
+    const uint16_t* rr = a.rep + seg_idx * D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const uint4 v = ok ? load16(rr + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], __builtin_bit_cast(bf16x8, v), acc, 0, 0,
+                                                    0);
+    }
+    if (ok) {
+      uint4 keys = make_uint4(order_key(acc[0]), order_key(acc[1]), order_key(acc[2]),
+                              order_key(acc[3]));
+      *reinterpret_cast<uint4*>(a.kin + seg_idx * (size_t)a.max_len + tok) = keys;
+    }
+  }
+}
+
+// token id -> its position within the segment list: values of the sort
+struct PositionInSegment {
+  uint32_t max_len;
+  __host__ __device__ int32_t operator()(uint32_t i) const { return (int32_t)(i % max_len); }
+};
+
+// ---------------------------------------------------------------------------
+// Attention: pass 1 (dense, causal, inside the segment) then pass 2 (history
+// tiles in KV_perm order, early stop per query tile).
+// ---------------------------------------------------------------------------
+struct AttendArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  const int32_t* q_perm;
+  const int32_t* kv_perm;
+  uint16_t* out;
+  int32_t* num_tiles;
+  int B, Hq, Hkv, G, seg, max_len, nseg, max_blocks, P, qtiles, groups;
+  float scale_log2, tau;
+};
+
+// V^T in shared memory: row d holds the tile's 64 keys; 4-key groups are
+// swizzled by d mod 16.
+__device__ __forceinline__ int vt_index(int d, int key) {
+  return d * kTile + ((((key >> 2) ^ (d & 15))) << 2) + (key & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void s2o_attend_kernel(AttendArgs a) {
+  constexpr int KC = D / 32;   // k-steps of Q K^T
+  constexpr int DG = D / 16;   // 16-row groups of O^T
+  constexpr int KRS = D + 8;   // K row stride in shared memory (elements)
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int CPT = CH / 8;  // chunks per thread and row (rows 2p, 2p+1)
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * KRS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * kTile];
+  __shared__ int s_flag[2][kWaves];
+  __shared__ int s_maxpos[kWaves];
+
+  // (sequence, head, segment) groups heaviest first; the query tiles of one
+  // group stay on one XCD (workgroups go round-robin over the 8 XCDs), where
+  // they share the history tiles they gather
+  const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
+  const int grp_id = (kx / a.qtiles) * 8 + xcd, qt = kx % a.qtiles;
+  if (grp_id >= a.groups) return;
+  const int BH = a.B * a.Hq;
+  const int s = a.nseg - 1 - grp_id / BH, bh = grp_id % BH;
+  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int start = s * a.seg;
+  if (start >= L) return;
+  const int len = min(a.seg, L - start), q0 = qt * kTile;
+  if (q0 >= len) return;
+  const int nq = min(kTile, len - q0);
+
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int col = lane % 16, grp = lane / 16;
+  const int qi = 16 * w + col;
+  const bool qvalid = qi < nq;
+  const size_t seg_idx = (size_t)bh * a.nseg + s;
+  const int off = qvalid ? dbg_clamp(a.q_perm[seg_idx * a.seg + q0 + qi], 0, len, kDbgSelected) : 0;
+  const int pos = start + off;
+
+  bf16x8 qf[KC];
+  {
+    const uint16_t* qr = a.q + ((int64_t)bh * a.max_len + pos) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const uint4 v = qvalid ? load16(qr + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  int mp = qvalid ? pos : start;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) mp = max(mp, __shfl_xor(mp, o, kWave));
+  if (lane == 0) s_maxpos[w] = mp;
+  __syncthreads();
+  const int maxpos = max(max(s_maxpos[0], s_maxpos[1]), max(s_maxpos[2], s_maxpos[3]));
+  const int n1 = (maxpos - start) / kTile + 1;  // pass-1 tiles
+  const int n2 = start / kTile;                 // pass-2 (history) tiles
+  const int total = n1 + n2;
+  const int32_t* kvp = a.kv_perm + seg_idx * (size_t)a.max_len;
+
+  // loader: rows 2p, 2p+1 of the tile, chunks ck + 8j
+  const int lp = tid % 32, ck = tid / 32;
+  uint4 kr[2][CPT], vr[2][CPT];
+  auto issue = [&](int n) {
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 2 * lp + rr;
+      int t;
+      bool ok;
+      if (n < n1) {
+        t = start + n * kTile + r;
+        ok = t < L;
+      } else {
+        t = dbg_clamp(kvp[(n - n1) * kTile + r], 0, start, kDbgSelected);
+        ok = true;
+      }
+      if (ok) {
+        const uint16_t* kp = token_row<D>(a.k_pool, a.table, b, g, t, a.Hkv, a.max_blocks, a.P);
+        const uint16_t* vp = a.v_pool + (kp - a.k_pool);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          kr[rr][j] = load16(kp + 8 * (ck + 8 * j));
+          vr[rr][j] = load16(vp + 8 * (ck + 8 * j));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) kr[rr][j] = vr[rr][j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = ck + 8 * j;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        *reinterpret_cast<uint4*>(&ks[(2 * lp + rr) * KRS + 8 * c]) = kr[rr][j];
+      const uint32_t x0[4] = {vr[0][j].x, vr[0][j].y, vr[0][j].z, vr[0][j].w};
+      const uint32_t x1[4] = {vr[1][j].x, vr[1][j].y, vr[1][j].z, vr[1][j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (e & 1) ? (x0[e >> 1] >> 16) : (x0[e >> 1] & 0xFFFFu);
+        const uint32_t hi = (e & 1) ? (x1[e >> 1] & 0xFFFF0000u) : (x1[e >> 1] << 16);
+        *reinterpret_cast<uint32_t*>(&vt[vt_index(8 * c + e, 2 * lp)]) = lo | hi;
+      }
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[DG];
+#pragma unroll
+  for (int dg = 0; dg < DG; ++dg) o[dg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int walked = n2;
+
+  issue(0);
+  for (int n = 0; n < total; ++n) {
+    stash();
+    if (n + 1 < total) issue(n + 1);
+    __syncthreads();
+
+    // S^T = K Q^T: four 16-key blocks, one query per lane column
+    f32x4 st[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&ks[(16 * kb + col) * KRS + 32 * c + 8 * grp]);
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
+                                                         st[kb], 0, 0, 0);
+      }
+    }
+    const bool pass1 = n < n1;
+    float x[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kb + 4 * grp + i;
+        const bool keep = !pass1 || start + n * kTile + key <= pos;
+        x[kb][i] = keep ? st[kb][i] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[kb][i]);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float mn = fmaxf(m, mt);
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    float ps = 0.f;
+    float p[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kb][i] = x[kb][i] == -INFINITY ? 0.f : exp2f(x[kb][i] - mn);
+        ps += p[kb][i];
+      }
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int dg = 0; dg < DG; ++dg) o[dg] *= alpha;
+
+    // O^T += V^T P^T over two 32-key chunks
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = (__bf16)p[2 * c][i];
+        pf[4 + i] = (__bf16)p[2 * c + 1][i];
+      }
+#pragma unroll
+      for (int dg = 0; dg < DG; ++dg) {
+        const int d = 16 * dg + col;
+        const uint2 va = *reinterpret_cast<const uint2*>(&vt[vt_index(d, 32 * c + 4 * grp)]);
+        const uint2 vb = *reinterpret_cast<const uint2*>(&vt[vt_index(d, 32 * c + 16 + 4 * grp)]);
+        const uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
+        o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dg],
+                                                        0, 0, 0);
+      }
+    }
+
+    if (!pass1) {
+      const bool below = !qvalid || ps < a.tau * l;
+      const int all = __all(below);
+      if (lane == 0) s_flag[n & 1][w] = all;
+    }
+    __syncthreads();
+    if (!pass1 && s_flag[n & 1][0] && s_flag[n & 1][1] && s_flag[n & 1][2] && s_flag[n & 1][3]) {
+      walked = n - n1 + 1;
+      break;
+    }
+  }
+
+  if (qvalid) {
+    const float inv = 1.f / l;
+    uint16_t* orow = a.out + ((int64_t)bh * a.max_len + pos) * D;
+#pragma unroll
+    for (int dg = 0; dg < DG; ++dg) {
+      bf16x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (__bf16)(o[dg][i] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 16 * dg + 4 * grp) = r;
+    }
+  }
+  if (tid == 0) a.num_tiles[seg_idx * (size_t)(a.seg / kTile) + qt] = walked;
+}
+
+template <int D>
+hipError_t index_d(const PrefillLaunch& L, hipStream_t stream) {
+  const PrefillLayout& lay = L.lay;
+  char* ws = static_cast<char*>(L.workspace);
+  IndexArgs a{};
+  a.q = static_cast<const uint16_t*>(L.q);
+  a.k_pool = static_cast<const uint16_t*>(L.k_pool);
+  a.table = L.table;
+  a.seq_lens = L.seq_lens;
+  a.q_perm = L.q_perm;
+  a.keysum = reinterpret_cast<double*>(ws + lay.off_keysum);
+  a.guide = reinterpret_cast<uint16_t*>(ws + lay.off_guide);
+  a.rep = reinterpret_cast<uint16_t*>(ws + lay.off_rep);
+  a.begin = reinterpret_cast<uint32_t*>(ws + lay.off_begin);
+  a.end = reinterpret_cast<uint32_t*>(ws + lay.off_end);
+  a.kin = reinterpret_cast<uint32_t*>(ws + lay.off_kin);
+  a.B = lay.B;
+  a.Hq = lay.Hq;
+  a.Hkv = lay.Hkv;
+  a.G = L.G;
+  a.seg = lay.seg;
+  a.max_len = lay.max_len;
+  a.nseg = lay.nseg;
+  a.max_blocks = L.max_blocks;
+  a.P = L.P;
+  s2o_sums_kernel<D><<<dim3(lay.nseg, lay.B * (lay.Hq + lay.Hkv)), kThreads, 0, stream>>>(a);
+  s2o_guide_kernel<D><<<dim3(lay.B * lay.Hkv), kThreads, 0, stream>>>(a);
+  s2o_qorder_kernel<D><<<dim3(lay.nseg, lay.B * lay.Hq), kThreads, 0, stream>>>(a);
+  s2o_kvscore_kernel<D>
+      <<<dim3((lay.max_len + kTile - 1) / kTile, lay.B * lay.Hkv), kThreads, 0, stream>>>(a);
+  if (hipError_t e = hipGetLastError()) return e;
+  uint32_t* kout = reinterpret_cast<uint32_t*>(ws + lay.off_kout);
+  const auto vals = rocprim::make_transform_iterator(rocprim::counting_iterator<uint32_t>(0),
+                                                     PositionInSegment{(uint32_t)lay.max_len});
+  size_t bytes = lay.sort_bytes;
+  return rocprim::segmented_radix_sort_pairs_desc(
+      ws + lay.off_sort, bytes, a.kin, kout, vals, L.kv_perm, (unsigned int)lay.items,
+      (unsigned int)lay.segs, a.begin, a.end, 0, 32, stream);
+}
+
+template <int D>
+hipError_t attend_d(const PrefillLaunch& L, hipStream_t stream) {
+  const PrefillLayout& lay = L.lay;
+  AttendArgs a{};
+  a.q = static_cast<const uint16_t*>(L.q);
+  a.k_pool = static_cast<const uint16_t*>(L.k_pool);
+  a.v_pool = static_cast<const uint16_t*>(L.v_pool);
+  a.table = L.table;
+  a.seq_lens = L.seq_lens;
+  a.q_perm = L.q_perm_in;
+  a.kv_perm = L.kv_perm_in;
+  a.out = static_cast<uint16_t*>(L.out);
+  a.num_tiles = L.num_tiles;
+  a.B = lay.B;
+  a.Hq = lay.Hq;
+  a.Hkv = lay.Hkv;
+  a.G = L.G;
+  a.seg = lay.seg;
+  a.max_len = lay.max_len;
+  a.nseg = lay.nseg;
+  a.max_blocks = L.max_blocks;
+  a.P = L.P;
+  a.qtiles = lay.seg / kTile;
+  a.groups = lay.B * lay.Hq * lay.nseg;
+  a.scale_log2 = L.scale * kLog2e;
+  a.tau = L.tau;
+  const int grid = (a.groups + 7) / 8 * 8 * a.qtiles;
+  s2o_attend_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t prefill_sort_bytes(const PrefillLayout& lay, size_t* bytes) {
+  const auto vals = rocprim::make_transform_iterator(rocprim::counting_iterator<uint32_t>(0),
+                                                     PositionInSegment{(uint32_t)lay.max_len});
+  *bytes = 0;
+  return rocprim::segmented_radix_sort_pairs_desc(
+      nullptr, *bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr, vals, (int32_t*)nullptr,
+      (unsigned int)lay.items, (unsigned int)lay.segs, (const uint32_t*)nullptr,
+      (const uint32_t*)nullptr, 0, 32, (hipStream_t)0);
+}
+
+hipError_t launch_prefill_index(const PrefillLaunch& L, hipStream_t stream) {
+  return L.D == 64 ? index_d<64>(L, stream) : index_d<128>(L, stream);
+}
+
+hipError_t launch_prefill_attend(const PrefillLaunch& L, hipStream_t stream) {
+  return L.D == 64 ? attend_d<64>(L, stream) : attend_d<128>(L, stream);
+}
+
+hipError_t debug_word_prefill(uint32_t* out, bool clear) { return debug_word_access(out, clear); }
+
+}  // namespace nsa

@@ -15,6 +15,9 @@
  * nsa_decode_step does the last two in one launch (and
  * nsa_decode_step_noalloc without a workspace); nsa_residency_diff reports
  * the blocks to fetch and release between consecutive selections.
+ * nsa_s2o_index and nsa_s2o_attend are S2O's prefill over the same paged
+ * cache: per-segment query and history orders, then a two-pass attention on
+ * the matrix cores with the early stop.
  *
  * Sources for the operations (web pages on the method):
  *   - NOSA technical summary (gist.science/es/paper/2510.13602),
@@ -29,7 +32,8 @@
  *   - S2O technical summary (gist.science/it/paper/2602.22575),
  *     "1. Permutazione Online" (keep the physical layout, gather through
  *     index arrays), "2. Regola di Arresto Anticipato" and
- *     "3. Implementazione del Kernel" (ordered traversal, early stop).
+ *     "3. Implementazione del Kernel" (ordered traversal, early stop; the
+     two passes of the prefill kernel).
  *   - NOSA blog post (blogs.edgentiq.com): block tables managed on the host.
  *
  * Conventions shared by every call
@@ -63,7 +67,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 4
+#define NSA_ABI_VERSION 5
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -387,15 +391,84 @@ nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32
                                   hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * S2O prefill (S2O summary, "1. Permutazione Online tramite Caricamento
+ * Guidato da Indici", "2. Regola di Arresto Anticipato", "3. Implementazione
+ * del Kernel").  Sequence b's L_b = seq_lens[b] prompt tokens are cut into
+ * segments of `segment` tokens (the last may be shorter); the keys and
+ * values of all L_b tokens are already in the pools.  For query head h
+ * (KV head g = h / G) and segment s starting at token a = s * segment:
+ *
+ *   guide     the mean key of tokens [0, a), rounded once to bf16 (zero
+ *             for s = 0)
+ *   rep       the mean query of the segment, rounded once to bf16
+ *   Q_perm    the segment's query offsets by descending q . guide (fp32
+ *             dot products of the bf16 values; equal scores: lower offset
+ *             first)
+ *   KV_perm   the history tokens [0, a) by descending k . rep (equal
+ *             scores: lower token first)
+ *
+ * nsa_s2o_attend: each tile of 64 queries Q_perm[64j .. 64j+63] attends
+ * (pass 1) densely and causally inside the segment -- the query at token p
+ * sees tokens [a, p] -- and then (pass 2) walks the history in tiles of 64
+ * tokens KV_perm[64n .. 64n+63].  After tile n, M_i is query i's attention
+ * mass of tile n and A_i its mass over everything it has seen (tile n
+ * included); the walk stops once M_i < tau * A_i for every query of the
+ * tile, keeping tile n.  tau = 0 never stops (dense causal attention).
+ * The output of a query is softmax(q . k * scale) over the tokens it saw,
+ * applied to V, accumulated in fp32 (P rounded to bf16 for the matrix
+ * cores), stored as bf16.
+ *
+ *   dtype            must be NSA_BF16 (NSA_ERR_UNSUPPORTED otherwise)
+ *   segment          multiple of 64 in [64, 4096]
+ *   max_seq_len      row stride in tokens of q, out and kv_perm; multiple of
+ *                    64, at most 64 * max_blocks_per_seq; seq_lens[b] <=
+ *                    max_seq_len is the caller's contract
+ *   q, out           [B][Hq][max_seq_len][D] bf16 (rows past L_b unused)
+ *   q_perm           [B][Hq][nseg][segment] int32, nseg = ceil(max_seq_len /
+ *                    segment); offsets in the segment, -1 past its length
+ *   kv_perm          [B][Hq][nseg][max_seq_len] int32; segment s uses its
+ *                    first s * segment entries (the rest is left untouched)
+ *   num_tiles        [B][Hq][nseg][segment / 64] int32 out: history tiles
+ *                    walked by each query tile (segments that exist only)
+ *   workspace        nsa_s2o_workspace_bytes bytes, 256-byte aligned, for
+ *                    nsa_s2o_index only; no initial contents needed
+ *
+ * B * Hq * nseg * max_seq_len must stay below 2^31 (NSA_ERR_UNSUPPORTED).
+ * nsa_s2o_workspace_bytes and nsa_s2o_index ask the device for the size of
+ * the segmented sort's storage (NSA_ERR_HIP without a device).
+ * ------------------------------------------------------------------------ */
+typedef struct nsa_prefill_params {
+  int32_t segment;      /* tokens per segment */
+  int32_t max_seq_len;  /* token stride of q, out and kv_perm */
+  float tau;            /* early-stop threshold, finite, >= 0 */
+} nsa_prefill_params;
+
+nsa_status nsa_s2o_workspace_bytes(const nsa_shape* shape, const nsa_prefill_params* params,
+                                   size_t* bytes);
+
+/* Q_perm and KV_perm of every (sequence, query head, segment). */
+nsa_status nsa_s2o_index(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
+                         const void* k_pool, const int32_t* block_table, const int32_t* seq_lens,
+                         int32_t* q_perm, int32_t* kv_perm, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Both passes with the early stop, on the given orders (any valid
+ * permutations: they decide which tokens a query tile walks first). */
+nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* q_perm, const int32_t* kv_perm,
+                          void* out, int32_t* num_tiles, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * Device-side contract checks.  Libraries built with -DNSA_DEBUG (build.py
  * --checks) check, where the kernels read them, the values that are the
  * caller's contract: block-table entries in [0, num_phys_blocks) (bit 1),
- * listed block ids below the row's full blocks (bit 2), eviction-set ids
- * below the row's full blocks (bit 4), seq_lens at most
- * 64 * max_blocks_per_seq (bit 8).  A violation sets its bit and the value
- * is clamped into range, so that no access leaves the caller's buffers (the
- * results of that call are then meaningless).  Release builds compile the
- * checks out.
+ * listed block ids below the row's full blocks and S2O order entries inside
+ * their range (bit 2), eviction-set ids below the row's full blocks (bit 4),
+ * seq_lens at most 64 * max_blocks_per_seq, or max_seq_len for the prefill
+ * (bit 8).  A violation sets its bit and the value is clamped into range, so
+ * that no access leaves the caller's buffers (the results of that call are
+ * then meaningless).  Release builds compile the checks out.
  * ------------------------------------------------------------------------ */
 /* 1 when the library was built with the checks, 0 otherwise. */
 int32_t nsa_debug_checks(void);

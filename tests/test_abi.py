@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = N.load()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(N.EXPORTS) == names
@@ -208,3 +208,25 @@ def test_debug_checks_queries():
         pytest.skip("a build with the device checks")
     assert N.nsa_debug_error() == 0
     assert lib.nsa_debug_error(None, 0) == N.NSA_ERR_INVALID_ARGUMENT
+
+
+def test_s2o_validation():
+    """S2O prefill arguments are checked before any HIP call."""
+    sh = shape(batch=1, max_blocks_per_seq=512, num_phys_blocks=512)
+    ok = N.PrefillParams(1024, 32768, 1e-3)
+    ptrs = [FAKE] * 7
+    expect(N.NSA_ERR_UNSUPPORTED, N.nsa_s2o_workspace_bytes, shape(dtype=N.NSA_F32), ok)
+    for bad in (N.PrefillParams(96, 32768, 1e-3), N.PrefillParams(8192, 32768, 1e-3),
+                N.PrefillParams(1024, 32768 + 32, 1e-3), N.PrefillParams(1024, 64 * 513, 1e-3),
+                N.PrefillParams(1024, 32768, -1.0), N.PrefillParams(1024, 32768, float("inf"))):
+        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_workspace_bytes, sh, bad)
+        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_index, sh, bad, *ptrs, 1 << 30)
+        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_attend, sh, bad, *ptrs, FAKE, FAKE)
+    big = shape(batch=64, max_blocks_per_seq=2048, num_phys_blocks=2048 * 64)
+    expect(N.NSA_ERR_UNSUPPORTED, N.nsa_s2o_workspace_bytes, big, N.PrefillParams(1024, 131072, 0))
+    msg = expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_attend, sh, ok, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, None, FAKE)
+    assert "out" in msg
+    msg = expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_index, sh, ok, FAKE + 2, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, 1 << 30)
+    assert "aligned" in msg
