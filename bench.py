@@ -39,7 +39,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {"tiny-fp32": 0, "nosa-1b": 1, "sparda-8b": 2, "long-128k": 3, "early-stop": 4}
+PREFILL_WORKLOADS = ("s2o-prefill-32k",)
 KERNEL_SOURCES = {
     "select": "block_sparse_kv_nsa_amd/csrc/nsa_select.hip",
     "decode": "block_sparse_kv_nsa_amd/csrc/nsa_decode.hip",
@@ -52,7 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="long-128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="long-128k",
+                    choices=sorted(WORKLOADS) + list(PREFILL_WORKLOADS))
     ap.add_argument("--instances", type=int, default=0, help="layer instances to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle leg")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows sampled by the oracle leg")
@@ -583,6 +586,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this path shards by rows with no exchange, see the design notes)", file=sys.stderr)
         return 2
+    if args.workload in PREFILL_WORKLOADS:
+        return prefill_main(args)
     import workloads as W
     cfg = W.config(WORKLOADS[args.workload])
     if args.dense and not cfg.ordered:
@@ -656,6 +661,233 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_leg(args, cfg)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+# ----------------------------------------------------------------------------
+# S2O prefill: one step = nsa_s2o_index + nsa_s2o_attend over one batch of
+# prompts (every token's K/V already in the pools)
+# ----------------------------------------------------------------------------
+def prefill_flops(cfg, seq_lens, num_tiles) -> float:
+    """Matrix-core flops the method needs for the walked tiles: 4 * D per
+    (query, attended token) -- Q K^T and P V, two flops per multiply-add --
+    over pass 1 (tokens [a, p] for the query at p) and the n* history tiles
+    of its query tile (64 tokens each)."""
+    import numpy as np
+    seg, D = cfg.segment, cfg.head_dim
+    pairs = 0
+    for b, L in enumerate(seq_lens):
+        for s in range(-(-int(L) // seg)):
+            a = s * seg
+            n = min(seg, int(L) - a)
+            offs = np.arange(n)
+            pairs += cfg.num_q_heads * int((offs + 1).sum())   # pass 1, every head
+            nt = num_tiles[b, :, s, :-(-n // 64)].astype(np.int64)     # [Hq][tiles]
+            sizes = np.minimum(64, n - 64 * np.arange(nt.shape[1]))
+            pairs += int((nt * 64 * sizes[None, :]).sum())
+    return 4.0 * D * pairs
+
+
+def prefill_gpu_leg(args, cfg):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import block_sparse_kv_nsa_amd as N
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    pb = W.build_prefill(cfg)
+    print(f"[bench] {cfg.name}: inputs drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    B, Hq, Hkv, D, seg = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.segment
+    max_len = -(-cfg.seq_len // 64) * 64
+    nseg = -(-max_len // seg)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_host = np.zeros((B, Hq, max_len, D), dtype=np.uint16)
+    q_host[:, :, :cfg.seq_len] = pb.q
+    q, kp, vp = bf16(q_host), bf16(pb.k_pool), bf16(pb.v_pool)
+    del q_host
+    table = torch.from_numpy(pb.table).to(dev)
+    lens = torch.from_numpy(pb.seq_lens).to(dev)
+    shape = N.Shape.make(B, Hq, Hkv, D, cfg.max_blocks, cfg.num_phys_blocks, N.NSA_BF16)
+    params = N.PrefillParams(seg, max_len, cfg.tau)
+    ws_bytes = N.nsa_s2o_workspace_bytes(shape, params)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    q_perm = torch.empty((B, Hq, nseg, seg), dtype=torch.int32, device=dev)
+    kv_perm = torch.empty((B, Hq, nseg, max_len), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, max_len, D), dtype=torch.bfloat16, device=dev)
+    num_tiles = torch.empty((B, Hq, nseg, seg // 64), dtype=torch.int32, device=dev)
+
+    def index():
+        N.nsa_s2o_index(shape, params, q, kp, table, lens, q_perm, kv_perm, ws, ws_bytes)
+
+    def attend():
+        N.nsa_s2o_attend(shape, params, q, kp, vp, table, lens, q_perm, kv_perm, out, num_tiles,
+                         ws, ws_bytes)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        index()
+        if ev is not None:
+            ev[1].record()
+        attend()
+        if ev is not None:
+            ev[2].record()
+
+    step()
+    torch.cuda.synchronize()
+    t_set = time.perf_counter()
+    while time.perf_counter() - t_set < 0.25:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1_000_000)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    n_ev = min(args.steps, 200)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(evs[i])
+    torch.cuda.synchronize()
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ev
+    att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_ev
+    nt = num_tiles.cpu().numpy()
+    flops = prefill_flops(cfg, pb.seq_lens, nt)
+    walked, hist = 0, 0
+    per_tile, full = [], 0
+    for b, L in enumerate(pb.seq_lens):
+        for s in range(-(-int(L) // seg)):
+            n = min(seg, int(L) - s * seg)
+            t = nt[b, :, s, :-(-n // 64)]
+            walked += int(t.sum())
+            hist += t.size * (s * seg // 64)
+            if s:
+                per_tile.append(t.flatten())
+                full += int((t == s * seg // 64).sum())
+    per_tile = np.concatenate(per_tile) if per_tile else np.zeros(1)
+    walk_stats = {"mean": round(float(per_tile.mean()), 2),
+                  "p50": int(np.percentile(per_tile, 50)), "p99": int(np.percentile(per_tile, 99)),
+                  "max": int(per_tile.max()), "query_tiles_without_stop": full,
+                  "query_tiles": int(per_tile.size)}
+    dense_pairs = sum(Hq * int(L) * (int(L) + 1) // 2 for L in pb.seq_lens)
+    return dict(total_ms=total_ms, wall_s=wall, idx_ms=idx_ms, att_ms=att_ms, flops=flops,
+                walked=walked, hist=hist, dense_flops=4.0 * D * dense_pairs, walk_stats=walk_stats,
+                ws_bytes=ws_bytes, tokens=int(sum(int(L) for L in pb.seq_lens)))
+
+
+def prefill_cpu_leg(args, cfg):
+    """The S2O oracle on a bounded sample of one (sequence, head): both orders
+    of two segments (a quarter and three quarters in: a segment's cost grows
+    about linearly with its history, so their mean stands for the mean
+    segment) and four of their query tiles, scaled to every tile, segment,
+    head and sequence."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import s2o_prefill as S
+
+    host_cpus = os.cpu_count() or 1
+    threads = min(host_cpus, 16)
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
+    except Exception:  # pragma: no cover
+        limiter = None
+    f = lambda a: W.stored_to_f64(a, cfg.dtype)  # noqa: E731
+    keys, vals = (f(x) for x in W.kv_row(cfg, 0, 0))
+    q = f(W.q_row(cfg, 0, 0))
+    L, seg = q.shape[0], cfg.segment
+    nseg = -(-L // seg)
+    picks = sorted(set(int(round(x * (nseg - 1))) for x in (0.25, 0.75)))
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    tiles_per_seg = -(-seg // S.TILE)
+    tile_pick = sorted(set(int(round(x)) for x in np.linspace(0, tiles_per_seg - 1, 4)))
+
+    def one_segment(s):
+        a, e = s * seg, min(s * seg + seg, L)
+        t0 = time.perf_counter()
+        qo, _ = S.query_order(q[a:e], keys, a, cfg.dtype)
+        ko, _ = S.history_order(q[a:e], keys, a, cfg.dtype)
+        t_orders = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for j in tile_pick:
+            pos = a + qo[S.TILE * j:S.TILE * (j + 1)]
+            S.query_tile(q[pos], pos, keys, vals, a, ko, cfg.tau, scale)
+        return t_orders + (time.perf_counter() - t0) * tiles_per_seg / len(tile_pick)
+
+    one_segment(1)                              # warm-up
+    times = [sum(one_segment(s) for s in picks) for _ in range(3)]
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_pass = sorted(times)[1]
+    step_s = per_pass / len(picks) * nseg * cfg.num_q_heads * cfg.batch
+    return {"value": cfg.batch * cfg.seq_len / step_s, "unit": "tokens/s", "cores": threads,
+            "host_cpus": host_cpus, "kind": "oracle",
+            "sample": f"median of 3 passes (after a warm-up on segment 1) over segments {picks} of "
+                      f"{nseg} of sequence 0, query head 0: both orders and query tiles "
+                      f"{tile_pick} of {tiles_per_seg} (float64 NumPy, BLAS limited to {threads} "
+                      f"threads); scaled to every tile, {nseg} segments, {cfg.num_q_heads} heads "
+                      f"and {cfg.batch} sequences"}
+
+
+def prefill_main(args) -> int:
+    import workloads as W
+    cfg = W.prefill_config(args.workload)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    g = prefill_gpu_leg(args, cfg)
+    ms_per_step = g["total_ms"] / args.steps
+    att_tflops = g["flops"] / (g["att_ms"] / 1e3) / 1e12
+    kernels = {"index": {"ms": round(g["idx_ms"], 5)},
+               "attend": {"ms": round(g["att_ms"], 5), "flops": g["flops"],
+                          "TFLOP/s": round(att_tflops, 1),
+                          "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+    dom = "attend" if g["att_ms"] >= g["idx_ms"] else "index"
+    line = {
+        "metric": "S2O prefill tokens/s (segment orders + two-pass attention with early stop), 1 GPU",
+        "value": round(g["tokens"] / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len,
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "segment": cfg.segment, "tau": cfg.tau,
+                   "timed_as": "K x (nsa_s2o_index + nsa_s2o_attend)", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "attend", "achieved": kernels["attend"]["TFLOP/s"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": kernels["attend"]["frac"], "traffic": None},
+        "dominant": dom,
+        "kernels": kernels,
+        "metrics": {"history_tiles_walked": g["walked"], "history_tiles": g["hist"],
+                    "walk_per_query_tile": g["walk_stats"],
+                    "density_vs_dense_causal": round(g["flops"] / g["dense_flops"], 4),
+                    "workspace_bytes": g["ws_bytes"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = prefill_cpu_leg(args, cfg)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -164,7 +164,7 @@ def load() -> ctypes.CDLL:
     lib.nsa_s2o_index.argtypes = [P(Shape), P(PrefillParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.nsa_s2o_index.restype = i32
     lib.nsa_s2o_attend.argtypes = [P(Shape), P(PrefillParams), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                   vp]
+                                   vp, sz, vp]
     lib.nsa_s2o_attend.restype = i32
     lib.nsa_decode_step_grid.argtypes = [P(Shape), P(SelectParams), i32, i32, P(StepGrid)]
     lib.nsa_decode_step_grid.restype = i32
@@ -335,10 +335,12 @@ def nsa_s2o_index(shape: Shape, params: PrefillParams, q, k_pool, block_table, s
 
 
 def nsa_s2o_attend(shape: Shape, params: PrefillParams, q, k_pool, v_pool, block_table, seq_lens,
-                   q_perm, kv_perm, out, num_tiles, stream=None) -> None:
+                   q_perm, kv_perm, out, num_tiles, workspace, workspace_bytes: int,
+                   stream=None) -> None:
     st = load().nsa_s2o_attend(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_pool),
                                _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(q_perm),
-                               _ptr(kv_perm), _ptr(out), _ptr(num_tiles), _stream(stream))
+                               _ptr(kv_perm), _ptr(out), _ptr(num_tiles), _ptr(workspace),
+                               int(workspace_bytes), _stream(stream))
     _check(st, "nsa_s2o_attend")
 
 

@@ -642,7 +642,8 @@ nsa_status nsa_s2o_index(const nsa_shape* shape, const nsa_prefill_params* param
 nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
                           const void* k_pool, const void* v_pool, const int32_t* block_table,
                           const int32_t* seq_lens, const int32_t* q_perm, const int32_t* kv_perm,
-                          void* out, int32_t* num_tiles, hipStream_t stream) {
+                          void* out, int32_t* num_tiles, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "nsa_s2o_attend";
   nsa::PrefillLayout lay;
   if (nsa_status st = prefill_checked(fn, shape, params, &lay)) return st;
@@ -655,6 +656,10 @@ nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* para
   NSA_REQUIRE_PTR(kv_perm, 4);
   NSA_REQUIRE_PTR(out, 16);
   NSA_REQUIRE_PTR(num_tiles, 4);
+  NSA_REQUIRE_PTR(workspace, 256);
+  if (workspace_bytes < lay.attend_bytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn,
+                workspace_bytes, lay.attend_bytes);
   nsa::PrefillLaunch L{};
   L.D = shape->head_dim;
   L.G = shape->num_q_heads / shape->num_kv_heads;
@@ -667,6 +672,7 @@ nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* para
   L.kv_perm_in = kv_perm;
   L.out = out;
   L.num_tiles = num_tiles;
+  L.workspace = workspace;
   L.max_blocks = shape->max_blocks_per_seq;
   L.P = shape->num_phys_blocks;
   L.scale = scale_of(shape);

@@ -329,7 +329,10 @@ hipError_t debug_word_step(uint32_t* out, bool clear);
 // S2O prefill.  Index step workspace:
 //   [segment key sums (float64) | guide vectors | representative queries |
 //    segment begin offsets | segment end offsets | history score keys (in) |
-//    history score keys (sorted) | the segmented sort's own storage]
+//    history score keys (sorted) | pass-1 states (m, l) | pass-1 states acc |
+//    the segmented sort's own storage]
+// nsa_s2o_attend uses only the pass-1 states, which come before the sort's
+// storage (whose size only the device can tell): its size is attend_bytes.
 // Every list is indexed by segment (b, query head h, segment s), or by
 // (b, KV head g, segment s) for the key sums and guide vectors; the history
 // keys of segment i occupy [i * max_seq_len, i * max_seq_len + s * seg).
@@ -339,7 +342,7 @@ struct PrefillLayout {
   size_t segs;   // B * Hq * nseg
   size_t items;  // segs * max_len
   size_t off_keysum, off_guide, off_rep, off_begin, off_end, off_kin, off_kout, off_sort,
-      sort_bytes, bytes;
+      sort_bytes, off_ml, off_acc, attend_bytes, bytes;
 };
 
 inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int D, int seg, int max_len,
@@ -362,7 +365,11 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int D, int seg, int 
   s.off_end = round_up(s.off_begin + s.segs * 4, 256);
   s.off_kin = round_up(s.off_end + s.segs * 4, 256);
   s.off_kout = round_up(s.off_kin + s.items * 4, 256);
-  s.off_sort = round_up(s.off_kout + s.items * 4, 256);
+  const size_t rows = (size_t)B * Hq * max_len;  // one state per query
+  s.off_ml = round_up(s.off_kout + s.items * 4, 256);
+  s.off_acc = round_up(s.off_ml + rows * 8, 256);
+  s.attend_bytes = round_up(s.off_acc + rows * D * 4, 256);
+  s.off_sort = s.attend_bytes;
   s.sort_bytes = sort_bytes;
   s.bytes = round_up(s.off_sort + sort_bytes, 256);
   return s;

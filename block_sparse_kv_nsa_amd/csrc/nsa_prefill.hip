@@ -23,15 +23,19 @@
 // then a segmented radix sort of the keys per (sequence, head, segment)
 // (rocPRIM; stable, so equal scores keep ascending token order).
 //
-// Attention (nsa_s2o_attend): s2o_attend_kernel, one workgroup per tile of
-// 64 permuted queries.  Each wave holds 16 queries as the B operand of
-// S^T = K Q^T (v_mfma_f32_16x16x32_bf16): the output puts one query per lane
-// column, so softmax statistics stay per lane and P^T feeds the V^T P^T
-// product without a transpose.  K tiles sit in shared memory row-major
-// (rows padded by 16 bytes), V tiles transposed with a 4-key-group swizzle
-// so that both the stores and the 8-byte operand reads are free of bank
-// conflicts.  The next tile's K/V are loaded into registers while the
-// current one is computed.
+// Attention (nsa_s2o_attend): s2o_pass1_kernel, one workgroup per tile of 64
+// consecutive queries, attends causally inside the segment and leaves each
+// query's online-softmax state (m, l, acc) in the workspace;
+// s2o_pass2_kernel, one workgroup per tile of 64 permuted queries, resumes
+// those states and walks the history with the early stop.  Each wave holds
+// 16 queries as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): the
+// output puts one query per lane column, so softmax statistics stay per lane
+// and P^T feeds the V^T P^T product without a transpose.  K tiles sit in
+// shared memory row-major (rows padded by 16 bytes), V tiles transposed with
+// a 4-key-group swizzle so that both the stores and the 8-byte operand reads
+// are free of bank conflicts.  The next tile's K/V are loaded into registers
+// while the current one is computed; pass 2 also fetches the token ids two
+// tiles ahead and their table entries one tile ahead.
 #include <hip/hip_runtime.h>
 
 #include <rocprim/device/device_segmented_radix_sort.hpp>
@@ -275,8 +279,11 @@ struct PositionInSegment {
 };
 
 // ---------------------------------------------------------------------------
-// Attention: pass 1 (dense, causal, inside the segment) then pass 2 (history
-// tiles in KV_perm order, early stop per query tile).
+// Attention.  Pass 1 (s2o_pass1_kernel): each tile of 64 consecutive queries
+// attends densely and causally to its segment and leaves (m, l, acc) per
+// query in the workspace.  Pass 2 (s2o_pass2_kernel): each tile of 64
+// permuted queries resumes those states and walks the history in KV_perm
+// order until the early stop.
 // ---------------------------------------------------------------------------
 struct AttendArgs {
   const uint16_t* q;
@@ -288,6 +295,8 @@ struct AttendArgs {
   const int32_t* kv_perm;
   uint16_t* out;
   int32_t* num_tiles;
+  float* st_ml;   // [B*Hq][max_len][2]: m (log2 units), l
+  float* st_acc;  // [B*Hq][max_len][D]: unnormalised output
   int B, Hq, Hkv, G, seg, max_len, nseg, max_blocks, P, qtiles, groups;
   float scale_log2, tau;
 };
@@ -298,203 +307,304 @@ __device__ __forceinline__ int vt_index(int d, int key) {
   return d * kTile + ((((key >> 2) ^ (d & 15))) << 2) + (key & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void s2o_attend_kernel(AttendArgs a) {
-  constexpr int KC = D / 32;   // k-steps of Q K^T
-  constexpr int DG = D / 16;   // 16-row groups of O^T
-  constexpr int KRS = D + 8;   // K row stride in shared memory (elements)
-  constexpr int CH = D / 8;    // 16-byte chunks per row
-  constexpr int CPT = CH / 8;  // chunks per thread and row (rows 2p, 2p+1)
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTile * KRS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * kTile];
-  __shared__ int s_flag[2][kWaves];
-  __shared__ int s_maxpos[kWaves];
-
-  // (sequence, head, segment) groups heaviest first; the query tiles of one
-  // group stay on one XCD (workgroups go round-robin over the 8 XCDs), where
-  // they share the history tiles they gather
+// The workgroup of a launch over (sequence, head, segment) groups with
+// `qtiles` query tiles each: groups heaviest (latest segment) first, and the
+// query tiles of one group on one XCD (workgroups go round-robin over the 8
+// XCDs), where they share the tiles they gather.  Returns false for the
+// padding workgroups past the last group.
+struct GroupTile {
+  int s, bh, qt;
+};
+__device__ __forceinline__ bool group_tile(const AttendArgs& a, GroupTile* g) {
   const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
-  const int grp_id = (kx / a.qtiles) * 8 + xcd, qt = kx % a.qtiles;
-  if (grp_id >= a.groups) return;
+  const int grp_id = (kx / a.qtiles) * 8 + xcd;
+  if (grp_id >= a.groups) return false;
   const int BH = a.B * a.Hq;
-  const int s = a.nseg - 1 - grp_id / BH, bh = grp_id % BH;
-  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G;
-  const int L = seq_len_of(a.seq_lens, b, a.max_len);
-  const int start = s * a.seg;
-  if (start >= L) return;
-  const int len = min(a.seg, L - start), q0 = qt * kTile;
-  if (q0 >= len) return;
-  const int nq = min(kTile, len - q0);
+  g->s = a.nseg - 1 - grp_id / BH;
+  g->bh = grp_id % BH;
+  g->qt = kx % a.qtiles;
+  return true;
+}
 
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-  const int col = lane % 16, grp = lane / 16;
-  const int qi = 16 * w + col;
-  const bool qvalid = qi < nq;
-  const size_t seg_idx = (size_t)bh * a.nseg + s;
-  const int off = qvalid ? dbg_clamp(a.q_perm[seg_idx * a.seg + q0 + qi], 0, len, kDbgSelected) : 0;
-  const int pos = start + off;
+// Shared memory of one 64-token tile and its loader: each thread moves rows
+// 2p and 2p+1 (p = tid % 32), 16-byte chunks ck + 8j (ck = tid / 32).
+template <int D>
+struct TileSmem {
+  static constexpr int KRS = D + 8;   // K row stride (elements), rows 16-byte padded
+  static constexpr int CPT = D / 64;  // chunks per thread and row
+  uint16_t ks[kTile * KRS];
+  uint16_t vt[D * kTile];
+};
 
-  bf16x8 qf[KC];
-  {
-    const uint16_t* qr = a.q + ((int64_t)bh * a.max_len + pos) * D;
+template <int D>
+struct TileRegs {
+  uint4 k[2][TileSmem<D>::CPT], v[2][TileSmem<D>::CPT];
+  __device__ __forceinline__ void load_kv(const uint16_t* k_pool, const uint16_t* v_pool,
+                                          int64_t r0, int64_t r1, bool ok0, bool ok1, int ck) {
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const uint4 v = qvalid ? load16(qr + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, v);
+    for (int j = 0; j < TileSmem<D>::CPT; ++j) {
+      const int c = 8 * (ck + 8 * j);
+      k[0][j] = ok0 ? load16(k_pool + r0 + c) : make_uint4(0, 0, 0, 0);
+      k[1][j] = ok1 ? load16(k_pool + r1 + c) : make_uint4(0, 0, 0, 0);
+      v[0][j] = ok0 ? load16(v_pool + r0 + c) : make_uint4(0, 0, 0, 0);
+      v[1][j] = ok1 ? load16(v_pool + r1 + c) : make_uint4(0, 0, 0, 0);
     }
   }
-  int mp = qvalid ? pos : start;
+  __device__ __forceinline__ void stash(TileSmem<D>& sm, int lp, int ck) const {
+    constexpr int KRS = TileSmem<D>::KRS;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) mp = max(mp, __shfl_xor(mp, o, kWave));
-  if (lane == 0) s_maxpos[w] = mp;
-  __syncthreads();
-  const int maxpos = max(max(s_maxpos[0], s_maxpos[1]), max(s_maxpos[2], s_maxpos[3]));
-  const int n1 = (maxpos - start) / kTile + 1;  // pass-1 tiles
-  const int n2 = start / kTile;                 // pass-2 (history) tiles
-  const int total = n1 + n2;
-  const int32_t* kvp = a.kv_perm + seg_idx * (size_t)a.max_len;
-
-  // loader: rows 2p, 2p+1 of the tile, chunks ck + 8j
-  const int lp = tid % 32, ck = tid / 32;
-  uint4 kr[2][CPT], vr[2][CPT];
-  auto issue = [&](int n) {
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = 2 * lp + rr;
-      int t;
-      bool ok;
-      if (n < n1) {
-        t = start + n * kTile + r;
-        ok = t < L;
-      } else {
-        t = dbg_clamp(kvp[(n - n1) * kTile + r], 0, start, kDbgSelected);
-        ok = true;
-      }
-      if (ok) {
-        const uint16_t* kp = token_row<D>(a.k_pool, a.table, b, g, t, a.Hkv, a.max_blocks, a.P);
-        const uint16_t* vp = a.v_pool + (kp - a.k_pool);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          kr[rr][j] = load16(kp + 8 * (ck + 8 * j));
-          vr[rr][j] = load16(vp + 8 * (ck + 8 * j));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) kr[rr][j] = vr[rr][j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
+    for (int j = 0; j < TileSmem<D>::CPT; ++j) {
       const int c = ck + 8 * j;
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
-        *reinterpret_cast<uint4*>(&ks[(2 * lp + rr) * KRS + 8 * c]) = kr[rr][j];
-      const uint32_t x0[4] = {vr[0][j].x, vr[0][j].y, vr[0][j].z, vr[0][j].w};
-      const uint32_t x1[4] = {vr[1][j].x, vr[1][j].y, vr[1][j].z, vr[1][j].w};
+        *reinterpret_cast<uint4*>(&sm.ks[(2 * lp + rr) * KRS + 8 * c]) = k[rr][j];
+      const uint32_t x0[4] = {v[0][j].x, v[0][j].y, v[0][j].z, v[0][j].w};
+      const uint32_t x1[4] = {v[1][j].x, v[1][j].y, v[1][j].z, v[1][j].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = (e & 1) ? (x0[e >> 1] >> 16) : (x0[e >> 1] & 0xFFFFu);
         const uint32_t hi = (e & 1) ? (x1[e >> 1] & 0xFFFF0000u) : (x1[e >> 1] << 16);
-        *reinterpret_cast<uint32_t*>(&vt[vt_index(8 * c + e, 2 * lp)]) = lo | hi;
+        *reinterpret_cast<uint32_t*>(&sm.vt[vt_index(8 * c + e, 2 * lp)]) = lo | hi;
       }
     }
-  };
+  }
+};
 
+// One tile of 64 keys for this wave's 16 queries (one per lane column):
+// S^T = K Q^T, online-softmax update of (m, l, o), O^T += V^T P^T.  Keys at
+// or past `mask_from` (token index relative to the tile, -1: none) are
+// masked for queries before them: key k is kept iff k <= rel (the query's
+// position relative to the tile).  Returns the tile's mass in units of
+// 2^-m (after the update).
+template <int D>
+__device__ __forceinline__ float tile_step(const TileSmem<D>& sm, const bf16x8 (&qf)[D / 32],
+                                           f32x4 (&o)[D / 16], float& m, float& l, int col,
+                                           int grp, float scale_log2, bool masked, int rel) {
+  constexpr int KC = D / 32, DG = D / 16, KRS = TileSmem<D>::KRS;
+  f32x4 st[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(&sm.ks[(16 * kb + col) * KRS + 32 * c + 8 * grp]);
+      st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], st[kb],
+                                                       0, 0, 0);
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * kb + 4 * grp + i;
+      st[kb][i] = (!masked || key <= rel) ? st[kb][i] * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, st[kb][i]);
+    }
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+  const float mn = fmaxf(m, mt);
+  const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+  float ps = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st[kb][i] = st[kb][i] == -INFINITY ? 0.f : exp2f(st[kb][i] - mn);
+      ps += st[kb][i];
+    }
+  }
+  ps += __shfl_xor(ps, 16, kWave);
+  ps += __shfl_xor(ps, 32, kWave);
+  l = l * alpha + ps;
+  m = mn;
+#pragma unroll
+  for (int dg = 0; dg < DG; ++dg) o[dg] *= alpha;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)st[2 * c][i];
+      pf[4 + i] = (__bf16)st[2 * c + 1][i];
+    }
+#pragma unroll
+    for (int dg = 0; dg < DG; ++dg) {
+      const int d = 16 * dg + col;
+      const uint2 va = *reinterpret_cast<const uint2*>(&sm.vt[vt_index(d, 32 * c + 4 * grp)]);
+      const uint2 vb = *reinterpret_cast<const uint2*>(&sm.vt[vt_index(d, 32 * c + 16 + 4 * grp)]);
+      const uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
+      o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dg], 0,
+                                                      0, 0);
+    }
+  }
+  return ps;
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const uint16_t* qrow, bool ok,
+                                       int grp) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const uint4 v = ok ? load16(qrow + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
+    qf[c] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// Pass 1: queries a + 64*qt .. +63 in order; tiles 0..qt of the segment
+// (block slabs, found through the table), the last one causally masked.
+template <int D>
+__global__ __launch_bounds__(kThreads, 3) void s2o_pass1_kernel(AttendArgs a) {
+  constexpr int DG = D / 16;
+  __shared__ __attribute__((aligned(16))) TileSmem<D> sm;
+  __shared__ int s_slot[kMaxSegSort / kTile];
+  GroupTile gt;
+  if (!group_tile(a, &gt)) return;
+  const int b = gt.bh / a.Hq, g = (gt.bh % a.Hq) / a.G;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int start = gt.s * a.seg;
+  if (start >= L) return;
+  const int len = min(a.seg, L - start), q0 = gt.qt * kTile;
+  if (q0 >= len) return;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int col = lane % 16, grp = lane / 16;
+  const int qi = 16 * w + col;
+  const bool qvalid = q0 + qi < len;
+  const int pos = start + q0 + (qvalid ? qi : 0);
+  bf16x8 qf[D / 32];
+  load_q<D>(qf, a.q + ((int64_t)gt.bh * a.max_len + pos) * D, qvalid, grp);
+  const int ntiles = gt.qt + 1;
+  if (tid < ntiles)
+    s_slot[tid] = dbg_clamp(a.table[(int64_t)b * a.max_blocks + start / kTile + tid], 0, a.P,
+                            kDbgTable);
+  __syncthreads();
+  const int lp = tid % 32, ck = tid / 32;
+  TileRegs<D> tr;
+  auto issue = [&](int n) {
+    const int64_t slab = ((int64_t)s_slot[n] * a.Hkv + g) * kBlock;
+    const int t0 = start + n * kTile + 2 * lp;
+    tr.load_kv(a.k_pool, a.v_pool, (slab + 2 * lp) * D, (slab + 2 * lp + 1) * D, t0 < L,
+               t0 + 1 < L, ck);
+  };
   float m = -INFINITY, l = 0.f;
   f32x4 o[DG];
 #pragma unroll
   for (int dg = 0; dg < DG; ++dg) o[dg] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int walked = n2;
-
   issue(0);
-  for (int n = 0; n < total; ++n) {
-    stash();
-    if (n + 1 < total) issue(n + 1);
+  for (int n = 0; n < ntiles; ++n) {
+    tr.stash(sm, lp, ck);
+    if (n + 1 < ntiles) issue(n + 1);
     __syncthreads();
+    tile_step<D>(sm, qf, o, m, l, col, grp, a.scale_log2, n == gt.qt, pos - start - n * kTile);
+    __syncthreads();
+  }
+  if (qvalid) {
+    const int64_t row = (int64_t)gt.bh * a.max_len + pos;
+    if (grp == 0) *reinterpret_cast<f32x2*>(a.st_ml + row * 2) = f32x2{m, l};
+#pragma unroll
+    for (int dg = 0; dg < DG; ++dg)
+      *reinterpret_cast<f32x4*>(a.st_acc + row * D + 16 * dg + 4 * grp) = o[dg];
+  }
+}
 
-    // S^T = K Q^T: four 16-key blocks, one query per lane column
-    f32x4 st[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&ks[(16 * kb + col) * KRS + 32 * c + 8 * grp]);
-        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
-                                                         st[kb], 0, 0, 0);
-      }
-    }
-    const bool pass1 = n < n1;
-    float x[4][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kb + 4 * grp + i;
-        const bool keep = !pass1 || start + n * kTile + key <= pos;
-        x[kb][i] = keep ? st[kb][i] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[kb][i]);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float mn = fmaxf(m, mt);
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
-    float ps = 0.f;
-    float p[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kb][i] = x[kb][i] == -INFINITY ? 0.f : exp2f(x[kb][i] - mn);
-        ps += p[kb][i];
-      }
-    }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    l = l * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int dg = 0; dg < DG; ++dg) o[dg] *= alpha;
+// Pass 2: the tile's permuted queries resume their pass-1 states and walk the
+// history tiles in KV_perm order.  Loads run ahead of the tile being
+// computed: the token ids two tiles ahead, their table entries and the K/V
+// rows one tile ahead.
+template <int D>
+__global__ __launch_bounds__(kThreads, 3) void s2o_pass2_kernel(AttendArgs a) {
+  constexpr int DG = D / 16;
+  __shared__ __attribute__((aligned(16))) TileSmem<D> sm;
+  __shared__ int s_flag[2][kWaves];
+  GroupTile gt;
+  if (!group_tile(a, &gt)) return;
+  const int b = gt.bh / a.Hq, g = (gt.bh % a.Hq) / a.G;
+  const int L = seq_len_of(a.seq_lens, b, a.max_len);
+  const int start = gt.s * a.seg;
+  if (start >= L) return;
+  const int len = min(a.seg, L - start), q0 = gt.qt * kTile;
+  if (q0 >= len) return;
+  const int nq = min(kTile, len - q0);
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int col = lane % 16, grp = lane / 16;
+  const int qi = 16 * w + col;
+  const bool qvalid = qi < nq;
+  const size_t seg_idx = (size_t)gt.bh * a.nseg + gt.s;
+  const int off = qvalid ? dbg_clamp(a.q_perm[seg_idx * a.seg + q0 + qi], 0, len, kDbgSelected) : 0;
+  const int pos = start + off;
+  const int64_t row = (int64_t)gt.bh * a.max_len + pos;
 
-    // O^T += V^T P^T over two 32-key chunks
+  bf16x8 qf[D / 32];
+  load_q<D>(qf, a.q + row * D, qvalid, grp);
+  float m = 0.f, l = 1.f;
+  f32x4 o[DG];
+  if (qvalid) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.st_ml + row * 2);
+    m = ml[0];
+    l = ml[1];
+  }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = (__bf16)p[2 * c][i];
-        pf[4 + i] = (__bf16)p[2 * c + 1][i];
-      }
-#pragma unroll
-      for (int dg = 0; dg < DG; ++dg) {
-        const int d = 16 * dg + col;
-        const uint2 va = *reinterpret_cast<const uint2*>(&vt[vt_index(d, 32 * c + 4 * grp)]);
-        const uint2 vb = *reinterpret_cast<const uint2*>(&vt[vt_index(d, 32 * c + 16 + 4 * grp)]);
-        const uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
-        o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dg],
-                                                        0, 0, 0);
-      }
-    }
+  for (int dg = 0; dg < DG; ++dg)
+    o[dg] = qvalid ? *reinterpret_cast<const f32x4*>(a.st_acc + row * D + 16 * dg + 4 * grp)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (!pass1) {
-      const bool below = !qvalid || ps < a.tau * l;
-      const int all = __all(below);
+  const int n2 = start / kTile;  // history tiles
+  const int32_t* kvp = a.kv_perm + seg_idx * (size_t)a.max_len;
+  const int lp = tid % 32, ck = tid / 32;
+  const int64_t tbl = (int64_t)b * a.max_blocks;
+  auto ids_of = [&](int n) {
+    int2 t = make_int2(0, 0);
+    if (n < n2) t = *reinterpret_cast<const int2*>(kvp + n * kTile + 2 * lp);
+    t.x = dbg_clamp(t.x, 0, max(start, 1), kDbgSelected);
+    t.y = dbg_clamp(t.y, 0, max(start, 1), kDbgSelected);
+    return t;
+  };
+  auto slots_of = [&](int2 t, int n) {
+    int2 sl = make_int2(0, 0);
+    if (n < n2) {
+      sl.x = dbg_clamp(a.table[tbl + (t.x >> 6)], 0, a.P, kDbgTable);
+      sl.y = dbg_clamp(a.table[tbl + (t.y >> 6)], 0, a.P, kDbgTable);
+    }
+    return sl;
+  };
+  TileRegs<D> tr;
+  auto issue = [&](int2 t, int2 sl, int n) {
+    const int64_t r0 = (((int64_t)sl.x * a.Hkv + g) * kBlock + (t.x & 63)) * D;
+    const int64_t r1 = (((int64_t)sl.y * a.Hkv + g) * kBlock + (t.y & 63)) * D;
+    tr.load_kv(a.k_pool, a.v_pool, r0, r1, n < n2, n < n2, ck);
+  };
+
+  int walked = n2;
+  if (n2 > 0) {
+    int2 id1 = ids_of(1), id2 = ids_of(2);
+    {
+      const int2 id0 = ids_of(0);
+      issue(id0, slots_of(id0, 0), 0);
+    }
+    int2 sl1 = slots_of(id1, 1);
+    for (int n = 0; n < n2; ++n) {
+      tr.stash(sm, lp, ck);
+      if (n + 1 < n2) issue(id1, sl1, n + 1);
+      // tile n+2: its table entries; tile n+3: its ids
+      id1 = id2;
+      sl1 = slots_of(id2, n + 2);
+      id2 = ids_of(n + 3);
+      __syncthreads();
+      const float ps = tile_step<D>(sm, qf, o, m, l, col, grp, a.scale_log2, false, 0);
+      const int all = __all(!qvalid || ps < a.tau * l);
       if (lane == 0) s_flag[n & 1][w] = all;
-    }
-    __syncthreads();
-    if (!pass1 && s_flag[n & 1][0] && s_flag[n & 1][1] && s_flag[n & 1][2] && s_flag[n & 1][3]) {
-      walked = n - n1 + 1;
-      break;
+      __syncthreads();
+      if (s_flag[n & 1][0] && s_flag[n & 1][1] && s_flag[n & 1][2] && s_flag[n & 1][3]) {
+        walked = n + 1;
+        break;
+      }
     }
   }
 
   if (qvalid) {
     const float inv = 1.f / l;
-    uint16_t* orow = a.out + ((int64_t)bh * a.max_len + pos) * D;
+    uint16_t* orow = a.out + row * D;
 #pragma unroll
     for (int dg = 0; dg < DG; ++dg) {
       bf16x4 r;
@@ -503,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void s2o_attend_kernel(AttendArgs a) {
       *reinterpret_cast<bf16x4*>(orow + 16 * dg + 4 * grp) = r;
     }
   }
-  if (tid == 0) a.num_tiles[seg_idx * (size_t)(a.seg / kTile) + qt] = walked;
+  if (tid == 0) a.num_tiles[seg_idx * (size_t)(a.seg / kTile) + gt.qt] = walked;
 }
 
 template <int D>
@@ -549,6 +659,7 @@ hipError_t index_d(const PrefillLaunch& L, hipStream_t stream) {
 template <int D>
 hipError_t attend_d(const PrefillLaunch& L, hipStream_t stream) {
   const PrefillLayout& lay = L.lay;
+  char* ws = static_cast<char*>(L.workspace);
   AttendArgs a{};
   a.q = static_cast<const uint16_t*>(L.q);
   a.k_pool = static_cast<const uint16_t*>(L.k_pool);
@@ -559,6 +670,8 @@ hipError_t attend_d(const PrefillLaunch& L, hipStream_t stream) {
   a.kv_perm = L.kv_perm_in;
   a.out = static_cast<uint16_t*>(L.out);
   a.num_tiles = L.num_tiles;
+  a.st_ml = reinterpret_cast<float*>(ws + lay.off_ml);
+  a.st_acc = reinterpret_cast<float*>(ws + lay.off_acc);
   a.B = lay.B;
   a.Hq = lay.Hq;
   a.Hkv = lay.Hkv;
@@ -573,7 +686,8 @@ hipError_t attend_d(const PrefillLaunch& L, hipStream_t stream) {
   a.scale_log2 = L.scale * kLog2e;
   a.tau = L.tau;
   const int grid = (a.groups + 7) / 8 * 8 * a.qtiles;
-  s2o_attend_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
+  s2o_pass1_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
+  s2o_pass2_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -407,10 +407,10 @@ nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32
  *   KV_perm   the history tokens [0, a) by descending k . rep (equal
  *             scores: lower token first)
  *
- * nsa_s2o_attend: each tile of 64 queries Q_perm[64j .. 64j+63] attends
- * (pass 1) densely and causally inside the segment -- the query at token p
- * sees tokens [a, p] -- and then (pass 2) walks the history in tiles of 64
- * tokens KV_perm[64n .. 64n+63].  After tile n, M_i is query i's attention
+ * nsa_s2o_attend: every query attends (pass 1) densely and causally inside
+ * its segment -- the query at token p sees tokens [a, p] -- and then each
+ * tile of 64 queries Q_perm[64j .. 64j+63] (pass 2) walks the history in
+ * tiles of 64 tokens KV_perm[64n .. 64n+63].  After tile n, M_i is query i's attention
  * mass of tile n and A_i its mass over everything it has seen (tile n
  * included); the walk stops once M_i < tau * A_i for every query of the
  * tile, keeping tile n.  tau = 0 never stops (dense causal attention).
@@ -430,8 +430,11 @@ nsa_status nsa_decode_step_status(void* workspace, size_t workspace_bytes, int32
  *                    first s * segment entries (the rest is left untouched)
  *   num_tiles        [B][Hq][nseg][segment / 64] int32 out: history tiles
  *                    walked by each query tile (segments that exist only)
- *   workspace        nsa_s2o_workspace_bytes bytes, 256-byte aligned, for
- *                    nsa_s2o_index only; no initial contents needed
+ *   workspace        nsa_s2o_workspace_bytes bytes, 256-byte aligned, no
+ *                    initial contents needed; the two calls may share one
+ *                    when run in order on one stream (nsa_s2o_attend keeps
+ *                    each query's pass-1 state there: (m, l) and its
+ *                    unnormalised output, 4 * (D + 2) bytes per query)
  *
  * B * Hq * nseg * max_seq_len must stay below 2^31 (NSA_ERR_UNSUPPORTED).
  * nsa_s2o_workspace_bytes and nsa_s2o_index ask the device for the size of
@@ -457,7 +460,8 @@ nsa_status nsa_s2o_index(const nsa_shape* shape, const nsa_prefill_params* param
 nsa_status nsa_s2o_attend(const nsa_shape* shape, const nsa_prefill_params* params, const void* q,
                           const void* k_pool, const void* v_pool, const int32_t* block_table,
                           const int32_t* seq_lens, const int32_t* q_perm, const int32_t* kv_perm,
-                          void* out, int32_t* num_tiles, hipStream_t stream);
+                          void* out, int32_t* num_tiles, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * Device-side contract checks.  Libraries built with -DNSA_DEBUG (build.py

@@ -78,7 +78,7 @@ class Run:
         lib().nsa_s2o_attend(self.shape, self.params, self.q, self.k_pool, self.v_pool, self.table,
                              self.seq_lens, self.q_perm if q_perm is None else q_perm,
                              self.kv_perm if kv_perm is None else kv_perm, self.out,
-                             self.num_tiles, stream)
+                             self.num_tiles, self.ws, self.ws_bytes, stream)
 
     def run(self):
         self.index()

@@ -221,12 +221,16 @@ def test_s2o_validation():
                 N.PrefillParams(1024, 32768, -1.0), N.PrefillParams(1024, 32768, float("inf"))):
         expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_workspace_bytes, sh, bad)
         expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_index, sh, bad, *ptrs, 1 << 30)
-        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_attend, sh, bad, *ptrs, FAKE, FAKE)
+        expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_attend, sh, bad, *ptrs, FAKE, FAKE, FAKE,
+               1 << 30)
     big = shape(batch=64, max_blocks_per_seq=2048, num_phys_blocks=2048 * 64)
     expect(N.NSA_ERR_UNSUPPORTED, N.nsa_s2o_workspace_bytes, big, N.PrefillParams(1024, 131072, 0))
     msg = expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_attend, sh, ok, FAKE, FAKE, FAKE, FAKE,
-                 FAKE, FAKE, FAKE, None, FAKE)
+                 FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40)
     assert "out" in msg
+    msg = expect(N.NSA_ERR_WORKSPACE_TOO_SMALL, N.nsa_s2o_attend, sh, ok, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096)
+    assert "workspace" in msg
     msg = expect(N.NSA_ERR_INVALID_ARGUMENT, N.nsa_s2o_index, sh, ok, FAKE + 2, FAKE, FAKE, FAKE,
                  FAKE, FAKE, FAKE, 1 << 30)
     assert "aligned" in msg
