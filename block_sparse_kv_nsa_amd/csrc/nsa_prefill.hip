@@ -319,7 +319,7 @@ __device__ __forceinline__ int vt_index(int d, int key) {
 }
 
 // The workgroup of a launch over (sequence, KV head, segment) units, each
-// with G query heads of `qtiles` query tiles.  All workgroups of a unit go
+// with G query heads of `per_head` workgroups.  All workgroups of a unit go
 // to one XCD (workgroups go round-robin over the 8 XCDs), where its heads
 // and query tiles share the K/V tiles they gather in that XCD's L2; units
 // are taken latest segment first.  Returns false for the padding workgroups
@@ -327,17 +327,17 @@ __device__ __forceinline__ int vt_index(int d, int key) {
 struct GroupTile {
   int s, b, g, bh, qt;
 };
-__device__ __forceinline__ bool group_tile(const AttendArgs& a, GroupTile* t) {
+__device__ __forceinline__ bool group_tile(const AttendArgs& a, int per_head, GroupTile* t) {
   const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
-  const int per_unit = a.G * a.qtiles;
+  const int per_unit = a.G * per_head;
   const int unit = (kx / per_unit) * 8 + xcd, r = kx % per_unit;
   const int BG = a.B * a.Hkv;
   if (unit >= BG * a.nseg) return false;
   t->s = a.nseg - 1 - unit / BG;
   t->b = (unit % BG) / a.Hkv;
   t->g = unit % a.Hkv;
-  t->bh = t->b * a.Hq + t->g * a.G + r / a.qtiles;
-  t->qt = r % a.qtiles;
+  t->bh = t->b * a.Hq + t->g * a.G + r / per_head;
+  t->qt = r % per_head;
   return true;
 }
 
@@ -407,30 +407,61 @@ struct TileRegs {
 // and most tiles skip the rescaling of the accumulators.
 constexpr float kLazy = 8.f;
 
-// One tile of 64 keys for this wave's 16 queries (one per lane column):
-// S^T = K Q^T, online-softmax update of (m, l, o) with a lazy reference,
-// O^T += V^T P^T.  MASKED: key k of the tile is kept iff k <= rel (the
-// query's position relative to the tile).  Every lane must see at least one
-// key with a finite logit before its first tile with none (true of both
-// passes: pass 1 starts with the tile holding the segment's first token).
-// Returns the tile's mass in units of 2^-m.
-template <int D, bool MASKED>
-__device__ __forceinline__ float tile_step(const TileSmem<D>& sm, const bf16x8 (&qf)[D / 32],
-                                           f32x4 (&o)[D / 16], float& m, float& l, int col,
-                                           int grp, float scale_log2, int rel) {
-  constexpr int KC = D / 32, DG = D / 16;
-  f32x4 st[4];
+// One tile of 64 keys for this wave's 16 queries (one per lane column), in
+// three parts: S^T = K Q^T (tile_qk), the online-softmax update of (m, l, o)
+// with a lazy reference (tile_softmax), O^T += V^T P^T (tile_pv).  The
+// two-query-group forms (a wave with 32 queries) read each K and V operand
+// from shared memory once for both groups; every group's arithmetic is the
+// same as in the one-group form.  MASKED: key k of the tile is kept iff
+// k <= rel (the query's position relative to the tile).  Every lane must
+// see at least one key with a finite logit before its first tile with none
+// (true of both passes: pass 1 starts with the tile holding the segment's
+// first token).
+template <int D>
+__device__ __forceinline__ void tile_qk(const TileSmem<D>& sm, const bf16x8 (&qf)[D / 32],
+                                        f32x4 (&st)[4], int col, int grp) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
+    for (int c = 0; c < D / 32; ++c) {
       const uint4 kv =
           *reinterpret_cast<const uint4*>(&sm.ks[TileSmem<D>::k_index(16 * kb + col, 4 * c + grp)]);
       st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], st[kb],
                                                        0, 0, 0);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_qk2(const TileSmem<D>& sm, const bf16x8 (&qa)[D / 32],
+                                         const bf16x8 (&qb)[D / 32], f32x4 (&sa)[4],
+                                         f32x4 (&sb)[4], int col, int grp) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    // one row block's operands at a time (the registers of 32 queries'
+    // accumulators leave no room to read them all ahead)
+    __builtin_amdgcn_sched_barrier(0);
+    sa[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const bf16x8 kv = __builtin_bit_cast(
+          bf16x8,
+          *reinterpret_cast<const uint4*>(&sm.ks[TileSmem<D>::k_index(16 * kb + col, 4 * c + grp)]));
+      sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qa[c], sa[kb], 0, 0, 0);
+      sb[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[c], sb[kb], 0, 0, 0);
+    }
+  }
+}
+
+// The tile's weights 2^(x - m) as the P operand (pf) and the update of
+// (m, l, o); returns the tile's mass in units of 2^-m.
+template <int D, bool MASKED>
+__device__ __forceinline__ float tile_softmax(f32x4 (&st)[4], f32x4 (&o)[D / 16], float& m,
+                                              float& l, bf16x8 (&pf)[2], int grp,
+                                              float scale_log2, int rel) {
+  constexpr int DG = D / 16;
   float mt = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -468,21 +499,78 @@ __device__ __forceinline__ float tile_step(const TileSmem<D>& sm, const bf16x8 (
   l += ps;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    bf16x8 pf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pf[i] = (__bf16)st[2 * c][i];
-      pf[4 + i] = (__bf16)st[2 * c + 1][i];
-    }
-#pragma unroll
-    for (int dg = 0; dg < DG; ++dg) {
-      const int d = 16 * dg + col;
-      const uint4 vv = *reinterpret_cast<const uint4*>(&sm.vt[vt_index(d, 32 * c + 4 * grp)]);
-      o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dg], 0,
-                                                      0, 0);
+      pf[c][i] = (__bf16)st[2 * c][i];
+      pf[c][4 + i] = (__bf16)st[2 * c + 1][i];
     }
   }
   return ps;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv(const TileSmem<D>& sm, const bf16x8 (&pf)[2],
+                                        f32x4 (&o)[D / 16], int col, int grp) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int dg = 0; dg < D / 16; ++dg) {
+      const int d = 16 * dg + col;
+      const uint4 vv = *reinterpret_cast<const uint4*>(&sm.vt[vt_index(d, 32 * c + 4 * grp)]);
+      o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf[c], o[dg],
+                                                      0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv2(const TileSmem<D>& sm, const bf16x8 (&pa)[2],
+                                         const bf16x8 (&pb)[2], f32x4 (&oa)[D / 16],
+                                         f32x4 (&ob)[D / 16], int col, int grp) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dg = 0; dg < D / 16; ++dg) {
+      const int d = 16 * dg + col;
+      const bf16x8 vv = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(&sm.vt[vt_index(d, 32 * c + 4 * grp)]));
+      oa[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pa[c], oa[dg], 0, 0, 0);
+      ob[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[c], ob[dg], 0, 0, 0);
+    }
+  }
+}
+
+// One tile for one query group; returns the tile's mass in units of 2^-m.
+template <int D, bool MASKED>
+__device__ __forceinline__ float tile_step(const TileSmem<D>& sm, const bf16x8 (&qf)[D / 32],
+                                           f32x4 (&o)[D / 16], float& m, float& l, int col,
+                                           int grp, float scale_log2, int rel) {
+  f32x4 st[4];
+  tile_qk<D>(sm, qf, st, col, grp);
+  bf16x8 pf[2];
+  const float ps = tile_softmax<D, MASKED>(st, o, m, l, pf, grp, scale_log2, rel);
+  tile_pv<D>(sm, pf, o, col, grp);
+  return ps;
+}
+
+// One tile for two query groups sharing every K and V operand read, each
+// group masked by its own relative position (rel >= 63: the whole tile;
+// rel < 0: none of it, which leaves a group that has seen a finite logit
+// unchanged: its weights are all 0).  ps_a, ps_b: each group's tile mass in
+// units of 2^-m.
+template <int D>
+__device__ __forceinline__ void tile_step2(const TileSmem<D>& sm, const bf16x8 (&qa)[D / 32],
+                                           const bf16x8 (&qb)[D / 32], f32x4 (&oa)[D / 16],
+                                           f32x4 (&ob)[D / 16], float& ma, float& la, float& mb,
+                                           float& lb, int col, int grp, float scale_log2,
+                                           int rel_a, int rel_b, float& ps_a, float& ps_b) {
+  f32x4 sa[4], sb[4];
+  tile_qk2<D>(sm, qa, qb, sa, sb, col, grp);
+  bf16x8 pa[2], pb[2];
+  ps_a = tile_softmax<D, true>(sa, oa, ma, la, pa, grp, scale_log2, rel_a);
+  ps_b = tile_softmax<D, true>(sb, ob, mb, lb, pb, grp, scale_log2, rel_b);
+  tile_pv2<D>(sm, pa, pb, oa, ob, col, grp);
 }
 
 template <int D>
@@ -495,29 +583,39 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const uint16_t* qro
   }
 }
 
-// Pass 1: queries a + 64*qt .. +63 in order; tiles 0..qt of the segment
-// (block slabs, found through the table), the last one causally masked.
+// Pass 1: two consecutive query tiles of a segment per workgroup, qt0 = 2p
+// and qt1 = 2p + 1 (queries a + 64*qt .. +63 in order); each wave holds 16
+// queries of each, and every K and V operand read from shared memory serves
+// both.  Tiles 0..qt1 of the segment (block slabs, found through the table),
+// each query's keys masked causally: tile qt0 is the diagonal of qt0 and
+// whole for qt1, tile qt1 the diagonal of qt1 and empty for qt0 (which it
+// leaves unchanged).  A query's logits, weights and accumulation order are
+// those of a one-tile workgroup.  When qt1 holds no query of the segment its
+// group computes on zero queries and is not stored.
 template <int D>
-__global__ __launch_bounds__(kThreads, 3) void s2o_pass1_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void s2o_pass1_kernel(AttendArgs a) {
   constexpr int DG = D / 16;
   __shared__ __attribute__((aligned(16))) TileSmem<D> sm;
   __shared__ int s_slot[kMaxSegSort / kTile];
   GroupTile gt;
-  if (!group_tile(a, &gt)) return;
+  if (!group_tile(a, (a.qtiles + 1) / 2, &gt)) return;
   const int b = gt.b, g = gt.g;
   const int L = seq_len_of(a.seq_lens, b, a.max_len);
   const int start = gt.s * a.seg;
   if (start >= L) return;
-  const int len = min(a.seg, L - start), q0 = gt.qt * kTile;
+  const int len = min(a.seg, L - start);
+  const int qt0 = 2 * gt.qt, qt1 = qt0 + 1, q0 = qt0 * kTile, q1 = qt1 * kTile;
   if (q0 >= len) return;
+  const bool two = q1 < len;  // the second query tile holds queries
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const int col = lane % 16, grp = lane / 16;
   const int qi = 16 * w + col;
-  const bool qvalid = q0 + qi < len;
-  const int pos = start + q0 + (qvalid ? qi : 0);
-  bf16x8 qf[D / 32];
-  load_q<D>(qf, a.q + ((int64_t)gt.bh * a.max_len + pos) * D, qvalid, grp);
-  const int ntiles = gt.qt + 1;
+  const bool qv0 = q0 + qi < len, qv1 = two && q1 + qi < len;
+  const int pos0 = start + q0 + (qv0 ? qi : 0), pos1 = start + q1 + (qv1 ? qi : 0);
+  bf16x8 qf0[D / 32], qf1[D / 32];
+  load_q<D>(qf0, a.q + ((int64_t)gt.bh * a.max_len + pos0) * D, qv0, grp);
+  load_q<D>(qf1, a.q + ((int64_t)gt.bh * a.max_len + pos1) * D, qv1, grp);
+  const int ntiles = (two ? qt1 : qt0) + 1;
   if (tid < ntiles)
     s_slot[tid] = dbg_clamp(a.table[(int64_t)b * a.max_blocks + start / kTile + tid], 0, a.P,
                             kDbgTable);
@@ -534,28 +632,34 @@ __global__ __launch_bounds__(kThreads, 3) void s2o_pass1_kernel(AttendArgs a) {
                  t0 + 2 * lp < L, t0 + 2 * lp + 1 < L, ck);
     }
   };
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[DG];
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  f32x4 o0[DG], o1[DG];
 #pragma unroll
-  for (int dg = 0; dg < DG; ++dg) o[dg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dg = 0; dg < DG; ++dg) {
+    o0[dg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    o1[dg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   issue(0);
   for (int n = 0; n < ntiles; ++n) {
     tr.stash(sm, lp, ck);
     if (n + 1 < ntiles) issue(n + 1);
     __syncthreads();
-    if (n == gt.qt)
-      tile_step<D, true>(sm, qf, o, m, l, col, grp, a.scale_log2, pos - start - n * kTile);
-    else
-      tile_step<D, false>(sm, qf, o, m, l, col, grp, a.scale_log2, 0);
+    // relative positions: >= 63 below the diagonal tile, < 0 past it
+    const int t0 = start + n * kTile;
+    float ps0, ps1;
+    tile_step2<D>(sm, qf0, qf1, o0, o1, m0, l0, m1, l1, col, grp, a.scale_log2,
+                  min(pos0 - t0, kTile), min(pos1 - t0, kTile), ps0, ps1);
     __syncthreads();
   }
-  if (qvalid) {
+  auto put = [&](int pos, float m, float l, const f32x4 (&o)[DG]) {
     const int64_t row = (int64_t)gt.bh * a.max_len + pos;
     if (grp == 0) *reinterpret_cast<f32x2*>(a.st_ml + row * 2) = f32x2{m, l};
 #pragma unroll
     for (int dg = 0; dg < DG; ++dg)
       *reinterpret_cast<f32x4*>(a.st_acc + row * D + 16 * dg + 4 * grp) = o[dg];
-  }
+  };
+  if (qv0) put(pos0, m0, l0, o0);
+  if (qv1) put(pos1, m1, l1, o1);
 }
 
 // Pass 2: the tile's permuted queries resume their pass-1 states and walk the
@@ -568,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 3) void s2o_pass2_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) TileSmem<D> sm;
   __shared__ int s_flag[2][kWaves];
   GroupTile gt;
-  if (!group_tile(a, &gt)) return;
+  if (!group_tile(a, a.qtiles, &gt)) return;
   const int b = gt.b, g = gt.g;
   const int L = seq_len_of(a.seq_lens, b, a.max_len);
   const int start = gt.s * a.seg;
@@ -734,10 +838,9 @@ hipError_t attend_d(const PrefillLaunch& L, hipStream_t stream) {
   a.qtiles = lay.seg / kTile;
   a.scale_log2 = L.scale * kLog2e;
   a.tau = L.tau;
-  const int units = lay.B * lay.Hkv * lay.nseg;
-  const int grid = (units + 7) / 8 * 8 * L.G * a.qtiles;
-  s2o_pass1_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
-  s2o_pass2_kernel<D><<<dim3(grid), kThreads, 0, stream>>>(a);
+  const int units = (lay.B * lay.Hkv * lay.nseg + 7) / 8 * 8;
+  s2o_pass1_kernel<D><<<dim3(units * L.G * ((a.qtiles + 1) / 2)), kThreads, 0, stream>>>(a);
+  s2o_pass2_kernel<D><<<dim3(units * L.G * a.qtiles), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
